@@ -1,0 +1,124 @@
+"""The pins must fail when a plausible mistake is planted in the oracle.
+
+Each case monkeypatches one oracle function with a wrong variant (on the CPU
+only) and checks that at least one of the pin tests for that function raises.
+"""
+import numpy as np
+import pytest
+
+from oracle import gdn, quant
+from tests import test_oracle_gdn as tg
+from tests import test_oracle_quant as tq
+
+
+def _wrong_sign(M, q, k, v, alpha, beta):
+    a = alpha[:, None, None]
+    b = beta[:, None, None]
+    kM = np.einsum("ni,nij->nj", k, M)
+    M = a * (M + b * k[:, :, None] * kM[:, None, :]) + b * k[:, :, None] * v[:, None, :]
+    return M, np.einsum("ni,nij->nj", q, M)
+
+
+def _gate_misplaced(M, q, k, v, alpha, beta):
+    a = alpha[:, None, None]
+    b = beta[:, None, None]
+    kM = np.einsum("ni,nij->nj", k, M)
+    M = a * M - b * k[:, :, None] * kM[:, None, :] + b * k[:, :, None] * v[:, None, :]
+    return M, np.einsum("ni,nij->nj", q, M)
+
+
+def _transposed_write(M, q, k, v, alpha, beta):
+    a = alpha[:, None, None]
+    b = beta[:, None, None]
+    kM = np.einsum("ni,nij->nj", k, M)
+    M = a * (M - b * k[:, :, None] * kM[:, None, :]) + b * v[:, :, None] * k[:, None, :]
+    return M, np.einsum("ni,nij->nj", q, M)
+
+
+def _read_before_write(M, q, k, v, alpha, beta):
+    o = np.einsum("ni,nij->nj", q, M)
+    a = alpha[:, None, None]
+    b = beta[:, None, None]
+    kM = np.einsum("ni,nij->nj", k, M)
+    M = a * (M - b * k[:, :, None] * kM[:, None, :]) + b * k[:, :, None] * v[:, None, :]
+    return M, o
+
+
+def _no_beta_on_write(M, q, k, v, alpha, beta):
+    a = alpha[:, None, None]
+    b = beta[:, None, None]
+    kM = np.einsum("ni,nij->nj", k, M)
+    M = a * (M - b * k[:, :, None] * kM[:, None, :]) + k[:, :, None] * v[:, None, :]
+    return M, np.einsum("ni,nij->nj", q, M)
+
+
+GDN_PINS = [tg.test_beta_zero_is_pure_decay, tg.test_basis_key_overwrites_one_row_exactly,
+            tg.test_one_token_from_zero, tg.test_delta_rule_maps_key_to_value,
+            lambda: [tg.test_exact_rational_brute_force(s) for s in range(3)]]
+
+
+@pytest.mark.parametrize("bad", [_wrong_sign, _gate_misplaced, _transposed_write,
+                                 _read_before_write, _no_beta_on_write])
+def test_gdn_pins_catch(bad, monkeypatch):
+    monkeypatch.setattr(gdn, "step", bad)
+    caught = 0
+    for pin in GDN_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError):
+            caught += 1
+    assert caught >= 1, bad.__name__
+
+
+def _enc_half_up(M, bits):
+    M = np.asarray(M, dtype=np.float64)
+    qm = quant._qmax_per_tile(bits, M.shape[:-2])[..., None]
+    a = np.max(np.abs(M), axis=-2)
+    s = (a / qm).astype(np.float32)
+    s64 = s.astype(np.float64)[..., None, :]
+    x = np.where(s64 > 0, M / np.where(s64 > 0, s64, 1), 0.0)
+    return np.clip(np.floor(x + 0.5), -qm[..., None], qm[..., None]).astype(np.int16), s
+
+
+def _enc_wrong_qmax(M, bits):
+    M = np.asarray(M, dtype=np.float64)
+    qm = quant._qmax_per_tile(bits, M.shape[:-2])[..., None] + 1
+    a = np.max(np.abs(M), axis=-2)
+    s = (a / qm).astype(np.float32)
+    s64 = s.astype(np.float64)[..., None, :]
+    x = np.where(s64 > 0, M / np.where(s64 > 0, s64, 1), 0.0)
+    return np.clip(np.rint(x), -qm[..., None], qm[..., None]).astype(np.int16), s
+
+
+def _enc_row_scales(M, bits):
+    c, s = quant.__dict__["_orig_encode"](np.swapaxes(M, -1, -2), bits)
+    return np.swapaxes(c, -1, -2), s
+
+
+def _enc_scale_f64(M, bits):
+    M = np.asarray(M, dtype=np.float64)
+    qm = quant._qmax_per_tile(bits, M.shape[:-2])[..., None]
+    a = np.max(np.abs(M), axis=-2)
+    s = a / qm
+    s64 = s[..., None, :]
+    x = np.where(s64 > 0, M / np.where(s64 > 0, s64, 1), 0.0)
+    return np.clip(np.rint(x), -qm[..., None], qm[..., None]).astype(np.int16), s
+
+
+QUANT_PINS = [lambda: [tq.test_constructed_exact_ties_go_to_even(b) for b in (4, 8)],
+              lambda: [tq.test_zero_column(b) for b in (4, 8)],
+              lambda: [tq.test_quantizer_invariants_gaussian(b) for b in (4, 8)],
+              tq.test_scale_is_absmax_over_qmax_in_float32]
+
+
+@pytest.mark.parametrize("bad", [_enc_half_up, _enc_wrong_qmax, _enc_row_scales, _enc_scale_f64])
+def test_quant_pins_catch(bad, monkeypatch):
+    monkeypatch.setitem(quant.__dict__, "_orig_encode", quant.encode)
+    monkeypatch.setattr(quant, "encode", bad)
+    caught = 0
+    for pin in QUANT_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught >= 1, bad.__name__

@@ -1,0 +1,123 @@
+"""Pins of the oracle's column-scaled quantizer (oracle/quant.py)."""
+import json
+import os
+
+import numpy as np
+import pytest
+from hypothesis import given, settings
+from hypothesis import strategies as st
+from hypothesis.extra import numpy as hnp
+
+from oracle import quant
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_rint_is_round_half_even():
+    x = np.array([0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 3.5, 6.5])
+    assert np.rint(x).tolist() == [0, 2, 2, -0, -2, -2, 4, 6]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_constructed_exact_ties_go_to_even(bits):
+    qm = quant.qmax(bits)
+    s = np.float32(0.0123)
+    s64 = float(s)
+    # column absmax is exactly qmax * s, so the encoded scale is exactly s
+    halves = np.arange(-qm + 0.5, qm - 0.5 + 1e-9, 1.0)
+    col = np.concatenate([[qm * s64], halves * s64])
+    M = col[None, :, None]
+    c, sc = quant.encode(M, bits)
+    assert sc[0, 0] == s
+    expect = np.rint(halves)               # even neighbour
+    assert np.all(expect % 2 == 0)
+    assert c[0, 1:, 0].tolist() == expect.astype(int).tolist()
+    assert c[0, 0, 0] == qm
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_zero_column(bits):
+    M = np.zeros((1, 8, 3))
+    M[0, 2, 1] = 0.5
+    c, s = quant.encode(M, bits)
+    assert s[0, 0] == 0 and s[0, 2] == 0
+    assert np.all(c[0, :, 0] == 0) and np.all(c[0, :, 2] == 0)
+    assert c[0, 2, 1] == quant.qmax(bits)
+
+
+def _check_invariants(M, bits):
+    qm = quant.qmax(bits)
+    c, s = quant.encode(M, bits)
+    D = quant.decode(c, s)
+    s64 = s.astype(np.float64)[..., None, :]
+    # round-trip error at most half a step (plus float64 rounding of the quotient)
+    assert np.all(np.abs(M - D) <= 0.5 * s64 * (1 + 1e-12) + 1e-300)
+    assert np.all(np.abs(c) <= qm)
+    nz = np.max(np.abs(M), axis=-2) > 0
+    reach = np.max(np.abs(c), axis=-2) == qm
+    assert np.all(reach[nz])
+    # re-encoding a decoded state gives the same codes and the scale within 1 ulp
+    c2, s2 = quant.encode(D, bits)
+    assert np.array_equal(c2, c)
+    ulp = np.spacing(s)
+    assert np.all(np.abs(s2.astype(np.float64) - s) <= ulp)
+    return c, s
+
+
+@settings(max_examples=60, deadline=None)
+@given(hnp.arrays(np.float64, (2, 6, 5),
+                  elements=st.floats(-1e3, 1e3, allow_nan=False, allow_infinity=False)
+                  .filter(lambda x: x == 0 or abs(x) > 1e-20)),
+       st.sampled_from([4, 8]))
+def test_quantizer_invariants_property(M, bits):
+    _check_invariants(M, bits)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_quantizer_invariants_gaussian(bits):
+    rng = np.random.default_rng(7)
+    M = rng.standard_normal((8, 64, 64)) * rng.uniform(0.01, 10, (8, 1, 64))
+    _check_invariants(M, bits)
+
+
+def test_scale_is_absmax_over_qmax_in_float32():
+    rng = np.random.default_rng(8)
+    M = rng.standard_normal((3, 16, 4))
+    for bits in (4, 8):
+        _, s = quant.encode(M, bits)
+        a = np.max(np.abs(M), axis=-2)
+        assert np.array_equal(s, (a / quant.qmax(bits)).astype(np.float32))
+
+
+def test_per_tile_bits():
+    rng = np.random.default_rng(9)
+    M = rng.standard_normal((2, 16, 4))
+    c, s = quant.encode(M, np.array([4, 8]))
+    c4, s4 = quant.encode(M[:1], 4)
+    c8, s8 = quant.encode(M[1:], 8)
+    assert np.array_equal(c[:1], c4) and np.array_equal(c[1:], c8)
+    assert np.array_equal(s[:1], s4) and np.array_equal(s[1:], s8)
+
+
+def test_tie_distance():
+    x = np.array([0.5, 1.0, -2.5, 3.25, 0.4999])
+    np.testing.assert_allclose(quant.tie_distance(x), [0, 0.5, 0, 0.25, 1e-4], atol=1e-12)
+
+
+def test_storage_ratios_against_the_pages():
+    with open(os.path.join(GOLDEN, "storage_ratios.json")) as f:
+        g = {r["name"]: r for r in json.load(f)["ratios"]}
+    d = 128
+    int4 = quant.tile_bytes(d, d, 4)
+    int8 = quant.tile_bytes(d, d, 8)
+    fp16 = d * d * 2
+    assert int4 == 8192 + 512 and int8 == 16384 + 512
+    r = g["int4_vs_fp16"]
+    assert abs(int4 / fp16 - r["printed"]) <= r["tolerance"]
+    r = g["int4_vs_int8"]
+    assert abs(int4 / int8 - r["printed"]) <= r["tolerance"]
+    r = g["mixed_4_8_vs_int8"]
+    mix = r["mix"]
+    ratio = (mix["heads4"] * int4 + mix["heads8"] * int8) / ((mix["heads4"] + mix["heads8"]) * int8)
+    assert abs(ratio - r["printed"]) <= r["tolerance"]
+    assert abs(ratio - 1344 / 2112) < 1e-12
