@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of PACE-style periodic-rounding GDN decode on one MI355X.
+
+One step = one decode period over the whole batch: every (sequence, head)
+state is decoded from its 4/8-bit codes, the period's k tokens are applied in
+float32 with the gated delta rule (outputs written for every token), and the
+state is re-encoded with per-column scales.  Default workload: 4096 sequences,
+16 heads (12 at 4 bits, 4 at 8 bits), d_k = d_v = 128, period 8, bf16 q/k/v,
+8 outlier value channels; 128 steps = 1024 decode steps.
+
+Inputs are synthetic and seeded (linear_attn_decode_pace_amd.inputs); a ring
+of distinct periods is resident in HBM before timing.  The initial state comes
+from 32 unquantized warm-up tokens run by the library's prefill kernel.
+
+Prints one JSON line: token-steps/s (sequences x tokens per second), the
+decode kernel's achieved HBM bandwidth against MI355X's 8 TB/s, and the float64
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from linear_attn_decode_pace_amd import inputs  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["linear_attn_decode_pace_amd/csrc/decode_mfma.hip",
+                  "linear_attn_decode_pace_amd/csrc/kernels_v0.hip",
+                  "linear_attn_decode_pace_amd/csrc/pace_layout.h"]
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w: inputs.Workload, n_tok: int, head_bits) -> int:
+    """Bytes one decode call must move at minimum: every stored code and scale
+    read and written once, q/k/v/alpha/beta read once, outputs written once
+    (float32)."""
+    e_in = 2 if w.dtype == inputs.DT_BF16 else 4
+    state = 0
+    for b in head_bits:
+        state += w.dk * w.dv * int(b) // 8 + 4 * w.dv
+    per_seq_tok = w.H * ((w.dk * 2 + w.dv) * e_in + 8 + 4 * w.dv)
+    return w.B * (2 * state + n_tok * per_seq_tok)
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        fp = os.path.join(ROOT, p)
+        if os.path.exists(fp):
+            with open(fp, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _gen_block(args):
+    w, seed, seg, t0, t1 = args
+    return inputs.tokens(w, seed, seg, t0, t1)
+
+
+def generate(w, seed, jobs, workers):
+    if workers <= 1 or len(jobs) == 1:
+        return [_gen_block((w, seed) + j) for j in jobs]
+    with cf.ProcessPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(_gen_block, [(w, seed) + j for j in jobs]))
+
+
+def traffic_from_profile(name: str, sha: str, n_launch_bytes: int):
+    fp = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(fp):
+        return None
+    with open(fp) as f:
+        t = json.load(f)
+    if t.get("kernel_sha") != sha:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, seed, warm_tok, periods_tok, head_bits, n_seq):
+    """Time the float64 oracle over the first n_seq sequences (all heads) for
+    the given periods, from the oracle's own warm-up state (warm-up untimed)."""
+    import numpy as np
+
+    from oracle import gdn
+    from oracle import pace as opace
+    from oracle import quant
+
+    b = np.repeat(np.arange(n_seq), w.H)
+    h = np.tile(np.arange(w.H), n_seq)
+    bits = np.tile(np.asarray(head_bits), n_seq).astype(np.int64)
+
+    def arr(tok):
+        return [tok.f64(x)[:, b, h] for x in ("q", "k", "v", "alpha", "beta")]
+
+    M0 = gdn.from_zero(w.dk, w.dv, *arr(warm_tok))
+    codes, scales = quant.encode(M0, bits)
+    toks = [arr(t) for t in periods_tok]
+    t0 = time.perf_counter()
+    for a in toks:
+        _, codes, scales, _ = opace.period(codes, scales, bits, *a)
+    dt = time.perf_counter() - t0
+    n_tok = sum(t.T for t in periods_tok)
+    try:
+        cpu = next((l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
+                    if l.startswith("model name")), platform.processor())
+    except OSError:
+        cpu = platform.processor()
+    return {"value": n_seq * n_tok / dt, "unit": "token-steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_seq} of {w.B} sequences x {w.H} heads, {len(periods_tok)} periods "
+                      f"of {w.period} tokens ({n_tok} decode steps), float64 numpy, "
+                      f"{dt:.1f} s on one core ({cpu})",
+            "seconds": dt}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=inputs.HEADLINE.name, choices=sorted(inputs.WORKLOADS))
+    ap.add_argument("--period", type=int, default=None, help="override the workload's period")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--ring", type=int, default=4, help="distinct input periods resident in HBM")
+    ap.add_argument("--cpu-seqs", type=int, default=256)
+    ap.add_argument("--cpu-periods", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workers", type=int, default=min(16, len(os.sched_getaffinity(0))))
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): every (sequence, head) "
+              "state is independent, so this layer needs no collective; the single-GPU figure "
+              "is the per-GPU figure.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from linear_attn_decode_pace_amd import pace, runtime
+
+    w = inputs.WORKLOADS[args.workload]
+    if args.period:
+        w = w.replace(period=args.period)
+    if w.prompt:
+        raise SystemExit("the prefill hand-off workload is a parity case; bench the decode workloads")
+    C = w.period
+    torch.cuda.set_device(0)
+    head_bits = inputs.head_bits(w, args.seed)
+
+    t = time.time()
+    ring_n = max(1, args.ring)
+    jobs = [(inputs.SEG_WARMUP, 0, w.warmup)] + \
+           [(inputs.SEG_DECODE, p * C, (p + 1) * C) for p in range(ring_n)]
+    toks = generate(w, args.seed, jobs, args.workers)
+    warm_tok, ring_tok = toks[0], toks[1:]
+    log(f"generated inputs in {time.time() - t:.1f} s")
+
+    M0 = torch.zeros((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    runtime.prefill(w, runtime.DeviceTokens(warm_tok), M0)
+    st = runtime.State(w, head_bits, pace.PACE_INIT_F32, M0)
+    del M0
+    ring = [runtime.DeviceTokens(tk) for tk in ring_tok]
+    out = runtime.out_buffer(w, C)
+    torch.cuda.synchronize()
+    log(f"state and {ring_n} input periods resident ({sum(r.nbytes for r in ring) / 1e9:.2f} GB)")
+
+    for i in range(args.warmup):
+        st.decode(ring[i % ring_n], out)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(K):
+        ev[i][0].record()
+        st.decode(ring[(args.warmup + i) % ring_n], out)
+        ev[i][1].record()
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    launch_ms = sum(a.elapsed_time(b) for a, b in ev) / K
+    log(f"timed {K} steps: {total_ms:.3f} ms on the device, {t_wall * 1e3:.1f} ms wall")
+
+    nbytes = algorithmic_bytes(w, C, head_bits)
+    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    sha = kernel_sha()
+    value = w.B * C * K / (total_ms * 1e-3)
+    res = {
+        "metric": "decode token-steps/s per GDN layer (seqs x tokens) + achieved HBM GB/s vs peak",
+        "value": value,
+        "unit": "token-steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "heads": w.H, "d_k": w.dk, "d_v": w.dv,
+                   "period": C, "heads_int8": int((head_bits == 8).sum()),
+                   "inputs": w.dtype, "outlier_channels": w.n_outliers,
+                   "decode_steps": K * C, "input_ring_periods": ring_n},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": traffic_from_profile(w.name, sha, nbytes),
+                     "algorithmic_bytes_per_launch": nbytes, "launch_ms": launch_ms,
+                     "kernel_sha": sha},
+    }
+    st.free()
+    del ring, out
+    if not args.no_cpu_baseline:
+        n_seq = min(args.cpu_seqs, w.B)
+        cb = cpu_baseline(w, args.seed, warm_tok, ring_tok[:max(1, args.cpu_periods)],
+                          head_bits, n_seq)
+        res["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,204 @@
+/*
+ * pace.h - C ABI of a periodic-rounding gated delta-rule (GDN) decode library
+ * whose recurrent state is stored as 4-bit (or 8-bit) codes with one float32
+ * scale per state column.  Built for AMD MI355X (gfx950) with HIP.
+ *
+ * What the library computes (sources are the pages this implementation follows):
+ *
+ *  - One recurrent state per (sequence, head), so a server can decode many
+ *    sequences at once with one state copy each ('PACE: four-bit recurrent
+ *    state by rounding less often', TL;DR; 'PACE: A New 4-Bit Recurrent State
+ *    Quantization Method That Makes Linear Attention Models More
+ *    Memory-Efficient', section 'Why Do We Need Low-Precision Recurrent
+ *    States?').  The state of one (sequence, head) is M in R^{d_k x d_v}:
+ *    row i is key channel i, column j is value channel j.
+ *
+ *  - The gated delta rule, for each token t (the gate sets the forgetting
+ *    rate, the delta rule makes each write an online-learning step:
+ *    '低比特量化新突破：GGA+PW让线性注意力长文本生成更准更短', section
+ *    '为什么低比特状态量化会“越写越错”'):
+ *        M_t = alpha_t (M_{t-1} - beta_t k_t (k_t^T M_{t-1})) + beta_t k_t v_t^T
+ *        o_t = M_t^T q_t
+ *    q and k must already be L2-normalised by the caller; q is not scaled.
+ *
+ *  - Periodic rounding: the stored state is decoded, one period of tokens is
+ *    applied in float32, and the state is re-encoded once at the end of the
+ *    period (PACE wiki page, TL;DR point (1) and flowchart; 'PACE: A New
+ *    4-Bit ...', section 'Periodic Rounding').  Outputs are read from the
+ *    high-precision state, before the period-end encode.
+ *
+ *  - Channel-aligned encoding: one scale per column, s_j = absmax_i |M_ij| / qmax
+ *    in float32 (qmax = 7 for 4 bits, 127 for 8 bits), codes
+ *    c_ij = round_to_nearest_even(M_ij / s_j); a zero column has s_j = 0 and
+ *    zero codes ('PACE: A New 4-Bit ...', section 'Channel-Aligned Encoding';
+ *    PACE wiki page, TL;DR point (2)).
+ *
+ *  - Mixed heads: each head has a bit width (4 or 8), the same for every
+ *    sequence; 8-bit heads are meant for heads whose rounding error persists
+ *    longest (PACE wiki page, TL;DR point (3); flowchart node '8-bit heads').
+ *    4-bit and 8-bit heads live in separate device pools.
+ *
+ * Conventions for every entry point:
+ *  - Return value: PACE_OK (0) or a negative PACE_E* status.  On error,
+ *    pace_last_error() returns a message for the calling thread.  No
+ *    exception crosses the ABI and nothing aborts the process.
+ *  - All argument checks happen before any HIP call, so a call that returns
+ *    PACE_EINVAL or PACE_EUNSUPPORTED has touched no device state.
+ *  - "device" pointers point to memory of the device that was current when the
+ *    state was allocated; "host" pointers to ordinary host memory.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    on it and the call returns without waiting, except where stated.  A state
+ *    handle must not be used from two streams at once.
+ *  - Tensor layouts are dense and row-major in the order written; "[T, B, H, d]"
+ *    means token-major, then sequence, then head, then channel.
+ */
+#ifndef PACE_H_
+#define PACE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PACE_ABI_VERSION 1
+
+/* status codes */
+#define PACE_OK 0
+#define PACE_EINVAL (-1)       /* a bad argument: null pointer, size, enum, alignment */
+#define PACE_ENOMEM (-2)       /* device allocation failed */
+#define PACE_EUNSUPPORTED (-3) /* a shape or period this build has no kernel for */
+#define PACE_EDEVICE (-4)      /* a HIP error (no device, launch failure, earlier fault) */
+
+/* element types of q, k, v */
+#define PACE_DTYPE_F32 0
+#define PACE_DTYPE_BF16 1
+
+/* pace_state_alloc init kinds */
+#define PACE_INIT_ZERO 0 /* all scales and codes zero; init must be NULL */
+#define PACE_INIT_F32 1  /* init: device float32 [B, H, d_k, d_v]; encoded once */
+#define PACE_INIT_RAW 2  /* init: device raw image written by pace_read_state(PACE_READ_RAW) */
+
+/* pace_read_state kinds */
+#define PACE_READ_CODES 0   /* dst: device int8 [B, H, d_k, d_v]; scales_dst: device float32 [B, H, d_v] */
+#define PACE_READ_DEQUANT 1 /* dst: device float32 [B, H, d_k, d_v] = c_ij * s_j; scales_dst may be NULL */
+#define PACE_READ_RAW 2     /* dst: device bytes [pace_raw_bytes()]; scales_dst must be NULL */
+
+/* config flags (none defined yet; must be 0) */
+
+typedef struct pace_state pace_state; /* opaque; owns the device pools */
+
+typedef struct pace_config {
+    int32_t batch;            /* B: sequences decoding concurrently, >= 1 */
+    int32_t heads;            /* H: heads of the layer, >= 1 */
+    int32_t d_k;              /* state rows (key channels): 64 or 128 */
+    int32_t d_v;              /* state columns (value channels): a multiple of 16, 16..256 */
+    int32_t period;           /* k: most tokens one pace_decode_period call may apply, 1..64 */
+    int32_t in_dtype;         /* PACE_DTYPE_F32 or PACE_DTYPE_BF16: element type of q, k, v */
+    const uint8_t *head_bits; /* host [H]: bit width of each head, 4 or 8; copied at alloc */
+    uint32_t flags;           /* must be 0 */
+} pace_config;
+
+typedef struct pace_stats {
+    uint64_t bytes_codes4;     /* device bytes of the 4-bit code pool */
+    uint64_t bytes_codes8;     /* device bytes of the 8-bit code pool */
+    uint64_t bytes_scales;     /* device bytes of the float32 column scales */
+    uint64_t bytes_total;      /* sum of the three above */
+    uint64_t bytes_fp16_equiv; /* the same states stored densely as fp16 */
+    uint64_t bytes_int8_equiv; /* the same states with every head at 8 bits (plus scales) */
+    int32_t heads4;            /* heads in the 4-bit pool */
+    int32_t heads8;            /* heads in the 8-bit pool */
+    uint64_t periods;          /* pace_decode_period calls applied since alloc */
+    uint64_t tokens;           /* tokens applied since alloc */
+    uint64_t zero_columns;     /* stored columns whose scale is 0 */
+} pace_stats;
+
+/* ABI version this library was built with (PACE_ABI_VERSION). */
+int pace_abi_version(void);
+
+/* Message for the last non-zero status returned on the calling thread ("" if none).
+ * The pointer stays valid until the next pace_* call on that thread. */
+const char *pace_last_error(void);
+
+/*
+ * Allocate the device pools of B x H states and initialise them.
+ *   cfg:       host; validated and copied (head_bits included).
+ *   init_kind: PACE_INIT_ZERO | PACE_INIT_F32 | PACE_INIT_RAW (see above).
+ *   init:      device pointer per init_kind; must stay valid until the
+ *              stream has run the initialisation.
+ *   stream:    hipStream_t for the initialisation work.
+ *   out:       host; receives the new handle (unchanged on error).
+ * The only call that allocates device memory (hipMalloc, so it may block).
+ * PACE_INIT_F32 encodes each (sequence, head) state with the column quantizer.
+ * Errors: EINVAL, EUNSUPPORTED (d_k, d_v or period outside what is built),
+ *         ENOMEM, EDEVICE.
+ */
+int pace_state_alloc(const pace_config *cfg, int init_kind, const void *init,
+                     void *stream, pace_state **out);
+
+/* Free the pools and the handle; waits for the device first.  NULL is a no-op. */
+int pace_state_free(pace_state *st);
+
+/* Configuration the handle was allocated with (head_bits points into the handle). */
+int pace_state_config(const pace_state *st, pace_config *out);
+
+/* Size in bytes of the raw image written by pace_read_state(PACE_READ_RAW). */
+int pace_raw_bytes(const pace_state *st, uint64_t *out);
+
+/*
+ * Apply one period of n_tok tokens (1 <= n_tok <= cfg.period) to every
+ * (sequence, head) state: decode the stored codes, apply the tokens in order
+ * in float32 with the gated delta rule, write o_t for each token, and
+ * re-encode the state with per-column scales at the end of the call.
+ *   q, k:  device [n_tok, B, H, d_k], in_dtype, 16-byte aligned.
+ *   v:     device [n_tok, B, H, d_v], in_dtype, 16-byte aligned.
+ *   alpha, beta: device float32 [n_tok, B, H], 4-byte aligned; alpha is the
+ *          gate (0 < alpha <= 1 expected), beta the write strength.
+ *   out:   device float32 [n_tok, B, H, d_v], 16-byte aligned; may not alias inputs.
+ * Errors: EINVAL (null handle or pointer, n_tok out of range, misalignment),
+ *         EDEVICE (launch failure or an earlier asynchronous fault).
+ */
+int pace_decode_period(pace_state *st, int32_t n_tok, const void *q, const void *k,
+                       const void *v, const float *alpha, const float *beta, float *out,
+                       void *stream);
+
+/*
+ * Read the stored state (see PACE_READ_*).  dst and scales_dst are device
+ * pointers sized as documented above.  The raw image is the library's own
+ * device layout (4-bit pool, then 8-bit pool, then scales) and is meant only
+ * to be handed back to pace_state_alloc(PACE_INIT_RAW) for a handle of the
+ * same configuration (checkpoint / resume).
+ * Errors: EINVAL, EDEVICE.
+ */
+int pace_read_state(const pace_state *st, int what, void *dst, float *scales_dst,
+                    void *stream);
+
+/*
+ * Storage accounting and counters of a handle.  out is host memory.  Counts
+ * zero columns on the device, so it waits for `stream`.
+ * Errors: EINVAL, EDEVICE.
+ */
+int pace_quant_stats(const pace_state *st, pace_stats *out, void *stream);
+
+/*
+ * Unquantized float32 gated delta rule over n_tok tokens, in place on a dense
+ * float32 state: used to build the state that decode starts from (warm-up
+ * tokens, or a prompt streamed in blocks).  The chunked-prefill motivation of
+ * periodic rounding is the PACE wiki page, TL;DR point (1).
+ *   state: device float32 [B, H, d_k, d_v], read and written.
+ *   q, k:  device [n_tok, B, H, d_k]; v: device [n_tok, B, H, d_v]; in_dtype.
+ *   alpha, beta: device float32 [n_tok, B, H].
+ *   out:   device float32 [n_tok, B, H, d_v], or NULL to skip outputs.
+ * Errors: EINVAL, EUNSUPPORTED, EDEVICE.
+ */
+int pace_prefill_f32(int32_t batch, int32_t heads, int32_t d_k, int32_t d_v, int32_t n_tok,
+                     int32_t in_dtype, const void *q, const void *k, const void *v,
+                     const float *alpha, const float *beta, float *state, float *out,
+                     void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PACE_H_ */

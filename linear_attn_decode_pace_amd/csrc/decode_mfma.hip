@@ -1,0 +1,512 @@
+// Fused dequant -> chunked gated-delta update -> requant kernel for gfx950.
+//
+// One 64-wide wavefront owns one (sequence, head) state tile M (d x d, d = 64
+// or 128) for the whole period and streams its packed codes and column scales
+// through registers once: read, update, re-encode, write.  The period's C = 8
+// tokens (fewer are padded with identity tokens alpha = 1, beta = 0) are
+// applied as one chunk in the WY / UT form of the gated delta rule, which
+// follows from unrolling M_t = alpha_t (M - beta_t k_t k_t^T M) + beta_t k_t v_t^T
+// over the chunk (periodic rounding applies a period's tokens in high
+// precision before one encode: 'PACE: four-bit recurrent state by rounding
+// less often', TL;DR (1) and flowchart):
+//
+//   gamma_t = prod_{r<=t} alpha_r,  Gamma_ts = prod_{s<r<=t} alpha_r
+//   A   = strictly lower (Gamma * K K^T),  T = (I + diag(beta) A)^-1 diag(beta)
+//   X   = V - diag(gamma) K M0                 U = T X
+//   O   = diag(gamma) Q M0 + lower_incl(Gamma * Q K^T) U
+//   M_C = gamma_C M0 + K^T diag(Gamma_C,:) U
+//
+// with M0 = codes * diag(s).  Dense contractions run on MFMA:
+//   * P = [K; Q] . codes  (16 x d x 16 per column block): bf16 MFMA, exact,
+//     because codes (|c| <= 127) and bf16 inputs are exact in bf16 and their
+//     products exact in float32;
+//   * the 8 x 8 chunk matrices applied to X and Y = diag(gamma) Q M0 give W
+//     (the update's right factor) and O: float32 MFMA (16x16x4), whose
+//     operand layout matches what each lane already holds;
+//   * K^T W (d x 8 x 16 per column block): bf16 MFMA with W split exactly into
+//     three bf16 parts (hi + mid + lo) stacked along the reduction dimension.
+// The state is accumulated in units of sigma_j = gamma_C s_j:
+//   acc = M_C / sigma_j = codes + K^T (W / sigma_j),
+// so the accumulator starts from the codes themselves (no per-entry multiply).
+// Re-encode (one scale per column: 'PACE: A New 4-Bit Recurrent State
+// Quantization Method ...', section 'Channel-Aligned Encoding'):
+//   absmax over the column's d rows (in-lane max, then two cross-lane xors),
+//   s_new = absmax / qmax, codes = rint(M / s_new) via a fused multiply-add
+//   against 1.5 * 2^23 (round to nearest even in one float32 rounding),
+//   nibble / byte packing with v_perm and v_bfi, one 16-byte store per lane.
+//
+// Lane l = 16 g + n owns, in every column block cb, column j = 16 cb + n and
+// the rows i with (i / 4) % 4 == g: exactly its rows of a 16 x 16 MFMA
+// accumulator tile, and exactly its bytes in the pool layout (pace_layout.h).
+#include "pace_mfma.h"
+
+namespace pace {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int CH = 8;      // tokens per chunk
+constexpr int WAVES = 4;   // tiles (waves) per workgroup
+constexpr int LROW = 136;  // bf16 elements per LDS token row (128 + 8 padding)
+
+struct WaveLds {
+    uint16_t kq[16][LROW];  // rows 0..7: k_t, rows 8..15: q_t (bf16 bits)
+    uint16_t v[CH][LROW];
+    float alpha[CH], beta[CH];
+    float kk[CH][CH], qk[CH][CH];  // k_t.k_s, q_t.k_s
+    float A[CH][CH];               // strictly lower Gamma * K K^T
+    float Lq[CH][CH];              // lower incl. diagonal Gamma * Q K^T
+    float Tt[CH][CH];              // Tt[s][t] = T[t][s]
+    float gam[CH];                 // gamma_t
+    float gamC[CH];                // Gamma_{C-1, t}
+};
+
+struct MfmaArgs {
+    PoolView p;
+    const uint16_t *q, *k, *v;
+    const float *alpha, *beta;
+    float *out;
+    const int32_t *heads8;  // slot -> head, 8-bit pool
+    const int32_t *heads4;  // slot -> head, 4-bit pool
+    int n_tok;
+    int tiles8;  // B * n8: work items below this are 8-bit tiles
+    int tiles;   // B * H
+};
+
+__device__ inline float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ inline uint32_t pk_bf16(float lo, float hi) {
+    f32x2 x = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+__device__ inline float lo_f32(uint32_t pk) { return __uint_as_float(pk << 16); }
+__device__ inline float hi_f32(uint32_t pk) { return __uint_as_float(pk & 0xffff0000u); }
+
+// Order this wavefront's LDS accesses (no workgroup barrier: waves of a block
+// are independent; LDS operations of one wave execute in issue order).
+__device__ inline void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+__device__ inline f32x4 mfma_bf16_k32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline f32x4 mfma_bf16_k16(s16x4 a, s16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ inline f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ inline float xor_max(float x, int mask) {
+    return fmaxf(x, __shfl_xor(x, mask));
+}
+
+// low bytes of four words -> one word
+__device__ inline uint32_t gather_low_bytes(uint32_t y0, uint32_t y1, uint32_t y2, uint32_t y3) {
+    uint32_t a = __builtin_amdgcn_perm(y1, y0, 0x0c0c0400u);  // [y0.b0, y1.b0, 0, 0]
+    uint32_t b = __builtin_amdgcn_perm(y3, y2, 0x04000c0cu);  // [0, 0, y2.b0, y3.b0]
+    return a | b;
+}
+
+template <int DK>
+struct CodeChunk;
+template <>
+struct CodeChunk<128> {
+    static constexpr int NKS = 4, NRT = 8;
+};
+template <>
+struct CodeChunk<64> {
+    static constexpr int NKS = 2, NRT = 4;
+};
+
+template <int DK, int BITS>
+struct Loader {
+    // dwords a lane holds per column block: 4-bit: one per k-slice; 8-bit: one per row tile
+    static constexpr int ND = BITS == 4 ? DK / 32 : DK / 16;
+    uint32_t d[ND];
+    __device__ inline void load(const uint8_t *codes, int cb, int lane) {
+        if constexpr (BITS == 4) {
+            const uint8_t *p = codes + (size_t)cb * (64 * DK / 8) + (size_t)lane * (DK / 8);
+            if constexpr (DK == 128) {
+                u32x4 x = *(const u32x4 *)p;
+                d[0] = x[0], d[1] = x[1], d[2] = x[2], d[3] = x[3];
+            } else {
+                u32x2 x = *(const u32x2 *)p;
+                d[0] = x[0], d[1] = x[1];
+            }
+        } else {
+            const uint8_t *p = codes + (size_t)cb * (64 * DK / 4) + (size_t)lane * 16;
+#pragma unroll
+            for (int qd = 0; qd < DK / 64; ++qd) {
+                u32x4 x = *(const u32x4 *)(p + qd * 1024);
+                d[4 * qd + 0] = x[0], d[4 * qd + 1] = x[1], d[4 * qd + 2] = x[2], d[4 * qd + 3] = x[3];
+            }
+        }
+    }
+    __device__ inline void store(uint8_t *codes, int cb, int lane) const {
+        if constexpr (BITS == 4) {
+            uint8_t *p = codes + (size_t)cb * (64 * DK / 8) + (size_t)lane * (DK / 8);
+            if constexpr (DK == 128) {
+                u32x4 x = {d[0], d[1], d[2], d[3]};
+                *(u32x4 *)p = x;
+            } else {
+                u32x2 x = {d[0], d[1]};
+                *(u32x2 *)p = x;
+            }
+        } else {
+            uint8_t *p = codes + (size_t)cb * (64 * DK / 4) + (size_t)lane * 16;
+#pragma unroll
+            for (int qd = 0; qd < DK / 64; ++qd) {
+                u32x4 x = {d[4 * qd], d[4 * qd + 1], d[4 * qd + 2], d[4 * qd + 3]};
+                *(u32x4 *)(p + qd * 1024) = x;
+            }
+        }
+    }
+    // code of (row tile rt, row r in the lane's group) as float
+    __device__ inline float code(int rt, int r) const {
+        if constexpr (BITS == 4)
+            return (float)__builtin_amdgcn_sbfe(d[rt >> 1], 8 * r + 4 * (rt & 1), 4);
+        else
+            return (float)__builtin_amdgcn_sbfe(d[rt], 8 * r, 8);
+    }
+};
+
+template <int DK, int BITS>
+__device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int slot, int lane) {
+    constexpr int NKS = CodeChunk<DK>::NKS;  // k-slices of 32 rows
+    constexpr int NRT = CodeChunk<DK>::NRT;  // row tiles of 16 rows
+    constexpr int NCB = DK / 16;             // column blocks (d_v = d_k)
+    constexpr float QMAX = BITS == 4 ? 7.f : 127.f;
+    const int g = lane >> 4, n = lane & 15;
+    const int n_tok = a.n_tok;
+    const size_t tok_stride = (size_t)a.p.B * a.p.H;
+    const size_t tile_row = (size_t)b * a.p.H + h;
+
+    uint8_t *codes = BITS == 4
+        ? a.p.codes4 + ((size_t)b * a.p.n4 + slot) * tile_code_bytes(DK, DK, 4)
+        : a.p.codes8 + ((size_t)b * a.p.n8 + slot) * tile_code_bytes(DK, DK, 8);
+    float *scl = a.p.scales + tile_row * DK;
+
+    // first column block's codes and scale: issue early
+    Loader<DK, BITS> cur;
+    cur.load(codes, 0, lane);
+    float s_cur = scl[n];
+
+    // ---- stage the chunk's tokens in LDS (padding tokens: k = q = v = 0) ----
+    {
+        constexpr int CPR = DK / 8;  // 16-byte chunks per token row
+#pragma unroll
+        for (int c = lane; c < 24 * CPR; c += 64) {
+            const int row = c / CPR, col = (c % CPR) * 8;
+            const int t = row & 7, which = row >> 3;
+            const uint16_t *src = which == 0 ? a.k : which == 1 ? a.q : a.v;
+            u32x4 val = {0u, 0u, 0u, 0u};
+            if (t < n_tok) val = *(const u32x4 *)(src + ((size_t)t * tok_stride + tile_row) * DK + col);
+            uint16_t *dst = which < 2 ? &L.kq[which * 8 + t][col] : &L.v[t][col];
+            *(u32x4 *)dst = val;
+        }
+        if (lane < 16) {
+            const int t = lane & 7;
+            const bool is_beta = lane >= 8;
+            float x = is_beta ? 0.f : 1.f;
+            if (t < n_tok) x = (is_beta ? a.beta : a.alpha)[(size_t)t * tok_stride + tile_row];
+            if (is_beta)
+                L.beta[t] = x;
+            else
+                L.alpha[t] = x;
+        }
+    }
+    wave_sync();
+
+    // ---- [K;Q] as the MFMA A operand: A row m = 4 gg + rr holds k_gg, k_{4+gg},
+    //      q_gg, q_{4+gg} for rr = 0..3; k index e of slice ks is state row
+    //      32 ks + 16 (e / 4) + 4 g + e % 4 (this lane's rows of two row tiles) ----
+    bf16x8 AP[NKS];
+    {
+        const int gg = n >> 2, rr = n & 3;
+        const int krow = (rr == 0) ? gg : (rr == 1) ? 4 + gg : (rr == 2) ? 8 + gg : 12 + gg;
+        bf16x8 BG[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int c0 = 32 * ks + 4 * g, c1 = c0 + 16;
+            u32x2 r0 = *(const u32x2 *)&L.kq[krow][c0];
+            u32x2 r1 = *(const u32x2 *)&L.kq[krow][c1];
+            u32x4 w = {r0[0], r0[1], r1[0], r1[1]};
+            AP[ks] = __builtin_bit_cast(bf16x8, w);
+            u32x4 z = {0u, 0u, 0u, 0u};
+            if (n < 8) {
+                u32x2 s0 = *(const u32x2 *)&L.kq[n][c0];
+                u32x2 s1 = *(const u32x2 *)&L.kq[n][c1];
+                z = u32x4{s0[0], s0[1], s1[0], s1[1]};
+            }
+            BG[ks] = __builtin_bit_cast(bf16x8, z);
+        }
+        // G[m][n] = row m of [K;Q] . k_n
+        f32x4 G = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) G = mfma_bf16_k32(AP[ks], BG[ks], G);
+        if (n < 8) {
+            L.kk[g][n] = G[0];
+            L.kk[4 + g][n] = G[1];
+            L.qk[g][n] = G[2];
+            L.qk[4 + g][n] = G[3];
+        }
+    }
+    wave_sync();
+
+    // ---- gates: Gamma_ts as products of alpha (no log / exp), A and Lq ----
+    {
+        float al[CH];
+#pragma unroll
+        for (int r = 0; r < CH; ++r) al[r] = L.alpha[r];
+        const int t = lane >> 3, s = lane & 7;
+        float gts = 1.f;
+#pragma unroll
+        for (int r = 1; r < CH; ++r) gts *= (r > s && r <= t) ? al[r] : 1.f;
+        L.A[t][s] = s < t ? gts * L.kk[t][s] : 0.f;
+        L.Lq[t][s] = s <= t ? gts * L.qk[t][s] : 0.f;
+        if (lane < CH) {
+            float gm = 1.f, gc = 1.f;
+#pragma unroll
+            for (int r = 0; r < CH; ++r) {
+                gm *= r <= lane ? al[r] : 1.f;
+                gc *= r > lane ? al[r] : 1.f;
+            }
+            L.gam[lane] = gm;
+            L.gamC[lane] = gc;
+        }
+    }
+    wave_sync();
+
+    // ---- UT transform: column s of Z = (I + diag(beta) A)^-1 by forward
+    //      substitution; T = Z diag(beta) ----
+    {
+        const int s = lane & 7;
+        float be[CH], z[CH];
+#pragma unroll
+        for (int r = 0; r < CH; ++r) be[r] = L.beta[r];
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+            float sum = 0.f;
+#pragma unroll
+            for (int u = 0; u < t; ++u) sum = fmaf(L.A[t][u], z[u], sum);
+            z[t] = (t == s ? 1.f : 0.f) - be[t] * sum;
+        }
+        if (lane < CH) {
+#pragma unroll
+            for (int t = 0; t < CH; ++t) L.Tt[s][t] = z[t] * be[s];
+        }
+    }
+    wave_sync();
+
+    // ---- per-lane chain operands (A of the 16x16x4 float32 MFMAs) ----
+    // chain W: output row m -> token m % 8: A[m][k] = Gamma_{C-1,m%8} T[m%8][4 st + k]
+    const int t1 = lane & 7;
+    const float gct = L.gamC[t1];
+    const float R1_0 = gct * L.Tt[g][t1];
+    const float R1_1 = gct * L.Tt[4 + g][t1];
+    // chain O: rows m < 8 -> token m: A = (Lq T) for X, identity for Y
+    float R2_0 = 0.f, R2_1 = 0.f;
+    if (n < 8) {
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            const float lq = L.Lq[n][u];
+            R2_0 = fmaf(lq, L.Tt[g][u], R2_0);
+            R2_1 = fmaf(lq, L.Tt[4 + g][u], R2_1);
+        }
+    }
+    const float R2_2 = n == g ? 1.f : 0.f;
+    const float R2_3 = n == 4 + g ? 1.f : 0.f;
+    const float gam_g = L.gam[g], gam_4g = L.gam[4 + g], gamC = L.gam[CH - 1];
+
+    // K^T as the A operand of the update: row i = 16 rt + n, k index 4 g + e is
+    // token 4 (g % 2) + e (the same tokens for the hi / mid / lo parts)
+    s16x4 AU[NRT];
+    {
+        const int t0 = 4 * (g & 1);
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+            const int i = 16 * rt + n;
+            s16x4 x;
+            x[0] = (short)L.kq[t0 + 0][i];
+            x[1] = (short)L.kq[t0 + 1][i];
+            x[2] = (short)L.kq[t0 + 2][i];
+            x[3] = (short)L.kq[t0 + 3][i];
+            AU[rt] = x;
+        }
+    }
+
+    // ---- column blocks ----
+#pragma unroll 1
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int j = 16 * cb + n;
+        Loader<DK, BITS> nxt;
+        float s_nxt = 0.f;
+        if (cb + 1 < NCB) {
+            nxt.load(codes, cb + 1, lane);
+            s_nxt = scl[j + 16];
+        }
+        const float s = s_cur;
+
+        // codes -> float32 (the accumulator's start) and bf16 B operands
+        f32x4 acc[NRT];
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[rt][r] = cur.code(rt, r);
+
+        f32x4 P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            u32x4 w = {pk_bf16(acc[2 * ks][0], acc[2 * ks][1]), pk_bf16(acc[2 * ks][2], acc[2 * ks][3]),
+                       pk_bf16(acc[2 * ks + 1][0], acc[2 * ks + 1][1]),
+                       pk_bf16(acc[2 * ks + 1][2], acc[2 * ks + 1][3])};
+            P = mfma_bf16_k32(AP[ks], __builtin_bit_cast(bf16x8, w), P);
+        }
+        // P (code units): [k_g . c, k_{4+g} . c, q_g . c, q_{4+g} . c] for column j
+
+        const float sg = gam_g * s, s4g = gam_4g * s;
+        const float X0 = fmaf(-sg, P[0], bf2f(L.v[g][j]));
+        const float X1 = fmaf(-s4g, P[1], bf2f(L.v[4 + g][j]));
+        const float Y0 = sg * P[2];
+        const float Y1 = s4g * P[3];
+
+        // accumulate in units of sigma = gamma_C s (1 for a zero column)
+        const float sig_raw = gamC * s;
+        const bool tiny = s > 0.f && !(sig_raw >= 1.17549435e-38f);
+        const float sig = (s > 0.f && !tiny) ? sig_raw : 1.f;
+        if (__builtin_amdgcn_ballot_w64(tiny)) {
+            // decay below float32's normal range: start from gamma_C s c directly
+            const float m0 = tiny ? sig_raw : 1.f;
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) acc[rt] *= m0;
+        }
+        const float inv_sig = 1.f / sig;
+
+        f32x4 W = {0.f, 0.f, 0.f, 0.f};
+        W = mfma_f32_k4(R1_0, X0 * inv_sig, W);
+        W = mfma_f32_k4(R1_1, X1 * inv_sig, W);
+        f32x4 O = {0.f, 0.f, 0.f, 0.f};
+        O = mfma_f32_k4(R2_0, X0, O);
+        O = mfma_f32_k4(R2_1, X1, O);
+        O = mfma_f32_k4(R2_2, Y0, O);
+        O = mfma_f32_k4(R2_3, Y1, O);
+        if (g < 2) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * g + r;
+                if (t < n_tok) a.out[((size_t)t * tok_stride + tile_row) * DK + j] = O[r];
+            }
+        }
+
+        // W (tokens 4 (g % 2) + r) split exactly-enough into three bf16 parts
+        const uint32_t hi01 = pk_bf16(W[0], W[1]), hi23 = pk_bf16(W[2], W[3]);
+        const float r0 = W[0] - lo_f32(hi01), r1 = W[1] - hi_f32(hi01);
+        const float r2 = W[2] - lo_f32(hi23), r3 = W[3] - hi_f32(hi23);
+        const uint32_t md01 = pk_bf16(r0, r1), md23 = pk_bf16(r2, r3);
+        const uint32_t lo01 = pk_bf16(r0 - lo_f32(md01), r1 - hi_f32(md01));
+        const uint32_t lo23 = pk_bf16(r2 - lo_f32(md23), r3 - hi_f32(md23));
+        const bool first = g < 2;
+        u32x2 b1 = {first ? hi01 : md01, first ? hi23 : md23};
+        u32x2 b2 = {first ? lo01 : 0u, first ? lo23 : 0u};
+        const s16x4 B1 = __builtin_bit_cast(s16x4, b1);
+        const s16x4 B2 = __builtin_bit_cast(s16x4, b2);
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+            acc[rt] = mfma_bf16_k16(AU[rt], B1, acc[rt]);
+            acc[rt] = mfma_bf16_k16(AU[rt], B2, acc[rt]);
+        }
+
+        // ---- re-encode the column ----
+        float am = 0.f;
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) am = fmaxf(am, fabsf(acc[rt][r]));
+        am = xor_max(am, 16);
+        am = xor_max(am, 32);
+        const float absmax = am * sig;
+        const float s_new = absmax / QMAX;
+        const float ratio = s_new > 0.f ? sig / s_new : 0.f;
+        uint32_t y[NRT][4];
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y[rt][r] = __float_as_uint(fmaf(acc[rt][r], ratio, 12582912.f));
+        Loader<DK, BITS> outc;
+        if constexpr (BITS == 4) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const uint32_t lo = gather_low_bytes(y[2 * ks][0], y[2 * ks][1], y[2 * ks][2], y[2 * ks][3]);
+                const uint32_t hi = gather_low_bytes(y[2 * ks + 1][0], y[2 * ks + 1][1],
+                                                     y[2 * ks + 1][2], y[2 * ks + 1][3]);
+                outc.d[ks] = (lo & 0x0f0f0f0fu) | ((hi << 4) & 0xf0f0f0f0u);
+            }
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) outc.d[rt] = gather_low_bytes(y[rt][0], y[rt][1], y[rt][2], y[rt][3]);
+        }
+        outc.store(codes, cb, lane);
+        if (g == 0) scl[j] = s_new;
+
+        cur = nxt;
+        s_cur = s_nxt;
+    }
+}
+
+template <int DK>
+__global__ void __launch_bounds__(64 * WAVES) decode_mfma_kernel(MfmaArgs a) {
+    __shared__ WaveLds lds[WAVES];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int w = blockIdx.x * WAVES + wave;
+    if (w >= a.tiles) return;
+    if (w < a.tiles8) {
+        const int b = w / a.p.n8, slot = w % a.p.n8;
+        process_tile<DK, 8>(a, lds[wave], b, a.heads8[slot], slot, lane);
+    } else {
+        const int w4 = w - a.tiles8;
+        const int b = w4 / a.p.n4, slot = w4 % a.p.n4;
+        process_tile<DK, 4>(a, lds[wave], b, a.heads4[slot], slot, lane);
+    }
+}
+
+}  // namespace
+
+bool mfma_supported(int dk, int dv, int n_tok, int in_bf16) {
+    return in_bf16 && dk == dv && (dk == 128 || dk == 64) && n_tok >= 1 && n_tok <= CH;
+}
+
+hipError_t launch_decode_mfma(const PoolView &p, const int32_t *heads8, const int32_t *heads4,
+                              int n_tok, const void *q, const void *k, const void *v,
+                              const float *alpha, const float *beta, float *out, hipStream_t s) {
+    MfmaArgs a;
+    a.p = p;
+    a.q = (const uint16_t *)q;
+    a.k = (const uint16_t *)k;
+    a.v = (const uint16_t *)v;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.out = out;
+    a.heads8 = heads8;
+    a.heads4 = heads4;
+    a.n_tok = n_tok;
+    a.tiles8 = p.B * p.n8;
+    a.tiles = p.B * p.H;
+    dim3 grid((a.tiles + WAVES - 1) / WAVES), block(64 * WAVES);
+    if (p.dk == 128)
+        hipLaunchKernelGGL(decode_mfma_kernel<128>, grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL(decode_mfma_kernel<64>, grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace pace

@@ -1,0 +1,241 @@
+// Straightforward HIP kernels: one thread per state column.
+//
+// These are the reference-shaped device kernels: the period decode applies
+// tokens one at a time with the gated delta rule in float32 (the recurrence
+// in the form M_t = alpha (M - beta k (k^T M)) + beta k v^T, o_t = M_t^T q_t),
+// the encoder implements the per-column absmax quantizer, and the read and
+// prefill kernels serve checkpointing and warm-up.  The fused MFMA kernel in
+// decode_mfma.hip is the fast path; this file is its second opinion and the
+// fallback for shapes it does not cover (float32 inputs, d_v not 128).
+//
+// A thread owns one column j of one (sequence, head) state, so every code
+// byte it reads or writes belongs to its column only (see pace_layout.h) and
+// decode can update the pool in place without synchronisation between threads.
+#include "pace_layout.h"
+
+namespace pace {
+namespace {
+
+__device__ inline float ld_in(const void *p, size_t idx, int bf16) {
+    if (bf16) {
+        uint32_t u = ((const uint16_t *)p)[idx];
+        return __uint_as_float(u << 16);
+    }
+    return ((const float *)p)[idx];
+}
+
+template <int DK>
+__device__ inline void load_column(const uint8_t *codes, int bits, int j, float s, float M[DK]) {
+#pragma unroll
+    for (int i = 0; i < DK; ++i) {
+        int c;
+        if (bits == 4) {
+            int sh;
+            size_t o = loc4(DK, i, j, &sh);
+            c = ((int)((uint32_t)codes[o] << (28 - sh))) >> 28;  // sign-extend the nibble
+        } else {
+            c = (int)(int8_t)codes[loc8(DK, i, j)];
+        }
+        M[i] = (float)c * s;
+    }
+}
+
+// Per-column quantizer: s = absmax / qmax (float32, correctly rounded),
+// c = rint(M / s) with round-half-even, clamped to +-qmax; s = 0 -> codes 0.
+template <int DK>
+__device__ inline float store_column(uint8_t *codes, int bits, int j, const float M[DK]) {
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < DK; ++i) amax = fmaxf(amax, fabsf(M[i]));
+    const int qm = bits == 4 ? 7 : 127;
+    float s = amax / (float)qm;
+    if (bits == 4) {
+        // whole bytes: rows (2ks, r) and (2ks+1, r) of one lane group share a byte
+#pragma unroll
+        for (int i = 0; i < DK; ++i) {
+            int rt = i >> 4;
+            if (rt & 1) continue;
+            int i2 = i + 16;
+            int c0 = 0, c1 = 0;
+            if (s > 0.f) {
+                c0 = (int)fminf(fmaxf(rintf(M[i] / s), -7.f), 7.f);
+                c1 = (int)fminf(fmaxf(rintf(M[i2] / s), -7.f), 7.f);
+            }
+            int sh;
+            size_t o = loc4(DK, i, j, &sh);
+            codes[o] = (uint8_t)((c0 & 15) | ((c1 & 15) << 4));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < DK; ++i) {
+            int c = 0;
+            if (s > 0.f) c = (int)fminf(fmaxf(rintf(M[i] / s), -127.f), 127.f);
+            codes[loc8(DK, i, j)] = (uint8_t)(int8_t)c;
+        }
+    }
+    return s;
+}
+
+// Apply tokens t = 0..n_tok-1 to the column held in M; writes o_t if out != NULL.
+template <int DK>
+__device__ inline void apply_tokens(float M[DK], float *sk, float *sq, int n_tok, int B, int H,
+                                    int dv, int b, int h, int j, const void *q, const void *k,
+                                    const void *v, const float *alpha, const float *beta,
+                                    float *out, int bf16) {
+    for (int t = 0; t < n_tok; ++t) {
+        size_t base = (((size_t)t * B + b) * H + h);
+        __syncthreads();
+        for (int i = threadIdx.x; i < DK; i += blockDim.x) {
+            sk[i] = ld_in(k, base * DK + i, bf16);
+            sq[i] = ld_in(q, base * DK + i, bf16);
+        }
+        __syncthreads();
+        const float a = alpha[base], bt = beta[base];
+        const float vj = ld_in(v, base * dv + j, bf16);
+        float d = 0.f;
+#pragma unroll
+        for (int i = 0; i < DK; ++i) d = fmaf(sk[i], M[i], d);
+        float o = 0.f;
+#pragma unroll
+        for (int i = 0; i < DK; ++i) {
+            float bk = bt * sk[i];
+            M[i] = a * (M[i] - bk * d) + bk * vj;
+            o = fmaf(sq[i], M[i], o);
+        }
+        if (out) out[base * dv + j] = o;
+    }
+}
+
+template <int DK>
+__global__ void decode_v0_kernel(PoolView p, int n_tok, const void *q, const void *k,
+                                 const void *v, const float *alpha, const float *beta,
+                                 float *out, int bf16) {
+    __shared__ float sk[DK], sq[DK];
+    const int tile = blockIdx.x, b = tile / p.H, h = tile % p.H, j = threadIdx.x;
+    int bits;
+    uint8_t *codes = tile_codes(p, b, h, &bits);
+    float *sc = p.scales + (size_t)tile * p.dv;
+    float M[DK];
+    load_column<DK>(codes, bits, j, sc[j], M);
+    apply_tokens<DK>(M, sk, sq, n_tok, p.B, p.H, p.dv, b, h, j, q, k, v, alpha, beta, out, bf16);
+    sc[j] = store_column<DK>(codes, bits, j, M);
+}
+
+template <int DK>
+__global__ void encode_f32_kernel(PoolView p, const float *src) {
+    const int tile = blockIdx.x, b = tile / p.H, h = tile % p.H, j = threadIdx.x;
+    int bits;
+    uint8_t *codes = tile_codes(p, b, h, &bits);
+    const float *m = src + (size_t)tile * DK * p.dv;
+    float M[DK];
+#pragma unroll
+    for (int i = 0; i < DK; ++i) M[i] = m[(size_t)i * p.dv + j];
+    p.scales[(size_t)tile * p.dv + j] = store_column<DK>(codes, bits, j, M);
+}
+
+template <int DK>
+__global__ void prefill_v0_kernel(int B, int H, int dv, int n_tok, int bf16, const void *q,
+                                  const void *k, const void *v, const float *alpha,
+                                  const float *beta, float *state, float *out) {
+    __shared__ float sk[DK], sq[DK];
+    const int tile = blockIdx.x, b = tile / H, h = tile % H, j = threadIdx.x;
+    float *m = state + (size_t)tile * DK * dv;
+    float M[DK];
+#pragma unroll
+    for (int i = 0; i < DK; ++i) M[i] = m[(size_t)i * dv + j];
+    apply_tokens<DK>(M, sk, sq, n_tok, B, H, dv, b, h, j, q, k, v, alpha, beta, out, bf16);
+#pragma unroll
+    for (int i = 0; i < DK; ++i) m[(size_t)i * dv + j] = M[i];
+}
+
+// what: 0 = codes to int8 [B,H,dk,dv] + scales, 1 = dequantized float32
+template <int DK>
+__global__ void read_kernel(PoolView p, int what, void *dst, float *sdst) {
+    const int tile = blockIdx.x, b = tile / p.H, h = tile % p.H, j = threadIdx.x;
+    int bits;
+    const uint8_t *codes = tile_codes(p, b, h, &bits);
+    const float s = p.scales[(size_t)tile * p.dv + j];
+    for (int i = 0; i < DK; ++i) {
+        int c;
+        if (bits == 4) {
+            int sh;
+            size_t o = loc4(DK, i, j, &sh);
+            c = ((int)((uint32_t)codes[o] << (28 - sh))) >> 28;
+        } else {
+            c = (int)(int8_t)codes[loc8(DK, i, j)];
+        }
+        size_t o = ((size_t)tile * DK + i) * p.dv + j;
+        if (what == 0)
+            ((int8_t *)dst)[o] = (int8_t)c;
+        else
+            ((float *)dst)[o] = (float)c * s;
+    }
+    if (sdst) sdst[(size_t)tile * p.dv + j] = s;
+}
+
+__global__ void count_zero_kernel(const float *scales, size_t n, unsigned long long *counter) {
+    unsigned int mine = 0;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (size_t)gridDim.x * blockDim.x)
+        mine += scales[i] == 0.f;
+    for (int off = 32; off > 0; off >>= 1) mine += __shfl_xor(mine, off);
+    if ((threadIdx.x & 63) == 0 && mine) atomicAdd(counter, (unsigned long long)mine);
+}
+
+}  // namespace
+
+hipError_t launch_decode_v0(const PoolView &p, int n_tok, const void *q, const void *k,
+                            const void *v, const float *alpha, const float *beta, float *out,
+                            int in_bf16, hipStream_t s) {
+    dim3 grid(p.B * p.H), block(p.dv);
+    if (p.dk == 128)
+        hipLaunchKernelGGL(decode_v0_kernel<128>, grid, block, 0, s, p, n_tok, q, k, v, alpha,
+                           beta, out, in_bf16);
+    else
+        hipLaunchKernelGGL(decode_v0_kernel<64>, grid, block, 0, s, p, n_tok, q, k, v, alpha,
+                           beta, out, in_bf16);
+    return hipGetLastError();
+}
+
+hipError_t launch_encode_f32(const PoolView &p, const float *src, hipStream_t s) {
+    dim3 grid(p.B * p.H), block(p.dv);
+    if (p.dk == 128)
+        hipLaunchKernelGGL(encode_f32_kernel<128>, grid, block, 0, s, p, src);
+    else
+        hipLaunchKernelGGL(encode_f32_kernel<64>, grid, block, 0, s, p, src);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_v0(int B, int H, int dk, int dv, int n_tok, int in_bf16,
+                             const void *q, const void *k, const void *v, const float *alpha,
+                             const float *beta, float *state, float *out, hipStream_t s) {
+    dim3 grid(B * H), block(dv);
+    if (dk == 128)
+        hipLaunchKernelGGL(prefill_v0_kernel<128>, grid, block, 0, s, B, H, dv, n_tok, in_bf16,
+                           q, k, v, alpha, beta, state, out);
+    else
+        hipLaunchKernelGGL(prefill_v0_kernel<64>, grid, block, 0, s, B, H, dv, n_tok, in_bf16,
+                           q, k, v, alpha, beta, state, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_read(const PoolView &p, int what, void *dst, float *scales_dst,
+                       hipStream_t s) {
+    dim3 grid(p.B * p.H), block(p.dv);
+    if (p.dk == 128)
+        hipLaunchKernelGGL(read_kernel<128>, grid, block, 0, s, p, what, dst, scales_dst);
+    else
+        hipLaunchKernelGGL(read_kernel<64>, grid, block, 0, s, p, what, dst, scales_dst);
+    return hipGetLastError();
+}
+
+hipError_t launch_count_zero_scales(const PoolView &p, unsigned long long *counter,
+                                    hipStream_t s) {
+    size_t n = (size_t)p.B * p.H * p.dv;
+    int blocks = (int)((n + 255) / 256);
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(count_zero_kernel, dim3(blocks), dim3(256), 0, s, p.scales, n, counter);
+    return hipGetLastError();
+}
+
+}  // namespace pace

@@ -1,0 +1,331 @@
+// C ABI of the PACE decode library: argument validation, pool ownership and
+// kernel dispatch.  Every check runs before the first HIP call; HIP errors are
+// turned into PACE_EDEVICE / PACE_ENOMEM with a thread-local message.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <new>
+#include <string>
+#include <vector>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/pace.h"
+#include "pace_layout.h"
+#include "pace_mfma.h"
+
+#define PACE_API extern "C" __attribute__((visibility("default")))
+
+struct pace_state {
+    pace_config cfg;
+    std::vector<uint8_t> bits;
+    std::vector<int32_t> map;  // host copy of the head map
+    int device = 0;
+    int n4 = 0, n8 = 0;
+    int32_t *d_map = nullptr;
+    uint8_t *codes4 = nullptr;
+    uint8_t *codes8 = nullptr;
+    float *scales = nullptr;
+    unsigned long long *d_counter = nullptr;
+    size_t bytes4 = 0, bytes8 = 0, bytes_scales = 0;
+    uint64_t periods = 0, tokens = 0;
+
+    pace::PoolView view() const {
+        pace::PoolView p;
+        p.codes4 = codes4;
+        p.codes8 = codes8;
+        p.scales = scales;
+        p.head_map = d_map;
+        p.B = cfg.batch;
+        p.H = cfg.heads;
+        p.dk = cfg.d_k;
+        p.dv = cfg.d_v;
+        p.n4 = n4;
+        p.n8 = n8;
+        return p;
+    }
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return PACE_OK;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    // clear the runtime's sticky last-error so that the caller's next HIP
+    // launch (ours or another library's) does not report this failure again
+    (void)hipGetLastError();
+    if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation)
+        return fail(PACE_ENOMEM, "%s: %s", what, hipGetErrorString(e));
+    return fail(PACE_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_shape(int32_t batch, int32_t heads, int32_t d_k, int32_t d_v) {
+    if (batch < 1 || heads < 1) return fail(PACE_EINVAL, "batch and heads must be >= 1");
+    if (d_k < 1 || d_v < 1) return fail(PACE_EINVAL, "d_k and d_v must be >= 1");
+    if ((int64_t)batch * heads > (int64_t)1 << 30)
+        return fail(PACE_EINVAL, "batch * heads too large");
+    if (d_k != 64 && d_k != 128) return fail(PACE_EUNSUPPORTED, "d_k must be 64 or 128");
+    if (d_v % 16 != 0 || d_v > 256) return fail(PACE_EUNSUPPORTED, "d_v must be a multiple of 16 up to 256");
+    return PACE_OK;
+}
+
+int check_dtype(int32_t dt) {
+    if (dt != PACE_DTYPE_F32 && dt != PACE_DTYPE_BF16)
+        return fail(PACE_EINVAL, "in_dtype must be PACE_DTYPE_F32 or PACE_DTYPE_BF16");
+    return PACE_OK;
+}
+
+int check_tokens(int32_t n_tok, int32_t in_dtype, const void *q, const void *k, const void *v,
+                 const float *alpha, const float *beta) {
+    if (!q || !k || !v || !alpha || !beta) return fail(PACE_EINVAL, "null input pointer");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+        return fail(PACE_EINVAL, "q, k, v must be 16-byte aligned");
+    if (!aligned(alpha, 4) || !aligned(beta, 4))
+        return fail(PACE_EINVAL, "alpha, beta must be 4-byte aligned");
+    (void)n_tok;
+    (void)in_dtype;
+    return PACE_OK;
+}
+
+}  // namespace
+
+PACE_API int pace_abi_version(void) { return PACE_ABI_VERSION; }
+
+PACE_API const char *pace_last_error(void) { return g_err.c_str(); }
+
+PACE_API int pace_state_alloc(const pace_config *cfg, int init_kind, const void *init,
+                              void *stream, pace_state **out) {
+    if (!cfg || !out) return fail(PACE_EINVAL, "cfg and out must not be NULL");
+    int rc = check_shape(cfg->batch, cfg->heads, cfg->d_k, cfg->d_v);
+    if (rc) return rc;
+    if (cfg->period < 1 || cfg->period > 64) return fail(PACE_EUNSUPPORTED, "period must be 1..64");
+    if ((rc = check_dtype(cfg->in_dtype))) return rc;
+    if (cfg->flags != 0) return fail(PACE_EINVAL, "flags must be 0");
+    if (!cfg->head_bits) return fail(PACE_EINVAL, "head_bits must not be NULL");
+    for (int h = 0; h < cfg->heads; ++h)
+        if (cfg->head_bits[h] != 4 && cfg->head_bits[h] != 8)
+            return fail(PACE_EINVAL, "head_bits[%d] = %d; must be 4 or 8", h, cfg->head_bits[h]);
+    if (init_kind == PACE_INIT_ZERO) {
+        if (init) return fail(PACE_EINVAL, "PACE_INIT_ZERO takes init = NULL");
+    } else if (init_kind == PACE_INIT_F32) {
+        if (!init || !aligned(init, 16)) return fail(PACE_EINVAL, "PACE_INIT_F32 needs a 16-byte aligned device pointer");
+    } else if (init_kind == PACE_INIT_RAW) {
+        if (!init) return fail(PACE_EINVAL, "PACE_INIT_RAW needs a device pointer");
+    } else {
+        return fail(PACE_EINVAL, "unknown init_kind %d", init_kind);
+    }
+
+    pace_state *st = new (std::nothrow) pace_state();
+    if (!st) return fail(PACE_ENOMEM, "host allocation failed");
+    st->cfg = *cfg;
+    st->bits.assign(cfg->head_bits, cfg->head_bits + cfg->heads);
+    st->cfg.head_bits = st->bits.data();
+    st->map.resize(cfg->heads);
+    std::vector<int32_t> h8, h4;
+    for (int h = 0; h < cfg->heads; ++h) {
+        int b = st->bits[h];
+        int slot = b == 4 ? st->n4++ : st->n8++;
+        st->map[h] = slot | (b << 16);
+        (b == 4 ? h4 : h8).push_back(h);
+    }
+    // device copy: [H] head map, then the head of each 8-bit slot, then of each 4-bit slot
+    st->map.insert(st->map.end(), h8.begin(), h8.end());
+    st->map.insert(st->map.end(), h4.begin(), h4.end());
+    const size_t tiles_b = (size_t)cfg->batch;
+    st->bytes4 = tiles_b * st->n4 * pace::tile_code_bytes(cfg->d_k, cfg->d_v, 4);
+    st->bytes8 = tiles_b * st->n8 * pace::tile_code_bytes(cfg->d_k, cfg->d_v, 8);
+    st->bytes_scales = tiles_b * cfg->heads * cfg->d_v * sizeof(float);
+
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    auto cleanup = [&](int code, const char *what, hipError_t err) {
+        if (st->codes4) (void)hipFree(st->codes4);
+        if (st->codes8) (void)hipFree(st->codes8);
+        if (st->scales) (void)hipFree(st->scales);
+        if (st->d_map) (void)hipFree(st->d_map);
+        if (st->d_counter) (void)hipFree(st->d_counter);
+        delete st;
+        (void)code;
+        return hip_fail(err, what);
+    };
+    if ((e = hipGetDevice(&st->device)) != hipSuccess) return cleanup(0, "hipGetDevice", e);
+    if (st->bytes4 && (e = hipMalloc((void **)&st->codes4, st->bytes4)) != hipSuccess)
+        return cleanup(0, "hipMalloc(codes4)", e);
+    if (st->bytes8 && (e = hipMalloc((void **)&st->codes8, st->bytes8)) != hipSuccess)
+        return cleanup(0, "hipMalloc(codes8)", e);
+    if ((e = hipMalloc((void **)&st->scales, st->bytes_scales)) != hipSuccess)
+        return cleanup(0, "hipMalloc(scales)", e);
+    if ((e = hipMalloc((void **)&st->d_map, sizeof(int32_t) * st->map.size())) != hipSuccess)
+        return cleanup(0, "hipMalloc(head map)", e);
+    if ((e = hipMalloc((void **)&st->d_counter, sizeof(unsigned long long))) != hipSuccess)
+        return cleanup(0, "hipMalloc(counter)", e);
+    if ((e = hipMemcpyAsync(st->d_map, st->map.data(), sizeof(int32_t) * st->map.size(),
+                            hipMemcpyHostToDevice, s)) != hipSuccess)
+        return cleanup(0, "copy head map", e);
+
+    if (init_kind == PACE_INIT_ZERO) {
+        if (st->bytes4 && (e = hipMemsetAsync(st->codes4, 0, st->bytes4, s)) != hipSuccess)
+            return cleanup(0, "zero codes4", e);
+        if (st->bytes8 && (e = hipMemsetAsync(st->codes8, 0, st->bytes8, s)) != hipSuccess)
+            return cleanup(0, "zero codes8", e);
+        if ((e = hipMemsetAsync(st->scales, 0, st->bytes_scales, s)) != hipSuccess)
+            return cleanup(0, "zero scales", e);
+    } else if (init_kind == PACE_INIT_F32) {
+        if ((e = pace::launch_encode_f32(st->view(), (const float *)init, s)) != hipSuccess)
+            return cleanup(0, "encode kernel", e);
+    } else {
+        const uint8_t *src = (const uint8_t *)init;
+        if (st->bytes4 && (e = hipMemcpyAsync(st->codes4, src, st->bytes4, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+            return cleanup(0, "raw copy codes4", e);
+        src += st->bytes4;
+        if (st->bytes8 && (e = hipMemcpyAsync(st->codes8, src, st->bytes8, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+            return cleanup(0, "raw copy codes8", e);
+        src += st->bytes8;
+        if ((e = hipMemcpyAsync(st->scales, src, st->bytes_scales, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+            return cleanup(0, "raw copy scales", e);
+    }
+    // the host copy of the head map must outlive the async copy: wait for it
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return cleanup(0, "initialisation", e);
+    *out = st;
+    return ok();
+}
+
+PACE_API int pace_state_free(pace_state *st) {
+    if (!st) return ok();
+    hipError_t e = hipDeviceSynchronize();
+    if (st->codes4) (void)hipFree(st->codes4);
+    if (st->codes8) (void)hipFree(st->codes8);
+    if (st->scales) (void)hipFree(st->scales);
+    if (st->d_map) (void)hipFree(st->d_map);
+    if (st->d_counter) (void)hipFree(st->d_counter);
+    delete st;
+    if (e != hipSuccess) return hip_fail(e, "pace_state_free");
+    return ok();
+}
+
+PACE_API int pace_state_config(const pace_state *st, pace_config *out) {
+    if (!st || !out) return fail(PACE_EINVAL, "null argument");
+    *out = st->cfg;
+    return ok();
+}
+
+PACE_API int pace_raw_bytes(const pace_state *st, uint64_t *out) {
+    if (!st || !out) return fail(PACE_EINVAL, "null argument");
+    *out = st->bytes4 + st->bytes8 + st->bytes_scales;
+    return ok();
+}
+
+PACE_API int pace_decode_period(pace_state *st, int32_t n_tok, const void *q, const void *k,
+                                const void *v, const float *alpha, const float *beta,
+                                float *out, void *stream) {
+    if (!st) return fail(PACE_EINVAL, "null state handle");
+    if (n_tok < 1 || n_tok > st->cfg.period)
+        return fail(PACE_EINVAL, "n_tok = %d outside 1..period (%d)", n_tok, st->cfg.period);
+    int rc = check_tokens(n_tok, st->cfg.in_dtype, q, k, v, alpha, beta);
+    if (rc) return rc;
+    if (!out || !aligned(out, 16)) return fail(PACE_EINVAL, "out must be a 16-byte aligned device pointer");
+    hipStream_t s = (hipStream_t)stream;
+    const int bf16 = st->cfg.in_dtype == PACE_DTYPE_BF16;
+    hipError_t e;
+    if (pace::mfma_supported(st->cfg.d_k, st->cfg.d_v, n_tok, bf16))
+        e = pace::launch_decode_mfma(st->view(), st->d_map + st->cfg.heads,
+                                     st->d_map + st->cfg.heads + st->n8, n_tok, q, k, v, alpha,
+                                     beta, out, s);
+    else
+        e = pace::launch_decode_v0(st->view(), n_tok, q, k, v, alpha, beta, out, bf16, s);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    st->periods += 1;
+    st->tokens += (uint64_t)n_tok;
+    return ok();
+}
+
+PACE_API int pace_read_state(const pace_state *st, int what, void *dst, float *scales_dst,
+                             void *stream) {
+    if (!st) return fail(PACE_EINVAL, "null state handle");
+    if (!dst) return fail(PACE_EINVAL, "dst must not be NULL");
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (what == PACE_READ_CODES) {
+        if (!scales_dst) return fail(PACE_EINVAL, "PACE_READ_CODES needs scales_dst");
+        e = pace::launch_read(st->view(), 0, dst, scales_dst, s);
+    } else if (what == PACE_READ_DEQUANT) {
+        e = pace::launch_read(st->view(), 1, dst, scales_dst, s);
+    } else if (what == PACE_READ_RAW) {
+        if (scales_dst) return fail(PACE_EINVAL, "PACE_READ_RAW takes scales_dst = NULL");
+        uint8_t *d = (uint8_t *)dst;
+        e = hipSuccess;
+        if (st->bytes4) e = hipMemcpyAsync(d, st->codes4, st->bytes4, hipMemcpyDeviceToDevice, s);
+        d += st->bytes4;
+        if (e == hipSuccess && st->bytes8)
+            e = hipMemcpyAsync(d, st->codes8, st->bytes8, hipMemcpyDeviceToDevice, s);
+        d += st->bytes8;
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(d, st->scales, st->bytes_scales, hipMemcpyDeviceToDevice, s);
+    } else {
+        return fail(PACE_EINVAL, "unknown read kind %d", what);
+    }
+    if (e != hipSuccess) return hip_fail(e, "read_state");
+    return ok();
+}
+
+PACE_API int pace_quant_stats(const pace_state *st, pace_stats *out, void *stream) {
+    if (!st || !out) return fail(PACE_EINVAL, "null argument");
+    hipStream_t s = (hipStream_t)stream;
+    const pace_config &c = st->cfg;
+    pace_stats r = {};
+    r.bytes_codes4 = st->bytes4;
+    r.bytes_codes8 = st->bytes8;
+    r.bytes_scales = st->bytes_scales;
+    r.bytes_total = st->bytes4 + st->bytes8 + st->bytes_scales;
+    r.bytes_fp16_equiv = (uint64_t)c.batch * c.heads * c.d_k * c.d_v * 2;
+    r.bytes_int8_equiv = (uint64_t)c.batch * c.heads * c.d_k * c.d_v + st->bytes_scales;
+    r.heads4 = st->n4;
+    r.heads8 = st->n8;
+    r.periods = st->periods;
+    r.tokens = st->tokens;
+    unsigned long long zeros = 0;
+    hipError_t e = hipMemsetAsync(st->d_counter, 0, sizeof zeros, s);
+    if (e == hipSuccess) e = pace::launch_count_zero_scales(st->view(), st->d_counter, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(&zeros, st->d_counter, sizeof zeros, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "quant_stats");
+    r.zero_columns = zeros;
+    *out = r;
+    return ok();
+}
+
+PACE_API int pace_prefill_f32(int32_t batch, int32_t heads, int32_t d_k, int32_t d_v,
+                              int32_t n_tok, int32_t in_dtype, const void *q, const void *k,
+                              const void *v, const float *alpha, const float *beta,
+                              float *state, float *out, void *stream) {
+    int rc = check_shape(batch, heads, d_k, d_v);
+    if (rc) return rc;
+    if ((rc = check_dtype(in_dtype))) return rc;
+    if (n_tok < 1) return fail(PACE_EINVAL, "n_tok must be >= 1");
+    if ((rc = check_tokens(n_tok, in_dtype, q, k, v, alpha, beta))) return rc;
+    if (!state || !aligned(state, 16)) return fail(PACE_EINVAL, "state must be a 16-byte aligned device pointer");
+    if (out && !aligned(out, 16)) return fail(PACE_EINVAL, "out must be 16-byte aligned");
+    hipError_t e = pace::launch_prefill_v0(batch, heads, d_k, d_v, n_tok,
+                                           in_dtype == PACE_DTYPE_BF16, q, k, v, alpha, beta,
+                                           state, out, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    return ok();
+}

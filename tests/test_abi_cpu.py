@@ -1,0 +1,94 @@
+"""The C ABI library: it loads, exports what include/pace.h declares, and
+rejects bad arguments before touching the device (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attn_decode_pace_amd import pace
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "pace.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pace_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(pace.LIB, n), n
+    assert sorted(pace.EXPORTED) == names
+
+
+def test_abi_version():
+    assert pace.pace_abi_version() == 1
+
+
+def _cfg(**kw):
+    c = dict(batch=2, heads=2, d_k=128, d_v=128, period=8, in_dtype=pace.PACE_DTYPE_BF16,
+             head_bits=[4, 8])
+    c.update(kw)
+    return c
+
+
+def _alloc_status(init_kind=pace.PACE_INIT_ZERO, init=None, **kw):
+    c = _cfg(**kw)
+    hb = (ctypes.c_uint8 * len(c["head_bits"]))(*c["head_bits"])
+    cfg = pace.pace_config(c["batch"], c["heads"], c["d_k"], c["d_v"], c["period"], c["in_dtype"],
+                           ctypes.cast(hb, ctypes.POINTER(ctypes.c_uint8)), 0)
+    out = ctypes.c_void_p()
+    return pace.LIB.pace_state_alloc(ctypes.byref(cfg), init_kind, init, None, ctypes.byref(out))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), pace.PACE_EINVAL),
+    (dict(heads=0, head_bits=[]), pace.PACE_EINVAL),
+    (dict(d_k=96), pace.PACE_EUNSUPPORTED),
+    (dict(d_v=100), pace.PACE_EUNSUPPORTED),
+    (dict(d_v=512), pace.PACE_EUNSUPPORTED),
+    (dict(period=0), pace.PACE_EUNSUPPORTED),
+    (dict(period=65), pace.PACE_EUNSUPPORTED),
+    (dict(in_dtype=7), pace.PACE_EINVAL),
+    (dict(head_bits=[4, 6]), pace.PACE_EINVAL),
+])
+def test_alloc_rejects_bad_config(kw, status):
+    assert _alloc_status(**kw) == status
+    assert pace.pace_last_error() != ""
+
+
+def test_alloc_rejects_bad_init():
+    assert _alloc_status(init_kind=9) == pace.PACE_EINVAL
+    assert _alloc_status(init_kind=pace.PACE_INIT_F32, init=None) == pace.PACE_EINVAL
+    assert _alloc_status(init_kind=pace.PACE_INIT_F32, init=0x1004) == pace.PACE_EINVAL  # misaligned
+    assert _alloc_status(init_kind=pace.PACE_INIT_ZERO, init=0x1000) == pace.PACE_EINVAL
+
+
+def test_null_arguments():
+    assert pace.LIB.pace_state_alloc(None, 0, None, None, None) == pace.PACE_EINVAL
+    assert pace.LIB.pace_decode_period(None, 1, 16, 16, 16, 16, 16, 16, None) == pace.PACE_EINVAL
+    assert pace.LIB.pace_read_state(None, 0, 16, 16, None) == pace.PACE_EINVAL
+    assert pace.LIB.pace_quant_stats(None, None, None) == pace.PACE_EINVAL
+    assert pace.LIB.pace_raw_bytes(None, None) == pace.PACE_EINVAL
+    assert pace.LIB.pace_state_free(None) == pace.PACE_OK
+
+
+def test_prefill_rejects_bad_arguments():
+    f = pace.LIB.pace_prefill_f32
+    good = (16, 32, 48, 64, 80)
+    assert f(1, 1, 128, 128, 1, 9, *good, 96, None, None) == pace.PACE_EINVAL
+    assert f(1, 1, 128, 128, 0, 1, *good, 96, None, None) == pace.PACE_EINVAL
+    assert f(1, 1, 96, 128, 1, 1, *good, 96, None, None) == pace.PACE_EUNSUPPORTED
+    assert f(1, 1, 128, 128, 1, 1, 17, 32, 48, 64, 80, 96, None, None) == pace.PACE_EINVAL
+    assert f(1, 1, 128, 128, 1, 1, *good, None, None, None) == pace.PACE_EINVAL
+    assert f(1, 1, 128, 128, 1, 1, *good, 100, None, None) == pace.PACE_EINVAL
+
+
+def test_binding_raises_with_message():
+    with pytest.raises(pace.PaceError) as e:
+        pace.pace_state_alloc(1, 1, 96, 128, 8, pace.PACE_DTYPE_BF16, [4], stream=0)
+    assert e.value.status == pace.PACE_EUNSUPPORTED and "d_k" in e.value.message

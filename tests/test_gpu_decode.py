@@ -1,0 +1,45 @@
+"""Period decode on the GPU against the float64 oracle (through the C ABI)."""
+import numpy as np
+import pytest
+
+from linear_attn_decode_pace_amd import inputs
+from tests.gpu_cases import default_calls, run_case
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_full_run():
+    # B=4, H=2, d=64, period 4, 64 decode steps, float32 inputs, all heads 4-bit
+    w = inputs.TINY
+    r = run_case(w, 0, default_calls(w))
+    assert r["tiles"] == 8 and r["calls"] == 16
+
+
+def test_bf16_mixed_ragged():
+    # odd batch and head counts, 2 of 5 heads at 8 bits, outlier value channels,
+    # and a short final call (a shorter last period)
+    w = inputs.ragged("ragged-mixed", 101, B=3, H=5, n_int8=2, n_outliers=8, steps=29)
+    calls = default_calls(w, 3) + [(24, 29)]
+    run_case(w, 1, calls)
+
+
+def test_bf16_d64_mixed():
+    w = inputs.ragged("d64-mixed", 102, B=5, H=4, dk=64, dv=64, n_int8=1, steps=24)
+    run_case(w, 2, default_calls(w))
+
+
+@pytest.mark.parametrize("period", [1, 2, 4, 8, 16])
+def test_period_sweep_small(period):
+    # the period sweep of the 256-sequence workload, on a 6-sequence batch
+    w = inputs.SWEEP.replace(B=6, period=period, steps=16)
+    run_case(w, 3, default_calls(w), label=f"sweep-k{period}")
+
+
+def test_all_heads_int8():
+    w = inputs.ragged("all8", 103, B=2, H=3, n_int8=3, steps=16)
+    run_case(w, 4, default_calls(w))
+
+
+def test_f32_inputs_d128():
+    w = inputs.ragged("f32-d128", 104, B=2, H=3, n_int8=1, dtype=inputs.DT_F32, steps=16)
+    run_case(w, 5, default_calls(w))

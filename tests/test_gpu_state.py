@@ -1,0 +1,157 @@
+"""State handling on the GPU: checkpoint/resume, determinism, reads, stats, prefill."""
+import numpy as np
+import pytest
+
+from linear_attn_decode_pace_amd import inputs
+from oracle import gdn, quant
+from oracle import pace as opace
+from tests import parity
+from tests.gpu_cases import say, tok_tiles
+
+pytestmark = pytest.mark.gpu
+
+W = inputs.ragged("state-mixed", 201, B=3, H=4, n_int8=1, n_outliers=8, steps=24)
+
+
+def _state(w, seed, kind=None):
+    from linear_attn_decode_pace_amd import pace, runtime
+    bits = inputs.head_bits(w, seed)
+    if kind is None:
+        return runtime.State(w, bits, pace.PACE_INIT_F32, runtime.warmup_state(w, seed)), bits
+    return runtime.State(w, bits, kind), bits
+
+
+def _decode(st, w, seed, p):
+    from linear_attn_decode_pace_amd import runtime
+    tok = inputs.decode_period(w, seed, p)
+    out = runtime.out_buffer(w, tok.T)
+    st.decode(runtime.DeviceTokens(tok), out)
+    return out
+
+
+def test_raw_resume_is_bitwise():
+    import torch
+    from linear_attn_decode_pace_amd import pace, runtime
+    say("[case] raw resume")
+    a, bits = _state(W, 0)
+    _decode(a, W, 0, 0)
+    _decode(a, W, 0, 1)
+    raw = a.read_raw()
+    b = runtime.State(W, bits, pace.PACE_INIT_RAW, raw)
+    assert torch.equal(b.read_raw(), raw)
+    oa = _decode(a, W, 0, 2)
+    ob = _decode(b, W, 0, 2)
+    assert torch.equal(oa, ob)
+    assert torch.equal(a.read_raw(), b.read_raw())
+
+
+def test_two_runs_are_bitwise_equal():
+    import torch
+    say("[case] determinism")
+    outs, raws = [], []
+    for _ in range(2):
+        st, _ = _state(W, 1)
+        o = [_decode(st, W, 1, p) for p in range(3)]
+        outs.append(torch.cat(o))
+        raws.append(st.read_raw())
+        st.free()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(raws[0], raws[1])
+
+
+def test_read_dequant_is_codes_times_scales():
+    import torch
+    st, _ = _state(W, 2)
+    _decode(st, W, 2, 0)
+    c, s = st.read_codes()
+    m = st.read_dequant()
+    ref = c.float() * s[:, :, None, :]
+    assert torch.equal(m, ref)
+
+
+def test_raw_layout_holds_the_codes():
+    # the raw image is [4-bit pool | 8-bit pool | scales]; its scales part equals the read scales
+    import torch
+    st, bits = _state(W, 3)
+    raw = st.read_raw()
+    _, s = st.read_codes()
+    n_sc = W.B * W.H * W.dv * 4
+    assert torch.equal(raw[-n_sc:].view(torch.float32).reshape(s.shape), s)
+    n4 = int((bits == 4).sum())
+    n8 = int((bits == 8).sum())
+    assert raw.numel() == W.B * (n4 * W.dk * W.dv // 2 + n8 * W.dk * W.dv) + n_sc
+
+
+def test_stats_closed_forms():
+    from linear_attn_decode_pace_amd import pace
+    w = inputs.MIXED.replace(B=8)
+    st, bits = _state(w, 4)
+    s = st.stats()
+    d = w.dk
+    assert s["heads4"] == 12 and s["heads8"] == 4
+    assert s["bytes_codes4"] == w.B * 12 * d * d // 2
+    assert s["bytes_codes8"] == w.B * 4 * d * d
+    assert s["bytes_scales"] == w.B * w.H * d * 4
+    assert s["bytes_total"] == s["bytes_codes4"] + s["bytes_codes8"] + s["bytes_scales"]
+    assert s["bytes_fp16_equiv"] == w.B * w.H * d * d * 2
+    ratio = s["bytes_total"] / s["bytes_int8_equiv"]
+    assert abs(ratio - 1344 / 2112) < 1e-12          # about two thirds of all-8-bit
+    assert s["zero_columns"] == 0 and s["periods"] == 0
+    _decode(st, w, 4, 0)
+    s = st.stats()
+    assert s["periods"] == 1 and s["tokens"] == w.period
+    st.free()
+    z, _ = _state(w, 4, pace.PACE_INIT_ZERO)
+    assert z.stats()["zero_columns"] == w.B * w.H * w.dv
+
+
+def test_zero_state_decode():
+    from linear_attn_decode_pace_amd import pace
+    w = W
+    st, bits = _state(w, 5, pace.PACE_INIT_ZERO)
+    n = w.B * w.H
+    bits_t = np.tile(bits, w.B).astype(np.int64)
+    codes = np.zeros((n, w.dk, w.dv), np.int16)
+    scales = np.zeros((n, w.dv), np.float32)
+    for p in range(2):
+        out = _decode(st, w, 5, p).reshape(w.period, n, w.dv).cpu().numpy()
+        tok = inputs.decode_period(w, 5, p)
+        q, k, v, a, b = tok_tiles(tok, np.arange(n), w.H)
+        O, c2, s2, Mpre = opace.period(codes, scales, bits_t, q, k, v, a, b)
+        parity.check_outputs(out, O, f"zero-init period {p}")
+        c, s = st.read_codes()
+        c = c.reshape(n, w.dk, w.dv).cpu().numpy()
+        s = s.reshape(n, w.dv).cpu().numpy()
+        parity.check_encoded(c, s, c2, s2, Mpre, f"zero-init period {p}")
+        codes, scales = c, s
+
+
+def test_prefill_outputs_and_state():
+    import torch
+    from linear_attn_decode_pace_amd import runtime
+    w = inputs.ragged("prefill-small", 202, B=2, H=3, steps=8)
+    tok = inputs.tokens(w, 0, inputs.SEG_PROMPT, 0, 40)
+    M = torch.zeros((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    out = runtime.out_buffer(w, tok.T)
+    runtime.prefill(w, runtime.DeviceTokens(tok), M, out)
+    n = w.B * w.H
+    q, k, v, a, b = tok_tiles(tok, np.arange(n), w.H)
+    Mr, Or = gdn.run(np.zeros((n, w.dk, w.dv)), q, k, v, a, b)
+    assert parity.rel_per_tile(M.reshape(n, w.dk, w.dv).cpu().numpy(), Mr, 0).max() <= 1e-5
+    assert parity.rel_per_tile(out.reshape(tok.T, n, w.dv).cpu().numpy(), Or, 1).max() <= 1e-5
+
+
+def test_enomem_for_absurd_batch():
+    from linear_attn_decode_pace_amd import pace
+    with pytest.raises(pace.PaceError) as e:
+        pace.pace_state_alloc(1 << 26, 16, 128, 128, 8, pace.PACE_DTYPE_BF16, [4] * 16)
+    assert e.value.status == pace.PACE_ENOMEM
+
+
+def test_decode_rejects_too_many_tokens():
+    from linear_attn_decode_pace_amd import pace, runtime
+    st, _ = _state(W, 6)
+    tok = runtime.DeviceTokens(inputs.tokens(W, 6, inputs.SEG_DECODE, 0, W.period + 1))
+    out = runtime.out_buffer(W, tok.T)
+    with pytest.raises(pace.PaceError) as e:
+        st.decode(tok, out)
+    assert e.value.status == pace.PACE_EINVAL
