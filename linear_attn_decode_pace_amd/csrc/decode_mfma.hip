@@ -51,6 +51,14 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Debug builds may define PACE_MFMA_TRACE(slot, lane, value) to record
+// intermediates of the first work item; it is a no-op otherwise.
+#ifndef PACE_MFMA_TRACE
+#define PACE_MFMA_TRACE(slot, lane, value) \
+    do {                                    \
+    } while (0)
+#endif
+
 constexpr int CH = 8;      // tokens per chunk
 constexpr int WAVES = 4;   // tiles (waves) per workgroup
 constexpr int LROW = 136;  // bf16 elements per LDS token row (128 + 8 padding)
@@ -174,14 +182,19 @@ struct Loader {
     // code of (row tile rt, row r in the lane's group) as float
     __device__ inline float code(int rt, int r) const {
         if constexpr (BITS == 4)
-            return (float)__builtin_amdgcn_sbfe(d[rt >> 1], 8 * r + 4 * (rt & 1), 4);
+            return (float)(int)__builtin_amdgcn_sbfe(d[rt >> 1], 8 * r + 4 * (rt & 1), 4);
         else
-            return (float)__builtin_amdgcn_sbfe(d[rt], 8 * r, 8);
+            return (float)(int)__builtin_amdgcn_sbfe(d[rt], 8 * r, 8);
     }
 };
 
 template <int DK, int BITS>
-__device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int slot, int lane) {
+__device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int slot, int lane,
+                             bool trace) {
+#define TRACE(slot_, v_)                                      \
+    do {                                                      \
+        if (trace) PACE_MFMA_TRACE((slot_), lane, (float)(v_)); \
+    } while (0)
     constexpr int NKS = CodeChunk<DK>::NKS;  // k-slices of 32 rows
     constexpr int NRT = CodeChunk<DK>::NRT;  // row tiles of 16 rows
     constexpr int NCB = DK / 16;             // column blocks (d_v = d_k)
@@ -254,6 +267,7 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
         f32x4 G = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) G = mfma_bf16_k32(AP[ks], BG[ks], G);
+        TRACE(0, G[0]); TRACE(1, G[1]); TRACE(2, G[2]); TRACE(3, G[3]);
         if (n < 8) {
             L.kk[g][n] = G[0];
             L.kk[4 + g][n] = G[1];
@@ -327,6 +341,10 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
     const float R2_2 = n == g ? 1.f : 0.f;
     const float R2_3 = n == 4 + g ? 1.f : 0.f;
     const float gam_g = L.gam[g], gam_4g = L.gam[4 + g], gamC = L.gam[CH - 1];
+    TRACE(4, R1_0); TRACE(5, R1_1); TRACE(6, R2_0); TRACE(7, R2_1); TRACE(8, R2_2); TRACE(9, R2_3);
+    TRACE(10, gam_g); TRACE(11, gam_4g); TRACE(12, gamC);
+    TRACE(13, L.A[lane >> 3][lane & 7]); TRACE(14, L.Tt[lane >> 3][lane & 7]);
+    TRACE(15, L.kk[lane >> 3][lane & 7]); TRACE(16, L.Lq[lane >> 3][lane & 7]);
 
     // K^T as the A operand of the update: row i = 16 rt + n, k index 4 g + e is
     // token 4 (g % 2) + e (the same tokens for the hi / mid / lo parts)
@@ -374,6 +392,7 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
         }
         // P (code units): [k_g . c, k_{4+g} . c, q_g . c, q_{4+g} . c] for column j
 
+        if (cb == 0) { TRACE(20, P[0]); TRACE(21, P[1]); TRACE(22, P[2]); TRACE(23, P[3]); TRACE(24, s); }
         const float sg = gam_g * s, s4g = gam_4g * s;
         const float X0 = fmaf(-sg, P[0], bf2f(L.v[g][j]));
         const float X1 = fmaf(-s4g, P[1], bf2f(L.v[4 + g][j]));
@@ -400,6 +419,10 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
         O = mfma_f32_k4(R2_1, X1, O);
         O = mfma_f32_k4(R2_2, Y0, O);
         O = mfma_f32_k4(R2_3, Y1, O);
+        if (cb == 0) {
+            TRACE(25, X0); TRACE(26, X1); TRACE(27, Y0); TRACE(28, Y1); TRACE(29, sig);
+            for (int r = 0; r < 4; ++r) { TRACE(30 + r, W[r]); TRACE(34 + r, O[r]); }
+        }
         if (g < 2) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -434,6 +457,11 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
             for (int r = 0; r < 4; ++r) am = fmaxf(am, fabsf(acc[rt][r]));
         am = xor_max(am, 16);
         am = xor_max(am, 32);
+        if (cb == 0) {
+            for (int rt = 0; rt < NRT; ++rt)
+                for (int r = 0; r < 4; ++r) TRACE(40 + 4 * rt + r, acc[rt][r]);
+            TRACE(38, am);
+        }
         const float absmax = am * sig;
         const float s_new = absmax / QMAX;
         const float ratio = s_new > 0.f ? sig / s_new : 0.f;
@@ -461,6 +489,7 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
         cur = nxt;
         s_cur = s_nxt;
     }
+#undef TRACE
 }
 
 template <int DK>
@@ -471,11 +500,11 @@ __global__ void __launch_bounds__(64 * WAVES) decode_mfma_kernel(MfmaArgs a) {
     if (w >= a.tiles) return;
     if (w < a.tiles8) {
         const int b = w / a.p.n8, slot = w % a.p.n8;
-        process_tile<DK, 8>(a, lds[wave], b, a.heads8[slot], slot, lane);
+        process_tile<DK, 8>(a, lds[wave], b, a.heads8[slot], slot, lane, w == 0);
     } else {
         const int w4 = w - a.tiles8;
         const int b = w4 / a.p.n4, slot = w4 % a.p.n4;
-        process_tile<DK, 4>(a, lds[wave], b, a.heads4[slot], slot, lane);
+        process_tile<DK, 4>(a, lds[wave], b, a.heads4[slot], slot, lane, w == 0);
     }
 }
 
