@@ -137,6 +137,8 @@ def main() -> int:
     ap.add_argument("--cpu-periods", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workers", type=int, default=min(16, len(os.sched_getaffinity(0))))
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device-to-device copy (profiler traffic calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -174,6 +176,14 @@ def main() -> int:
     out = runtime.out_buffer(w, C)
     torch.cuda.synchronize()
     log(f"state and {ring_n} input periods resident ({sum(r.nbytes for r in ring) / 1e9:.2f} GB)")
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for i in range(args.warmup):
         st.decode(ring[i % ring_n], out)

@@ -19,6 +19,9 @@ CFLAGS = [
     "-Wall", "-Wno-unused-function",
     # no packed-fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in VGPRs (no AGPR <-> VGPR copies around the
+    # VALU work on accumulator tiles)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -62,6 +62,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int CH = 8;      // tokens per chunk
 constexpr int WAVES = 4;   // tiles (waves) per workgroup
 constexpr int LROW = 136;  // bf16 elements per LDS token row (128 + 8 padding)
+constexpr int OROW = 132;  // floats per LDS output row (128 + 4 padding)
 
 struct WaveLds {
     uint16_t kq[16][LROW];  // rows 0..7: k_t, rows 8..15: q_t (bf16 bits)
@@ -73,6 +74,7 @@ struct WaveLds {
     float Tt[CH][CH];              // Tt[s][t] = T[t][s]
     float gam[CH];                 // gamma_t
     float gamC[CH];                // Gamma_{C-1, t}
+    float o[CH][OROW];             // the chunk's outputs, written out as whole rows
 };
 
 struct MfmaArgs {
@@ -179,20 +181,47 @@ struct Loader {
             }
         }
     }
-    // code of (row tile rt, row r in the lane's group) as float
-    __device__ inline float code(int rt, int r) const {
-        if constexpr (BITS == 4)
-            return (float)(int)__builtin_amdgcn_sbfe(d[rt >> 1], 8 * r + 4 * (rt & 1), 4);
-        else
-            return (float)(int)__builtin_amdgcn_sbfe(d[rt], 8 * r, 8);
+    // KAPPA * code of (row tile rt, row r in the lane's group) as float: 4-bit
+    // codes are moved to the high nibble of their byte (a signed byte worth
+    // 16 c), so one sign-extending byte conversion reads each of them
+    static constexpr float KAPPA = BITS == 4 ? 16.f : 1.f;
+    __device__ inline void codes_f32(f32x4 *acc) const {
+        if constexpr (BITS == 4) {
+#pragma unroll
+            for (int ks = 0; ks < ND; ++ks) {
+                const uint32_t lo = (d[ks] << 4) & 0xf0f0f0f0u;  // row tile 2 ks
+                const uint32_t hi = d[ks] & 0xf0f0f0f0u;         // row tile 2 ks + 1
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    acc[2 * ks][r] = (float)(int)__builtin_amdgcn_sbfe(lo, 8 * r, 8);
+                    acc[2 * ks + 1][r] = (float)(int)__builtin_amdgcn_sbfe(hi, 8 * r, 8);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < ND; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[rt][r] = (float)(int)__builtin_amdgcn_sbfe(d[rt], 8 * r, 8);
+        }
     }
 };
+
+// byte-offset access from a wave-uniform base: keeps per-lane address math in
+// 32 bits (the base lives in scalar registers)
+template <class T>
+__device__ inline T *at(T *base, uint32_t byte_off) {
+    return (T *)((char *)base + byte_off);
+}
+template <class T>
+__device__ inline const T *at(const T *base, uint32_t byte_off) {
+    return (const T *)((const char *)base + byte_off);
+}
 
 template <int DK, int BITS>
 __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int slot, int lane,
                              bool trace) {
-#define TRACE(slot_, v_)                                      \
-    do {                                                      \
+#define TRACE(slot_, v_)                                        \
+    do {                                                        \
         if (trace) PACE_MFMA_TRACE((slot_), lane, (float)(v_)); \
     } while (0)
     constexpr int NKS = CodeChunk<DK>::NKS;  // k-slices of 32 rows
@@ -201,7 +230,7 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
     constexpr float QMAX = BITS == 4 ? 7.f : 127.f;
     const int g = lane >> 4, n = lane & 15;
     const int n_tok = a.n_tok;
-    const size_t tok_stride = (size_t)a.p.B * a.p.H;
+    const uint32_t tok_stride = (uint32_t)a.p.B * (uint32_t)a.p.H;  // (sequence, head) rows per token
     const size_t tile_row = (size_t)b * a.p.H + h;
 
     uint8_t *codes = BITS == 4
@@ -209,33 +238,55 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
         : a.p.codes8 + ((size_t)b * a.p.n8 + slot) * tile_code_bytes(DK, DK, 8);
     float *scl = a.p.scales + tile_row * DK;
 
-    // first column block's codes and scale: issue early
-    Loader<DK, BITS> cur;
-    cur.load(codes, 0, lane);
-    float s_cur = scl[n];
-
-    // ---- stage the chunk's tokens in LDS (padding tokens: k = q = v = 0) ----
-    {
-        constexpr int CPR = DK / 8;  // 16-byte chunks per token row
+    // codes and scales of the first column blocks: a ring of PF column blocks
+    // kept in flight ahead of the one being processed
+    constexpr int PF = NCB < 4 ? NCB : 4;
+    Loader<DK, BITS> ring[PF];
+    float sring[PF];
 #pragma unroll
-        for (int c = lane; c < 24 * CPR; c += 64) {
+    for (int c = 0; c < PF; ++c) {
+        ring[c].load(codes, c, lane);
+        sring[c] = scl[16 * c + n];
+    }
+
+    // ---- stage the chunk's tokens in LDS (padding tokens: k = q = v = 0);
+    //      every load is issued before the first LDS write ----
+    {
+        constexpr int CPR = DK / 8;        // 16-byte chunks per token row
+        constexpr int NL = 24 * CPR / 64;  // loads per lane (6 for d = 128)
+        const uint16_t *srcs[3] = {a.k + tile_row * DK, a.q + tile_row * DK, a.v + tile_row * DK};
+        u32x4 val[NL];
+#pragma unroll
+        for (int it = 0; it < NL; ++it) {
+            const int c = lane + 64 * it;
             const int row = c / CPR, col = (c % CPR) * 8;
-            const int t = row & 7, which = row >> 3;
-            const uint16_t *src = which == 0 ? a.k : which == 1 ? a.q : a.v;
-            u32x4 val = {0u, 0u, 0u, 0u};
-            if (t < n_tok) val = *(const u32x4 *)(src + ((size_t)t * tok_stride + tile_row) * DK + col);
-            uint16_t *dst = which < 2 ? &L.kq[which * 8 + t][col] : &L.v[t][col];
-            *(u32x4 *)dst = val;
+            const int t = row & 7, which = (64 * it) / (8 * CPR);  // uniform per load
+            val[it] = u32x4{0u, 0u, 0u, 0u};
+            if (t < n_tok)
+                val[it] = __builtin_nontemporal_load(
+                    at((const u32x4 *)srcs[which], (uint32_t)(t * tok_stride * DK + col) * 2u));
         }
+        float ab = 0.f;
         if (lane < 16) {
             const int t = lane & 7;
             const bool is_beta = lane >= 8;
-            float x = is_beta ? 0.f : 1.f;
-            if (t < n_tok) x = (is_beta ? a.beta : a.alpha)[(size_t)t * tok_stride + tile_row];
-            if (is_beta)
-                L.beta[t] = x;
+            ab = is_beta ? 0.f : 1.f;
+            if (t < n_tok)
+                ab = *at(is_beta ? a.beta + tile_row : a.alpha + tile_row, (uint32_t)t * tok_stride * 4u);
+        }
+#pragma unroll
+        for (int it = 0; it < NL; ++it) {
+            const int c = lane + 64 * it;
+            const int row = c / CPR, col = (c % CPR) * 8;
+            const int t = row & 7, which = (64 * it) / (8 * CPR);
+            uint16_t *dst = which < 2 ? &L.kq[which * 8 + t][col] : &L.v[t][col];
+            *(u32x4 *)dst = val[it];
+        }
+        if (lane < 16) {
+            if (lane >= 8)
+                L.beta[lane & 7] = ab;
             else
-                L.alpha[t] = x;
+                L.alpha[lane & 7] = ab;
         }
     }
     wave_sync();
@@ -243,18 +294,23 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
     // ---- [K;Q] as the MFMA A operand: A row m = 4 gg + rr holds k_gg, k_{4+gg},
     //      q_gg, q_{4+gg} for rr = 0..3; k index e of slice ks is state row
     //      32 ks + 16 (e / 4) + 4 g + e % 4 (this lane's rows of two row tiles) ----
-    bf16x8 AP[NKS];
+    const int krow = ((n & 3) == 0) ? (n >> 2) : ((n & 3) == 1) ? 4 + (n >> 2)
+                   : ((n & 3) == 2) ? 8 + (n >> 2) : 12 + (n >> 2);
+    // A operand slice ks of [K;Q] (re-read from LDS where needed: saves registers)
+    auto ap_slice = [&](int ks) {
+        const int c0 = 32 * ks + 4 * g, c1 = c0 + 16;
+        u32x2 r0 = *(const u32x2 *)&L.kq[krow][c0];
+        u32x2 r1 = *(const u32x2 *)&L.kq[krow][c1];
+        u32x4 w = {r0[0], r0[1], r1[0], r1[1]};
+        return __builtin_bit_cast(bf16x8, w);
+    };
     {
-        const int gg = n >> 2, rr = n & 3;
-        const int krow = (rr == 0) ? gg : (rr == 1) ? 4 + gg : (rr == 2) ? 8 + gg : 12 + gg;
+        bf16x8 AP[NKS];
         bf16x8 BG[NKS];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const int c0 = 32 * ks + 4 * g, c1 = c0 + 16;
-            u32x2 r0 = *(const u32x2 *)&L.kq[krow][c0];
-            u32x2 r1 = *(const u32x2 *)&L.kq[krow][c1];
-            u32x4 w = {r0[0], r0[1], r1[0], r1[1]};
-            AP[ks] = __builtin_bit_cast(bf16x8, w);
+            AP[ks] = ap_slice(ks);
             u32x4 z = {0u, 0u, 0u, 0u};
             if (n < 8) {
                 u32x2 s0 = *(const u32x2 *)&L.kq[n][c0];
@@ -322,26 +378,34 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
     }
     wave_sync();
 
-    // ---- per-lane chain operands (A of the 16x16x4 float32 MFMAs) ----
-    // chain W: output row m -> token m % 8: A[m][k] = Gamma_{C-1,m%8} T[m%8][4 st + k]
-    const int t1 = lane & 7;
-    const float gct = L.gamC[t1];
-    const float R1_0 = gct * L.Tt[g][t1];
-    const float R1_1 = gct * L.Tt[4 + g][t1];
-    // chain O: rows m < 8 -> token m: A = (Lq T) for X, identity for Y
-    float R2_0 = 0.f, R2_1 = 0.f;
-    if (n < 8) {
+    // ---- A operand of the chunk mixing (float32 16x16x4 MFMA, 4 steps over
+    //      [X tokens 0-3, X 4-7, Y 0-3, Y 4-7]):
+    //      rows 0..7  -> W_t = Gamma_{C-1,t} (T X)_t          (A = Gamma_C T, 0)
+    //      rows 8..15 -> O_t = (Lq T X)_t + Y_t               (A = Lq T, I) ----
+    float CA[4];
+    {
+        const int t = n & 7;
+        const bool is_o = n >= 8;
+        float r0 = 0.f, r1 = 0.f;
+        if (is_o) {
 #pragma unroll
-        for (int u = 0; u < CH; ++u) {
-            const float lq = L.Lq[n][u];
-            R2_0 = fmaf(lq, L.Tt[g][u], R2_0);
-            R2_1 = fmaf(lq, L.Tt[4 + g][u], R2_1);
+            for (int u = 0; u < CH; ++u) {
+                const float lq = L.Lq[t][u];
+                r0 = fmaf(lq, L.Tt[g][u], r0);
+                r1 = fmaf(lq, L.Tt[4 + g][u], r1);
+            }
+        } else {
+            const float gct = L.gamC[t];
+            r0 = gct * L.Tt[g][t];
+            r1 = gct * L.Tt[4 + g][t];
         }
+        CA[0] = r0;
+        CA[1] = r1;
+        CA[2] = (is_o && t == g) ? 1.f : 0.f;
+        CA[3] = (is_o && t == 4 + g) ? 1.f : 0.f;
     }
-    const float R2_2 = n == g ? 1.f : 0.f;
-    const float R2_3 = n == 4 + g ? 1.f : 0.f;
     const float gam_g = L.gam[g], gam_4g = L.gam[4 + g], gamC = L.gam[CH - 1];
-    TRACE(4, R1_0); TRACE(5, R1_1); TRACE(6, R2_0); TRACE(7, R2_1); TRACE(8, R2_2); TRACE(9, R2_3);
+    TRACE(4, CA[0]); TRACE(5, CA[1]); TRACE(6, CA[2]); TRACE(7, CA[3]);
     TRACE(10, gam_g); TRACE(11, gam_4g); TRACE(12, gamC);
     TRACE(13, L.A[lane >> 3][lane & 7]); TRACE(14, L.Tt[lane >> 3][lane & 7]);
     TRACE(15, L.kk[lane >> 3][lane & 7]); TRACE(16, L.Lq[lane >> 3][lane & 7]);
@@ -363,24 +427,25 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
         }
     }
 
-    // ---- column blocks ----
-#pragma unroll 1
-    for (int cb = 0; cb < NCB; ++cb) {
-        const int j = 16 * cb + n;
-        Loader<DK, BITS> nxt;
-        float s_nxt = 0.f;
-        if (cb + 1 < NCB) {
-            nxt.load(codes, cb + 1, lane);
-            s_nxt = scl[j + 16];
-        }
-        const float s = s_cur;
 
-        // codes -> float32 (the accumulator's start) and bf16 B operands
+    // ---- column blocks (unrolled: ring slots stay in fixed registers) ----
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        // compiler-only barrier: keeps the per-block LDS re-reads from being
+        // hoisted out of the unrolled loop into long-lived registers
+        asm volatile("" ::: "memory");
+        const int j = 16 * cb + n;
+        const int slot = cb % PF;
+        const float s = sring[slot];
+
+        // KAPPA * codes -> float32 (the accumulator's start) and bf16 B operands
+        constexpr float KAPPA = Loader<DK, BITS>::KAPPA;
         f32x4 acc[NRT];
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[rt][r] = cur.code(rt, r);
+        ring[slot].codes_f32(acc);
+        if (cb + PF < NCB) {
+            ring[slot].load(codes, cb + PF, lane);
+            sring[slot] = scl[j + 16 * PF];
+        }
 
         f32x4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -388,50 +453,52 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
             u32x4 w = {pk_bf16(acc[2 * ks][0], acc[2 * ks][1]), pk_bf16(acc[2 * ks][2], acc[2 * ks][3]),
                        pk_bf16(acc[2 * ks + 1][0], acc[2 * ks + 1][1]),
                        pk_bf16(acc[2 * ks + 1][2], acc[2 * ks + 1][3])};
-            P = mfma_bf16_k32(AP[ks], __builtin_bit_cast(bf16x8, w), P);
+            P = mfma_bf16_k32(ap_slice(ks), __builtin_bit_cast(bf16x8, w), P);
         }
-        // P (code units): [k_g . c, k_{4+g} . c, q_g . c, q_{4+g} . c] for column j
-
+        // P = KAPPA * [k_g . c, k_{4+g} . c, q_g . c, q_{4+g} . c] for column j
         if (cb == 0) { TRACE(20, P[0]); TRACE(21, P[1]); TRACE(22, P[2]); TRACE(23, P[3]); TRACE(24, s); }
-        const float sg = gam_g * s, s4g = gam_4g * s;
+        const float sk = s * (1.f / KAPPA);  // exact: KAPPA is a power of two
+        const float sg = gam_g * sk, s4g = gam_4g * sk;
         const float X0 = fmaf(-sg, P[0], bf2f(L.v[g][j]));
         const float X1 = fmaf(-s4g, P[1], bf2f(L.v[4 + g][j]));
         const float Y0 = sg * P[2];
         const float Y1 = s4g * P[3];
 
-        // accumulate in units of sigma = gamma_C s (1 for a zero column)
+        // accumulate M / unit with unit = gamma_C s / KAPPA, so the accumulator
+        // starts from the loaded KAPPA * c (unit = 1 / KAPPA for a zero column)
         const float sig_raw = gamC * s;
         const bool tiny = s > 0.f && !(sig_raw >= 1.17549435e-38f);
-        const float sig = (s > 0.f && !tiny) ? sig_raw : 1.f;
+        const float sig = ((s > 0.f && !tiny) ? sig_raw : 1.f) * (1.f / KAPPA);
         if (__builtin_amdgcn_ballot_w64(tiny)) {
             // decay below float32's normal range: start from gamma_C s c directly
             const float m0 = tiny ? sig_raw : 1.f;
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) acc[rt] *= m0;
         }
-        const float inv_sig = 1.f / sig;
+        const float inv_sig = __builtin_amdgcn_rcpf(sig);
 
-        f32x4 W = {0.f, 0.f, 0.f, 0.f};
-        W = mfma_f32_k4(R1_0, X0 * inv_sig, W);
-        W = mfma_f32_k4(R1_1, X1 * inv_sig, W);
-        f32x4 O = {0.f, 0.f, 0.f, 0.f};
-        O = mfma_f32_k4(R2_0, X0, O);
-        O = mfma_f32_k4(R2_1, X1, O);
-        O = mfma_f32_k4(R2_2, Y0, O);
-        O = mfma_f32_k4(R2_3, Y1, O);
+        // one chain: lanes g < 2 get W (tokens 4 g + r), lanes g >= 2 get O
+        f32x4 WO = {0.f, 0.f, 0.f, 0.f};
+        WO = mfma_f32_k4(CA[0], X0, WO);
+        WO = mfma_f32_k4(CA[1], X1, WO);
+        WO = mfma_f32_k4(CA[2], Y0, WO);
+        WO = mfma_f32_k4(CA[3], Y1, WO);
+        f32x4 W;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float other = __shfl_xor(WO[r], 32);
+            W[r] = (g < 2 ? WO[r] : other) * inv_sig;  // tokens 4 (g % 2) + r, units of sig
+        }
         if (cb == 0) {
             TRACE(25, X0); TRACE(26, X1); TRACE(27, Y0); TRACE(28, Y1); TRACE(29, sig);
-            for (int r = 0; r < 4; ++r) { TRACE(30 + r, W[r]); TRACE(34 + r, O[r]); }
+            for (int r = 0; r < 4; ++r) { TRACE(30 + r, W[r]); TRACE(34 + r, WO[r]); }
         }
-        if (g < 2) {
+        if (g >= 2) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * g + r;
-                if (t < n_tok) a.out[((size_t)t * tok_stride + tile_row) * DK + j] = O[r];
-            }
+            for (int r = 0; r < 4; ++r) L.o[4 * (g - 2) + r][j] = WO[r];
         }
 
-        // W (tokens 4 (g % 2) + r) split exactly-enough into three bf16 parts
+        // W split into three bf16 parts (hi + mid + lo)
         const uint32_t hi01 = pk_bf16(W[0], W[1]), hi23 = pk_bf16(W[2], W[3]);
         const float r0 = W[0] - lo_f32(hi01), r1 = W[1] - hi_f32(hi01);
         const float r2 = W[2] - lo_f32(hi23), r3 = W[3] - hi_f32(hi23);
@@ -463,8 +530,8 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
             TRACE(38, am);
         }
         const float absmax = am * sig;
-        const float s_new = absmax / QMAX;
-        const float ratio = s_new > 0.f ? sig / s_new : 0.f;
+        const float s_new = absmax * (1.f / QMAX);
+        const float ratio = s_new > 0.f ? sig * __builtin_amdgcn_rcpf(s_new) : 0.f;
         uint32_t y[NRT][4];
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt)
@@ -485,9 +552,23 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
         }
         outc.store(codes, cb, lane);
         if (g == 0) scl[j] = s_new;
+    }
 
-        cur = nxt;
-        s_cur = s_nxt;
+    // ---- outputs: whole 16-byte chunks of whole rows (full cache lines) ----
+    wave_sync();
+    {
+        float *obase = a.out + tile_row * DK;
+        const uint32_t o_tok = tok_stride * DK * 4u;  // bytes between tokens of out
+        constexpr int CPR = DK / 4;                   // 16-byte chunks per output row
+#pragma unroll
+        for (int it = 0; it < CH * CPR / 64; ++it) {
+            const int c = lane + 64 * it;
+            const int t = c / CPR, col = (c % CPR) * 4;
+            if (t < n_tok) {
+                const f32x4 x = *(const f32x4 *)&L.o[t][col];
+                __builtin_nontemporal_store(x, at((f32x4 *)obase, (uint32_t)t * o_tok + (uint32_t)col * 4u));
+            }
+        }
     }
 #undef TRACE
 }
@@ -495,7 +576,10 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
 template <int DK>
 __global__ void __launch_bounds__(64 * WAVES) decode_mfma_kernel(MfmaArgs a) {
     __shared__ WaveLds lds[WAVES];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63;
+    // wave-uniform work item (scalar registers: the head lookups below are
+    // scalar-cache loads, not a dependent vector load at the head of the tile)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int w = blockIdx.x * WAVES + wave;
     if (w >= a.tiles) return;
     if (w < a.tiles8) {
@@ -510,8 +594,10 @@ __global__ void __launch_bounds__(64 * WAVES) decode_mfma_kernel(MfmaArgs a) {
 
 }  // namespace
 
-bool mfma_supported(int dk, int dv, int n_tok, int in_bf16) {
-    return in_bf16 && dk == dv && (dk == 128 || dk == 64) && n_tok >= 1 && n_tok <= CH;
+bool mfma_supported(int dk, int dv, int n_tok, int in_bf16, long long rows_per_token) {
+    // per-lane byte offsets (tokens x rows x d x 4 bytes) are kept in 32 bits
+    return in_bf16 && dk == dv && (dk == 128 || dk == 64) && n_tok >= 1 && n_tok <= CH &&
+           (long long)CH * rows_per_token * dk * 4 < (1ll << 31);
 }
 
 hipError_t launch_decode_mfma(const PoolView &p, const int32_t *heads8, const int32_t *heads4,

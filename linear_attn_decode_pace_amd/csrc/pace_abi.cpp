@@ -244,7 +244,8 @@ PACE_API int pace_decode_period(pace_state *st, int32_t n_tok, const void *q, co
     hipStream_t s = (hipStream_t)stream;
     const int bf16 = st->cfg.in_dtype == PACE_DTYPE_BF16;
     hipError_t e;
-    if (pace::mfma_supported(st->cfg.d_k, st->cfg.d_v, n_tok, bf16))
+    if (pace::mfma_supported(st->cfg.d_k, st->cfg.d_v, n_tok, bf16,
+                             (long long)st->cfg.batch * st->cfg.heads))
         e = pace::launch_decode_mfma(st->view(), st->d_map + st->cfg.heads,
                                      st->d_map + st->cfg.heads + st->n8, n_tok, q, k, v, alpha,
                                      beta, out, s);

@@ -6,8 +6,9 @@
 namespace pace {
 
 // True when the fused kernel covers this shape (bf16 inputs, d_k = d_v = 128
-// or 64, n_tok within the kernel's chunk).
-bool mfma_supported(int dk, int dv, int n_tok, int in_bf16);
+// or 64, n_tok within the kernel's chunk, B * H small enough for 32-bit lane
+// offsets); rows_per_token = B * H.
+bool mfma_supported(int dk, int dv, int n_tok, int in_bf16, long long rows_per_token);
 
 // heads8 / heads4: device [n8] / [n4], the head of each slot of the 8-bit /
 // 4-bit pool.
