@@ -128,7 +128,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=inputs.HEADLINE.name, choices=sorted(inputs.WORKLOADS))
     ap.add_argument("--period", type=int, default=None, help="override the workload's period")
     ap.add_argument("--seed", type=int, default=0)

@@ -59,6 +59,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     } while (0)
 #endif
 
+// column blocks of codes kept in flight ahead of the one being processed
+#ifndef PACE_MFMA_PREFETCH
+#define PACE_MFMA_PREFETCH 2
+#endif
+
 constexpr int CH = 8;      // tokens per chunk
 constexpr int WAVES = 4;   // tiles (waves) per workgroup
 constexpr int LROW = 136;  // bf16 elements per LDS token row (128 + 8 padding)
@@ -140,6 +145,9 @@ struct CodeChunk<64> {
 
 template <int DK, int BITS>
 struct Loader {
+    // Codes are streamed: read once and written once per period, with a pool
+    // far larger than the last-level cache, so loads and stores are
+    // non-temporal.
     // dwords a lane holds per column block: 4-bit: one per k-slice; 8-bit: one per row tile
     static constexpr int ND = BITS == 4 ? DK / 32 : DK / 16;
     uint32_t d[ND];
@@ -147,17 +155,17 @@ struct Loader {
         if constexpr (BITS == 4) {
             const uint8_t *p = codes + (size_t)cb * (64 * DK / 8) + (size_t)lane * (DK / 8);
             if constexpr (DK == 128) {
-                u32x4 x = *(const u32x4 *)p;
+                u32x4 x = __builtin_nontemporal_load((const u32x4 *)p);
                 d[0] = x[0], d[1] = x[1], d[2] = x[2], d[3] = x[3];
             } else {
-                u32x2 x = *(const u32x2 *)p;
+                u32x2 x = __builtin_nontemporal_load((const u32x2 *)p);
                 d[0] = x[0], d[1] = x[1];
             }
         } else {
             const uint8_t *p = codes + (size_t)cb * (64 * DK / 4) + (size_t)lane * 16;
 #pragma unroll
             for (int qd = 0; qd < DK / 64; ++qd) {
-                u32x4 x = *(const u32x4 *)(p + qd * 1024);
+                u32x4 x = __builtin_nontemporal_load((const u32x4 *)(p + qd * 1024));
                 d[4 * qd + 0] = x[0], d[4 * qd + 1] = x[1], d[4 * qd + 2] = x[2], d[4 * qd + 3] = x[3];
             }
         }
@@ -167,17 +175,17 @@ struct Loader {
             uint8_t *p = codes + (size_t)cb * (64 * DK / 8) + (size_t)lane * (DK / 8);
             if constexpr (DK == 128) {
                 u32x4 x = {d[0], d[1], d[2], d[3]};
-                *(u32x4 *)p = x;
+                __builtin_nontemporal_store(x, (u32x4 *)p);
             } else {
                 u32x2 x = {d[0], d[1]};
-                *(u32x2 *)p = x;
+                __builtin_nontemporal_store(x, (u32x2 *)p);
             }
         } else {
             uint8_t *p = codes + (size_t)cb * (64 * DK / 4) + (size_t)lane * 16;
 #pragma unroll
             for (int qd = 0; qd < DK / 64; ++qd) {
                 u32x4 x = {d[4 * qd], d[4 * qd + 1], d[4 * qd + 2], d[4 * qd + 3]};
-                *(u32x4 *)(p + qd * 1024) = x;
+                __builtin_nontemporal_store(x, (u32x4 *)(p + qd * 1024));
             }
         }
     }
@@ -240,7 +248,7 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
 
     // codes and scales of the first column blocks: a ring of PF column blocks
     // kept in flight ahead of the one being processed
-    constexpr int PF = NCB < 4 ? NCB : 4;
+    constexpr int PF = NCB < PACE_MFMA_PREFETCH ? NCB : PACE_MFMA_PREFETCH;
     Loader<DK, BITS> ring[PF];
     float sring[PF];
 #pragma unroll
