@@ -590,14 +590,14 @@ __global__ void __launch_bounds__(64 * WAVES) decode_mfma_kernel(MfmaArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int w = blockIdx.x * WAVES + wave;
     if (w >= a.tiles) return;
-    if (w < a.tiles8) {
-        const int b = w / a.p.n8, slot = w % a.p.n8;
-        process_tile<DK, 8>(a, lds[wave], b, a.heads8[slot], slot, lane, w == 0);
-    } else {
-        const int w4 = w - a.tiles8;
-        const int b = w4 / a.p.n4, slot = w4 % a.p.n4;
-        process_tile<DK, 4>(a, lds[wave], b, a.heads4[slot], slot, lane, w == 0);
-    }
+    // sequence-major order: the heads of one sequence are neighbours, so a
+    // workgroup mixes 4-bit and 8-bit tiles and reads whole input rows
+    const int b = w / a.p.H, h = w - b * a.p.H;
+    const int m = a.p.head_map[h];  // slot | bits << 16 (scalar load)
+    if ((m >> 16) == 8)
+        process_tile<DK, 8>(a, lds[wave], b, h, m & 0xffff, lane, w == 0);
+    else
+        process_tile<DK, 4>(a, lds[wave], b, h, m & 0xffff, lane, w == 0);
 }
 
 }  // namespace
