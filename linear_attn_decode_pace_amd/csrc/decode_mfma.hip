@@ -67,7 +67,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int CH = 8;      // tokens per chunk
 constexpr int WAVES = 4;   // tiles (waves) per workgroup
 constexpr int LROW = 136;  // bf16 elements per LDS token row (128 + 8 padding)
-constexpr int OROW = 132;  // floats per LDS output row (128 + 4 padding)
+constexpr int OCOL = 32;   // output columns staged before a flush (one 128-byte line per row)
+constexpr int OROW = 36;   // floats per LDS output staging row (32 + 4 padding)
 
 struct WaveLds {
     uint16_t kq[16][LROW];  // rows 0..7: k_t, rows 8..15: q_t (bf16 bits)
@@ -79,7 +80,7 @@ struct WaveLds {
     float Tt[CH][CH];              // Tt[s][t] = T[t][s]
     float gam[CH];                 // gamma_t
     float gamC[CH];                // Gamma_{C-1, t}
-    float o[CH][OROW];             // the chunk's outputs, written out as whole rows
+    float o[CH][OROW];             // outputs of two column blocks, flushed as full lines
 };
 
 struct MfmaArgs {
@@ -436,6 +437,9 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
     }
 
 
+    float *obase = a.out + tile_row * DK;
+    const uint32_t o_tok = tok_stride * DK * 4u;  // bytes between tokens of out
+
     // ---- column blocks (unrolled: ring slots stay in fixed registers) ----
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
@@ -503,7 +507,17 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
         }
         if (g >= 2) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) L.o[4 * (g - 2) + r][j] = WO[r];
+            for (int r = 0; r < 4; ++r) L.o[4 * (g - 2) + r][j % OCOL] = WO[r];
+        }
+        if (cb % 2 == 1) {
+            // every second column block: flush 8 rows x 128 bytes, one 16-byte
+            // chunk per lane (lane -> row lane / 8, chunk lane % 8)
+            wave_sync();
+            const int t = lane >> 3, c4 = (lane & 7) * 4;
+            const f32x4 x = *(const f32x4 *)&L.o[t][c4];
+            if (t < n_tok)
+                __builtin_nontemporal_store(
+                    x, at((f32x4 *)obase, (uint32_t)t * o_tok + (uint32_t)(16 * cb - 16 + c4) * 4u));
         }
 
         // W split into three bf16 parts (hi + mid + lo)
@@ -562,22 +576,6 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
         if (g == 0) scl[j] = s_new;
     }
 
-    // ---- outputs: whole 16-byte chunks of whole rows (full cache lines) ----
-    wave_sync();
-    {
-        float *obase = a.out + tile_row * DK;
-        const uint32_t o_tok = tok_stride * DK * 4u;  // bytes between tokens of out
-        constexpr int CPR = DK / 4;                   // 16-byte chunks per output row
-#pragma unroll
-        for (int it = 0; it < CH * CPR / 64; ++it) {
-            const int c = lane + 64 * it;
-            const int t = c / CPR, col = (c % CPR) * 4;
-            if (t < n_tok) {
-                const f32x4 x = *(const f32x4 *)&L.o[t][col];
-                __builtin_nontemporal_store(x, at((f32x4 *)obase, (uint32_t)t * o_tok + (uint32_t)col * 4u));
-            }
-        }
-    }
 #undef TRACE
 }
 
