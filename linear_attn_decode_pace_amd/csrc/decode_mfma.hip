@@ -65,7 +65,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #endif
 
 constexpr int CH = 8;      // tokens per chunk
-constexpr int WAVES = 4;   // tiles (waves) per workgroup
+#ifndef PACE_MFMA_WAVES
+#define PACE_MFMA_WAVES 4
+#endif
+constexpr int WAVES = PACE_MFMA_WAVES;  // tiles (waves) per workgroup
 constexpr int LROW = 136;  // bf16 elements per LDS token row (128 + 8 padding)
 constexpr int OCOL = 32;   // output columns staged before a flush (one 128-byte line per row)
 constexpr int OROW = 36;   // floats per LDS output staging row (32 + 4 padding)
