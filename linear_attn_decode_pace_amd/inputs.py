@@ -183,6 +183,30 @@ def tokens(w: Workload, seed: int, seg: int, t0: int, t1: int) -> Tokens:
                   w.dtype)
 
 
+def _tokens_job(args):
+    return tokens(*args)
+
+
+def iter_tokens(w: Workload, seed: int, seg: int, ranges, workers: int = 1):
+    """Tokens of several ranges [(t0, t1), ...] in order, generated by a
+    process pool when workers > 1 (the values do not depend on workers)."""
+    jobs = [(w, seed, seg, t0, t1) for t0, t1 in ranges]
+    if workers <= 1 or len(jobs) <= 1:
+        for j in jobs:
+            yield tokens(*j)
+        return
+    import concurrent.futures as cf
+    with cf.ProcessPoolExecutor(max_workers=workers) as ex:
+        for tok in ex.map(_tokens_job, jobs):
+            yield tok
+
+
+def concat(parts) -> Tokens:
+    parts = list(parts)
+    return Tokens(*[np.concatenate([getattr(p, n) for p in parts], axis=0)
+                    for n in ("q", "k", "v", "alpha", "beta")], parts[0].dtype)
+
+
 def decode_period(w: Workload, seed: int, p: int, period: Optional[int] = None) -> Tokens:
     """The tokens of decode period p (period length defaults to the workload's)."""
     c = w.period if period is None else period

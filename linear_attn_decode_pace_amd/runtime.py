@@ -109,10 +109,14 @@ def prefill(w: inputs.Workload, tok: DeviceTokens, state: torch.Tensor,
                           tok.alpha, tok.beta, state, out, stream)
 
 
-def warmup_state(w: inputs.Workload, seed: int, device="cuda") -> torch.Tensor:
+def warmup_state(w: inputs.Workload, seed: int, device="cuda",
+                 tok: Optional[inputs.Tokens] = None) -> torch.Tensor:
     """float32 state after the workload's unquantized warm-up tokens from zero,
-    computed by the library's prefill kernel."""
+    computed by the library's prefill kernel (tok: the warm-up tokens, if
+    already generated)."""
     M = torch.zeros((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=device)
     if w.warmup:
-        prefill(w, DeviceTokens(inputs.warmup_tokens(w, seed), device), M)
+        if tok is None:
+            tok = inputs.warmup_tokens(w, seed)
+        prefill(w, DeviceTokens(tok, device), M)
     return M

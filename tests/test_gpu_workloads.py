@@ -1,0 +1,80 @@
+"""The measured workloads at their full sizes, in the launch configuration the
+benchmark times, checked against the oracle on sampled tiles.
+
+Every GPU launch covers the whole batch; the oracle replays and free-runs the
+sampled (sequence, head) tiles one by one.  Samples always include the first
+and last sequence and tiles of both bit widths.
+"""
+import numpy as np
+import pytest
+
+from linear_attn_decode_pace_amd import inputs
+from oracle import gdn
+from tests.gpu_cases import default_calls, run_case, say
+
+pytestmark = pytest.mark.gpu
+
+WORKERS = 16
+
+
+def _sample(w, seed, n, rng_seed=0):
+    bits = inputs.head_bits(w, seed)
+    rng = np.random.default_rng(rng_seed)
+    tiles = w.B * w.H
+    pick = set(rng.choice(tiles, size=n, replace=False).tolist())
+    pick |= {0, w.H - 1, tiles - w.H, tiles - 1}
+    for width in (4, 8):
+        hs = np.nonzero(bits == width)[0]
+        if hs.size:
+            pick |= {int(hs[0]), int((w.B - 1) * w.H + hs[-1])}
+    return np.array(sorted(pick))
+
+
+def test_headline_full_batch_sampled():
+    # 4096 sequences x 16 heads (12 at 4 bits, 4 at 8 bits), period 8: the
+    # benchmark's launch; three periods checked on 64+ sampled tiles
+    w = inputs.HEADLINE
+    run_case(w, 0, default_calls(w, 3), sample=_sample(w, 0, 64), workers=WORKERS)
+
+
+def test_mixed_b1024_whole_run_sampled():
+    # 1024 sequences, all 512 decode steps (64 periods), outlier channels
+    w = inputs.MIXED
+    r = run_case(w, 0, default_calls(w), sample=_sample(w, 0, 24), workers=WORKERS)
+    assert r["calls"] == 64
+
+
+@pytest.mark.parametrize("period", [1, 2, 4, 8, 16])
+def test_sweep_b256_whole_run_sampled(period):
+    # 256 sequences, 256 decode steps at each period length
+    w = inputs.SWEEP.replace(period=period)
+    run_case(w, 0, default_calls(w), sample=_sample(w, 0, 24), workers=WORKERS,
+             label=f"sweep-b256-k{period}")
+
+
+def test_prompt_handoff_reduced_batch():
+    # 4096-token prompts through the library's float32 prefill into the
+    # quantized state, then decode at period 16 with 8 of 32 heads at 8 bits;
+    # the batch is reduced from 512 to 8 prompts (input volume), every other
+    # size is the workload's own
+    import torch
+
+    from linear_attn_decode_pace_amd import runtime
+
+    w = inputs.PREFILL.replace(B=8, steps=64)
+    seed = 0
+    idx = _sample(w, seed, 16)
+    M = torch.zeros((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    Mr = np.zeros((len(idx), w.dk, w.dv))
+    blk = 256
+    ranges = [(t, min(w.prompt, t + blk)) for t in range(0, w.prompt, blk)]
+    b, h = idx // w.H, idx % w.H
+    for i, tok in enumerate(inputs.iter_tokens(w, seed, inputs.SEG_PROMPT, ranges, WORKERS)):
+        runtime.prefill(w, runtime.DeviceTokens(tok), M)
+        arr = [tok.f64(x)[:, b, h] for x in ("q", "k", "v", "alpha", "beta")]
+        Mr, _ = gdn.run(Mr, *arr)
+        if i % 4 == 0:
+            say(f"[case] prompt tokens up to {ranges[i][1]}")
+    # hand-off state: float32 chunk-free prefill vs float64, 2e-3 relative L2
+    run_case(w, seed, default_calls(w), sample=idx, workers=WORKERS, M0_gpu=M, M0_ref=Mr,
+             label="prefill-b8-handoff", warm_rel=2e-3)
