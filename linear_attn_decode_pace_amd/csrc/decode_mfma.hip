@@ -65,15 +65,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #endif
 
 constexpr int CH = 8;      // tokens per chunk
-#ifndef PACE_MFMA_WAVES
-#define PACE_MFMA_WAVES 4
-#endif
-constexpr int WAVES = PACE_MFMA_WAVES;  // tiles (waves) per workgroup
 constexpr int LROW = 136;  // bf16 elements per LDS token row (128 + 8 padding)
 constexpr int OCOL = 32;   // output columns staged before a flush (one 128-byte line per row)
 constexpr int OROW = 36;   // floats per LDS output staging row (32 + 4 padding)
 
-struct WaveLds {
+// LDS of one tile: its tokens and the chunk's small matrices
+struct TileLds {
     uint16_t kq[16][LROW];  // rows 0..7: k_t, rows 8..15: q_t (bf16 bits)
     uint16_t v[CH][LROW];
     float alpha[CH], beta[CH];
@@ -83,7 +80,10 @@ struct WaveLds {
     float Tt[CH][CH];              // Tt[s][t] = T[t][s]
     float gam[CH];                 // gamma_t
     float gamC[CH];                // Gamma_{C-1, t}
-    float o[CH][OROW];             // outputs of two column blocks, flushed as full lines
+};
+// LDS of one wave: outputs of two column blocks, flushed as full lines
+struct WaveOut {
+    float o[CH][OROW];
 };
 
 struct MfmaArgs {
@@ -229,9 +229,35 @@ __device__ inline const T *at(const T *base, uint32_t byte_off) {
     return (const T *)((const char *)base + byte_off);
 }
 
-template <int DK, int BITS>
-__device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int slot, int lane,
-                             bool trace) {
+// Waves sharing one tile (WPT).  WPT = 1: a wave owns a whole tile and four
+// tiles share a workgroup.  WPT > 1 (a workgroup per tile, WPT waves splitting
+// its column blocks, the first wave computing the chunk matrices) measured
+// slower: the other waves wait at the barrier during that serial step.
+#ifndef PACE_MFMA_WPT128
+#define PACE_MFMA_WPT128 1
+#endif
+template <int DK>
+struct Split;
+template <>
+struct Split<128> {
+    static constexpr int WPT = PACE_MFMA_WPT128;
+};
+template <>
+struct Split<64> {
+    static constexpr int WPT = 1;
+};
+
+template <int WPT>
+__device__ inline void tile_sync() {
+    if constexpr (WPT == 1)
+        wave_sync();
+    else
+        __syncthreads();
+}
+
+template <int DK, int BITS, int WPT>
+__device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int b, int h,
+                             int slot, int lane, int q, bool trace) {
 #define TRACE(slot_, v_)                                        \
     do {                                                        \
         if (trace) PACE_MFMA_TRACE((slot_), lane, (float)(v_)); \
@@ -239,47 +265,50 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
     constexpr int NKS = CodeChunk<DK>::NKS;  // k-slices of 32 rows
     constexpr int NRT = CodeChunk<DK>::NRT;  // row tiles of 16 rows
     constexpr int NCB = DK / 16;             // column blocks (d_v = d_k)
+    constexpr int CPW = NCB / WPT;           // column blocks of this wave
+    static_assert(CPW % 2 == 0, "outputs are flushed every two column blocks");
     constexpr float QMAX = BITS == 4 ? 7.f : 127.f;
     const int g = lane >> 4, n = lane & 15;
     const int n_tok = a.n_tok;
     const uint32_t tok_stride = (uint32_t)a.p.B * (uint32_t)a.p.H;  // (sequence, head) rows per token
     const size_t tile_row = (size_t)b * a.p.H + h;
+    const int cb0 = q * CPW;
 
     uint8_t *codes = BITS == 4
         ? a.p.codes4 + ((size_t)b * a.p.n4 + slot) * tile_code_bytes(DK, DK, 4)
         : a.p.codes8 + ((size_t)b * a.p.n8 + slot) * tile_code_bytes(DK, DK, 8);
     float *scl = a.p.scales + tile_row * DK;
 
-    // codes and scales of the first column blocks: a ring of PF column blocks
-    // kept in flight ahead of the one being processed
-    constexpr int PF = NCB < PACE_MFMA_PREFETCH ? NCB : PACE_MFMA_PREFETCH;
+    // codes and scales of this wave's first column blocks: a ring of PF
+    // column blocks kept in flight ahead of the one being processed
+    constexpr int PF = CPW < PACE_MFMA_PREFETCH ? CPW : PACE_MFMA_PREFETCH;
     Loader<DK, BITS> ring[PF];
     float sring[PF];
 #pragma unroll
     for (int c = 0; c < PF; ++c) {
-        ring[c].load(codes, c, lane);
-        sring[c] = scl[16 * c + n];
+        ring[c].load(codes, cb0 + c, lane);
+        sring[c] = scl[16 * (cb0 + c) + n];
     }
 
-    // ---- stage the chunk's tokens in LDS (padding tokens: k = q = v = 0);
-    //      every load is issued before the first LDS write ----
+    // ---- stage the chunk's tokens in LDS (padding tokens: k = q = v = 0),
+    //      split over the tile's waves; every load before the first write ----
     {
-        constexpr int CPR = DK / 8;        // 16-byte chunks per token row
-        constexpr int NL = 24 * CPR / 64;  // loads per lane (6 for d = 128)
+        constexpr int CPR = DK / 8;                         // 16-byte chunks per token row
+        constexpr int NL = (24 * CPR + 64 * WPT - 1) / (64 * WPT);  // loads per lane
         const uint16_t *srcs[3] = {a.k + tile_row * DK, a.q + tile_row * DK, a.v + tile_row * DK};
         u32x4 val[NL];
 #pragma unroll
         for (int it = 0; it < NL; ++it) {
-            const int c = lane + 64 * it;
+            const int c = lane + 64 * (q + WPT * it);
             const int row = c / CPR, col = (c % CPR) * 8;
-            const int t = row & 7, which = (64 * it) / (8 * CPR);  // uniform per load
+            const int t = row & 7, which = row >> 3;
             val[it] = u32x4{0u, 0u, 0u, 0u};
-            if (t < n_tok)
+            if (row < 24 && t < n_tok)
                 val[it] = __builtin_nontemporal_load(
                     at((const u32x4 *)srcs[which], (uint32_t)(t * tok_stride * DK + col) * 2u));
         }
         float ab = 0.f;
-        if (lane < 16) {
+        if (q == 0 && lane < 16) {
             const int t = lane & 7;
             const bool is_beta = lane >= 8;
             ab = is_beta ? 0.f : 1.f;
@@ -288,20 +317,22 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
         }
 #pragma unroll
         for (int it = 0; it < NL; ++it) {
-            const int c = lane + 64 * it;
+            const int c = lane + 64 * (q + WPT * it);
             const int row = c / CPR, col = (c % CPR) * 8;
-            const int t = row & 7, which = (64 * it) / (8 * CPR);
-            uint16_t *dst = which < 2 ? &L.kq[which * 8 + t][col] : &L.v[t][col];
-            *(u32x4 *)dst = val[it];
+            const int t = row & 7, which = row >> 3;
+            if (row < 24) {
+                uint16_t *dst = which < 2 ? &L.kq[which * 8 + t][col] : &L.v[t][col];
+                *(u32x4 *)dst = val[it];
+            }
         }
-        if (lane < 16) {
+        if (q == 0 && lane < 16) {
             if (lane >= 8)
                 L.beta[lane & 7] = ab;
             else
                 L.alpha[lane & 7] = ab;
         }
     }
-    wave_sync();
+    tile_sync<WPT>();
 
     // ---- [K;Q] as the MFMA A operand: A row m = 4 gg + rr holds k_gg, k_{4+gg},
     //      q_gg, q_{4+gg} for rr = 0..3; k index e of slice ks is state row
@@ -316,79 +347,83 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
         u32x4 w = {r0[0], r0[1], r1[0], r1[1]};
         return __builtin_bit_cast(bf16x8, w);
     };
-    {
-        bf16x8 AP[NKS];
-        bf16x8 BG[NKS];
+
+    // ---- the chunk's small matrices, computed once per tile by its first wave ----
+    if (q == 0) {
+        {
+            bf16x8 AP[NKS];
+            bf16x8 BG[NKS];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const int c0 = 32 * ks + 4 * g, c1 = c0 + 16;
-            AP[ks] = ap_slice(ks);
-            u32x4 z = {0u, 0u, 0u, 0u};
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int c0 = 32 * ks + 4 * g, c1 = c0 + 16;
+                AP[ks] = ap_slice(ks);
+                u32x4 z = {0u, 0u, 0u, 0u};
+                if (n < 8) {
+                    u32x2 s0 = *(const u32x2 *)&L.kq[n][c0];
+                    u32x2 s1 = *(const u32x2 *)&L.kq[n][c1];
+                    z = u32x4{s0[0], s0[1], s1[0], s1[1]};
+                }
+                BG[ks] = __builtin_bit_cast(bf16x8, z);
+            }
+            // G[m][n] = row m of [K;Q] . k_n
+            f32x4 G = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) G = mfma_bf16_k32(AP[ks], BG[ks], G);
+            TRACE(0, G[0]); TRACE(1, G[1]); TRACE(2, G[2]); TRACE(3, G[3]);
             if (n < 8) {
-                u32x2 s0 = *(const u32x2 *)&L.kq[n][c0];
-                u32x2 s1 = *(const u32x2 *)&L.kq[n][c1];
-                z = u32x4{s0[0], s0[1], s1[0], s1[1]};
+                L.kk[g][n] = G[0];
+                L.kk[4 + g][n] = G[1];
+                L.qk[g][n] = G[2];
+                L.qk[4 + g][n] = G[3];
             }
-            BG[ks] = __builtin_bit_cast(bf16x8, z);
         }
-        // G[m][n] = row m of [K;Q] . k_n
-        f32x4 G = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) G = mfma_bf16_k32(AP[ks], BG[ks], G);
-        TRACE(0, G[0]); TRACE(1, G[1]); TRACE(2, G[2]); TRACE(3, G[3]);
-        if (n < 8) {
-            L.kk[g][n] = G[0];
-            L.kk[4 + g][n] = G[1];
-            L.qk[g][n] = G[2];
-            L.qk[4 + g][n] = G[3];
-        }
-    }
-    wave_sync();
+        wave_sync();
 
-    // ---- gates: Gamma_ts as products of alpha (no log / exp), A and Lq ----
-    {
-        float al[CH];
+        // gates: Gamma_ts as products of alpha (no log / exp), A and Lq
+        {
+            float al[CH];
 #pragma unroll
-        for (int r = 0; r < CH; ++r) al[r] = L.alpha[r];
-        const int t = lane >> 3, s = lane & 7;
-        float gts = 1.f;
+            for (int r = 0; r < CH; ++r) al[r] = L.alpha[r];
+            const int t = lane >> 3, s = lane & 7;
+            float gts = 1.f;
 #pragma unroll
-        for (int r = 1; r < CH; ++r) gts *= (r > s && r <= t) ? al[r] : 1.f;
-        L.A[t][s] = s < t ? gts * L.kk[t][s] : 0.f;
-        L.Lq[t][s] = s <= t ? gts * L.qk[t][s] : 0.f;
-        if (lane < CH) {
-            float gm = 1.f, gc = 1.f;
+            for (int r = 1; r < CH; ++r) gts *= (r > s && r <= t) ? al[r] : 1.f;
+            L.A[t][s] = s < t ? gts * L.kk[t][s] : 0.f;
+            L.Lq[t][s] = s <= t ? gts * L.qk[t][s] : 0.f;
+            if (lane < CH) {
+                float gm = 1.f, gc = 1.f;
 #pragma unroll
-            for (int r = 0; r < CH; ++r) {
-                gm *= r <= lane ? al[r] : 1.f;
-                gc *= r > lane ? al[r] : 1.f;
+                for (int r = 0; r < CH; ++r) {
+                    gm *= r <= lane ? al[r] : 1.f;
+                    gc *= r > lane ? al[r] : 1.f;
+                }
+                L.gam[lane] = gm;
+                L.gamC[lane] = gc;
             }
-            L.gam[lane] = gm;
-            L.gamC[lane] = gc;
         }
-    }
-    wave_sync();
+        wave_sync();
 
-    // ---- UT transform: column s of Z = (I + diag(beta) A)^-1 by forward
-    //      substitution; T = Z diag(beta) ----
-    {
-        const int s = lane & 7;
-        float be[CH], z[CH];
+        // UT transform: column s of Z = (I + diag(beta) A)^-1 by forward
+        // substitution; T = Z diag(beta)
+        {
+            const int s = lane & 7;
+            float be[CH], z[CH];
 #pragma unroll
-        for (int r = 0; r < CH; ++r) be[r] = L.beta[r];
+            for (int r = 0; r < CH; ++r) be[r] = L.beta[r];
 #pragma unroll
-        for (int t = 0; t < CH; ++t) {
-            float sum = 0.f;
+            for (int t = 0; t < CH; ++t) {
+                float sum = 0.f;
 #pragma unroll
-            for (int u = 0; u < t; ++u) sum = fmaf(L.A[t][u], z[u], sum);
-            z[t] = (t == s ? 1.f : 0.f) - be[t] * sum;
-        }
-        if (lane < CH) {
+                for (int u = 0; u < t; ++u) sum = fmaf(L.A[t][u], z[u], sum);
+                z[t] = (t == s ? 1.f : 0.f) - be[t] * sum;
+            }
+            if (lane < CH) {
 #pragma unroll
-            for (int t = 0; t < CH; ++t) L.Tt[s][t] = z[t] * be[s];
+                for (int t = 0; t < CH; ++t) L.Tt[s][t] = z[t] * be[s];
+            }
         }
     }
-    wave_sync();
+    tile_sync<WPT>();
 
     // ---- A operand of the chunk mixing (float32 16x16x4 MFMA, 4 steps over
     //      [X tokens 0-3, X 4-7, Y 0-3, Y 4-7]):
@@ -439,25 +474,25 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
         }
     }
 
-
     float *obase = a.out + tile_row * DK;
     const uint32_t o_tok = tok_stride * DK * 4u;  // bytes between tokens of out
 
-    // ---- column blocks (unrolled: ring slots stay in fixed registers) ----
+    // ---- this wave's column blocks (unrolled: ring slots stay in fixed registers) ----
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
+    for (int cc = 0; cc < CPW; ++cc) {
         // compiler-only barrier: keeps the per-block LDS re-reads from being
         // hoisted out of the unrolled loop into long-lived registers
         asm volatile("" ::: "memory");
+        const int cb = cb0 + cc;
         const int j = 16 * cb + n;
-        const int slot = cb % PF;
+        const int slot = cc % PF;
         const float s = sring[slot];
 
         // KAPPA * codes -> float32 (the accumulator's start) and bf16 B operands
         constexpr float KAPPA = Loader<DK, BITS>::KAPPA;
         f32x4 acc[NRT];
         ring[slot].codes_f32(acc);
-        if (cb + PF < NCB) {
+        if (cc + PF < CPW) {
             ring[slot].load(codes, cb + PF, lane);
             sring[slot] = scl[j + 16 * PF];
         }
@@ -510,14 +545,14 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
         }
         if (g >= 2) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) L.o[4 * (g - 2) + r][j % OCOL] = WO[r];
+            for (int r = 0; r < 4; ++r) WO_lds.o[4 * (g - 2) + r][j % OCOL] = WO[r];
         }
-        if (cb % 2 == 1) {
+        if (cc % 2 == 1) {
             // every second column block: flush 8 rows x 128 bytes, one 16-byte
             // chunk per lane (lane -> row lane / 8, chunk lane % 8)
             wave_sync();
             const int t = lane >> 3, c4 = (lane & 7) * 4;
-            const f32x4 x = *(const f32x4 *)&L.o[t][c4];
+            const f32x4 x = *(const f32x4 *)&WO_lds.o[t][c4];
             if (t < n_tok)
                 __builtin_nontemporal_store(
                     x, at((f32x4 *)obase, (uint32_t)t * o_tok + (uint32_t)(16 * cb - 16 + c4) * 4u));
@@ -578,27 +613,30 @@ __device__ void process_tile(const MfmaArgs &a, WaveLds &L, int b, int h, int sl
         outc.store(codes, cb, lane);
         if (g == 0) scl[j] = s_new;
     }
-
 #undef TRACE
 }
 
 template <int DK>
-__global__ void __launch_bounds__(64 * WAVES) decode_mfma_kernel(MfmaArgs a) {
-    __shared__ WaveLds lds[WAVES];
+__global__ void __launch_bounds__(256) decode_mfma_kernel(MfmaArgs a) {
+    constexpr int WPT = Split<DK>::WPT;
+    constexpr int TPB = WPT == 1 ? 4 : 1;  // tiles per workgroup
+    __shared__ TileLds tl[TPB];
+    __shared__ WaveOut wo[TPB * WPT];
     const int lane = threadIdx.x & 63;
-    // wave-uniform work item (scalar registers: the head lookups below are
-    // scalar-cache loads, not a dependent vector load at the head of the tile)
+    // wave-uniform indices (scalar registers: the head lookup below is a
+    // scalar-cache load, not a dependent vector load at the head of the tile)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int w = blockIdx.x * WAVES + wave;
-    if (w >= a.tiles) return;
-    // sequence-major order: the heads of one sequence are neighbours, so a
-    // workgroup mixes 4-bit and 8-bit tiles and reads whole input rows
+    const int tib = wave / WPT, q = wave - tib * WPT;
+    const int w = blockIdx.x * TPB + tib;
+    if (w >= a.tiles) return;  // whole tiles only: every wave of a workgroup agrees when WPT > 1
+    // sequence-major order: the heads of one sequence are neighbours, so
+    // workgroups on a CU mix 4-bit and 8-bit tiles and read whole input rows
     const int b = w / a.p.H, h = w - b * a.p.H;
     const int m = a.p.head_map[h];  // slot | bits << 16 (scalar load)
     if ((m >> 16) == 8)
-        process_tile<DK, 8>(a, lds[wave], b, h, m & 0xffff, lane, w == 0);
+        process_tile<DK, 8, WPT>(a, tl[tib], wo[wave], b, h, m & 0xffff, lane, q, w == 0 && q == 0);
     else
-        process_tile<DK, 4>(a, lds[wave], b, h, m & 0xffff, lane, w == 0);
+        process_tile<DK, 4, WPT>(a, tl[tib], wo[wave], b, h, m & 0xffff, lane, q, w == 0 && q == 0);
 }
 
 }  // namespace
@@ -625,11 +663,15 @@ hipError_t launch_decode_mfma(const PoolView &p, const int32_t *heads8, const in
     a.n_tok = n_tok;
     a.tiles8 = p.B * p.n8;
     a.tiles = p.B * p.H;
-    dim3 grid((a.tiles + WAVES - 1) / WAVES), block(64 * WAVES);
-    if (p.dk == 128)
-        hipLaunchKernelGGL(decode_mfma_kernel<128>, grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL(decode_mfma_kernel<64>, grid, block, 0, s, a);
+    if (p.dk == 128) {
+        constexpr int WPT = Split<128>::WPT, TPB = WPT == 1 ? 4 : 1;
+        hipLaunchKernelGGL(decode_mfma_kernel<128>, dim3((a.tiles + TPB - 1) / TPB),
+                           dim3(64 * WPT * TPB), 0, s, a);
+    } else {
+        constexpr int WPT = Split<64>::WPT, TPB = WPT == 1 ? 4 : 1;
+        hipLaunchKernelGGL(decode_mfma_kernel<64>, dim3((a.tiles + TPB - 1) / TPB),
+                           dim3(64 * WPT * TPB), 0, s, a);
+    }
     return hipGetLastError();
 }
 
