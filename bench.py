@@ -35,6 +35,8 @@ from linear_attn_decode_pace_amd import inputs  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["linear_attn_decode_pace_amd/csrc/decode_mfma.hip",
+                  "linear_attn_decode_pace_amd/csrc/decode_mfma16.hip",
+                  "linear_attn_decode_pace_amd/csrc/mfma_common.h",
                   "linear_attn_decode_pace_amd/csrc/kernels_v0.hip",
                   "linear_attn_decode_pace_amd/csrc/pace_layout.h"]
 

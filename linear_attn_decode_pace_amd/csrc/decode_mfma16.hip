@@ -1,0 +1,376 @@
+// Fused dequant -> chunked gated-delta update -> requant kernel for periods of
+// 9..16 tokens (gfx950).  Same algebra, pool layout and codec as the 8-token
+// kernel (decode_mfma.hip); the chunk is C = 16 (shorter periods are padded
+// with identity tokens alpha = 1, beta = 0):
+//
+//   gamma_t = prod_{r<=t} alpha_r,  Gamma_ts = prod_{s<r<=t} alpha_r
+//   A   = strictly lower (Gamma * K K^T),  T = (I + diag(beta) A)^-1 diag(beta)
+//   X   = V - diag(gamma) K M0,   Y = diag(gamma) Q M0,   U = T X
+//   O   = Y + lower_incl(Gamma * Q K^T) U,   M_C = gamma_C M0 + K^T diag(Gamma_C,:) U
+//
+// Token placement: lane group g (lane = 16 g + n) holds tokens 4 r + g,
+// r = 0..3, of the [K.codes; Q.codes] products (the MFMA output rows 4 g + r),
+// which is exactly the reduction index the float32 16x16x4 MFMA steps take
+// from each lane; the chunk-mixing chain then returns W and O rows 4 g + r,
+// i.e. tokens 4 g + r, which are the reduction indices this lane feeds to the
+// K^T W update (16x16x16 bf16 MFMA, W split into hi + mid + lo): no
+// cross-lane exchange is needed at C = 16.
+#include "mfma_common.h"
+
+namespace pace {
+namespace {
+
+constexpr int C16 = 16;     // tokens per chunk
+constexpr int LROW16 = 136;  // bf16 elements per LDS token row (128 + 8 padding)
+constexpr int OCOL16 = 32;   // output columns staged before a flush
+constexpr int OROW16 = 36;   // floats per LDS output staging row
+
+struct alignas(16) Tile16Lds {
+    uint16_t kq[2 * C16][LROW16];  // rows 0..15: k_t, rows 16..31: q_t (bf16 bits)
+    uint16_t v[C16][LROW16];
+    float alpha[C16], beta[C16];
+    union {
+        struct {
+            float kk[C16][C16], qk[C16][C16];  // k_t.k_s, q_t.k_s
+            float A[C16][C16];                 // strictly lower Gamma * K K^T
+            float Lq[C16][C16];                // lower incl. diagonal Gamma * Q K^T
+        } m;                                   // chunk matrices (dead after the operands are built)
+        float o[C16][OROW16];                  // outputs of two column blocks
+    } u;
+    float Tt[C16][C16];  // Tt[s][t] = T[t][s]
+    float gam[C16];      // gamma_t
+    float gamC[C16];     // Gamma_{C-1, t}
+};
+
+constexpr int TPB16 = 2;  // tiles (waves) per workgroup
+
+template <int DK, int BITS>
+__device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, int slot, int lane) {
+    constexpr int NKS = CodeChunk<DK>::NKS;  // k-slices of 32 rows
+    constexpr int NRT = CodeChunk<DK>::NRT;  // row tiles of 16 rows
+    constexpr int NCB = DK / 16;             // column blocks (d_v = d_k)
+    constexpr float QMAX = BITS == 4 ? 7.f : 127.f;
+    constexpr float KAPPA = Loader<DK, BITS>::KAPPA;
+    const int g = lane >> 4, n = lane & 15;
+    const int n_tok = a.n_tok;
+    const uint32_t tok_stride = (uint32_t)a.p.B * (uint32_t)a.p.H;
+    const size_t tile_row = (size_t)b * a.p.H + h;
+
+    uint8_t *codes = BITS == 4
+        ? a.p.codes4 + ((size_t)b * a.p.n4 + slot) * tile_code_bytes(DK, DK, 4)
+        : a.p.codes8 + ((size_t)b * a.p.n8 + slot) * tile_code_bytes(DK, DK, 8);
+    float *scl = a.p.scales + tile_row * DK;
+
+    constexpr int PF = NCB < PACE_MFMA_PREFETCH ? NCB : PACE_MFMA_PREFETCH;
+    Loader<DK, BITS> ring[PF];
+    float sring[PF];
+#pragma unroll
+    for (int c = 0; c < PF; ++c) {
+        ring[c].load(codes, c, lane);
+        sring[c] = scl[16 * c + n];
+    }
+
+    // ---- stage the chunk's tokens (48 rows) in LDS; padding tokens are zero ----
+    {
+        constexpr int CPR = DK / 8;                // 16-byte chunks per token row
+        constexpr int NL = 3 * C16 * CPR / 64;     // loads per lane (12 for d = 128)
+        const uint16_t *srcs[3] = {a.k + tile_row * DK, a.q + tile_row * DK, a.v + tile_row * DK};
+        u32x4 val[NL];
+#pragma unroll
+        for (int it = 0; it < NL; ++it) {
+            const int c = lane + 64 * it;
+            const int row = c / CPR, col = (c % CPR) * 8;
+            const int t = row & 15, which = row >> 4;  // uniform per load
+            val[it] = u32x4{0u, 0u, 0u, 0u};
+            if (t < n_tok)
+                val[it] = __builtin_nontemporal_load(
+                    at((const u32x4 *)srcs[which], (uint32_t)(t * tok_stride * DK + col) * 2u));
+        }
+        float ab = 0.f;
+        if (lane < 32) {
+            const int t = lane & 15;
+            const bool is_beta = lane >= 16;
+            ab = is_beta ? 0.f : 1.f;
+            if (t < n_tok)
+                ab = *at(is_beta ? a.beta + tile_row : a.alpha + tile_row, (uint32_t)t * tok_stride * 4u);
+        }
+#pragma unroll
+        for (int it = 0; it < NL; ++it) {
+            const int c = lane + 64 * it;
+            const int row = c / CPR, col = (c % CPR) * 8;
+            const int t = row & 15, which = row >> 4;
+            uint16_t *dst = which < 2 ? &L.kq[which * 16 + t][col] : &L.v[t][col];
+            *(u32x4 *)dst = val[it];
+        }
+        if (lane < 32) {
+            if (lane >= 16)
+                L.beta[lane & 15] = ab;
+            else
+                L.alpha[lane & 15] = ab;
+        }
+    }
+    wave_sync();
+
+    // ---- A operands: A row m of the K (Q) block is token 4 (m % 4) + m / 4, so
+    //      output row 4 g + r of P is token 4 r + g; k index e of slice ks is
+    //      state row 32 ks + 16 (e / 4) + 4 g + e % 4 ----
+    const int tok_n = 4 * (n & 3) + (n >> 2);
+    auto ap_slice = [&](int blk, int ks) {
+        const int c0 = 32 * ks + 4 * g, c1 = c0 + 16;
+        const int row = 16 * blk + tok_n;
+        u32x2 r0 = *(const u32x2 *)&L.kq[row][c0];
+        u32x2 r1 = *(const u32x2 *)&L.kq[row][c1];
+        u32x4 w = {r0[0], r0[1], r1[0], r1[1]};
+        return __builtin_bit_cast(bf16x8, w);
+    };
+    {
+        // G_K[m][n] = k_{t(m)} . k_n, G_Q[m][n] = q_{t(m)} . k_n
+        f32x4 GK = {0.f, 0.f, 0.f, 0.f}, GQ = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int c0 = 32 * ks + 4 * g, c1 = c0 + 16;
+            u32x2 s0 = *(const u32x2 *)&L.kq[n][c0];
+            u32x2 s1 = *(const u32x2 *)&L.kq[n][c1];
+            const bf16x8 BG = __builtin_bit_cast(bf16x8, u32x4{s0[0], s0[1], s1[0], s1[1]});
+            GK = mfma_bf16_k32(ap_slice(0, ks), BG, GK);
+            GQ = mfma_bf16_k32(ap_slice(1, ks), BG, GQ);
+        }
+        wave_sync();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            L.u.m.kk[4 * r + g][n] = GK[r];
+            L.u.m.qk[4 * r + g][n] = GQ[r];
+        }
+    }
+    wave_sync();
+
+    // ---- gates (products of alpha), A and Lq: lane -> row t = lane / 4,
+    //      columns s = 4 (lane % 4) + e ----
+    {
+        float al[C16];
+#pragma unroll
+        for (int r = 0; r < C16; ++r) al[r] = L.alpha[r];
+        const int t = lane >> 2, s0 = 4 * (lane & 3);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int s = s0 + e;
+            float gts = 1.f;
+#pragma unroll
+            for (int r = 1; r < C16; ++r) gts *= (r > s && r <= t) ? al[r] : 1.f;
+            L.u.m.A[t][s] = s < t ? gts * L.u.m.kk[t][s] : 0.f;
+            L.u.m.Lq[t][s] = s <= t ? gts * L.u.m.qk[t][s] : 0.f;
+        }
+        if (lane < C16) {
+            float gm = 1.f, gc = 1.f;
+#pragma unroll
+            for (int r = 0; r < C16; ++r) {
+                gm *= r <= lane ? al[r] : 1.f;
+                gc *= r > lane ? al[r] : 1.f;
+            }
+            L.gam[lane] = gm;
+            L.gamC[lane] = gc;
+        }
+    }
+    wave_sync();
+
+    // ---- UT transform: column s of Z = (I + diag(beta) A)^-1 by forward
+    //      substitution; T = Z diag(beta) ----
+    {
+        const int s = lane & 15;
+        float be[C16], z[C16];
+#pragma unroll
+        for (int r = 0; r < C16; ++r) be[r] = L.beta[r];
+#pragma unroll
+        for (int t = 0; t < C16; ++t) {
+            float sum = 0.f;
+#pragma unroll
+            for (int u = 0; u < t; ++u) sum = fmaf(L.u.m.A[t][u], z[u], sum);
+            z[t] = (t == s ? 1.f : 0.f) - be[t] * sum;
+        }
+        if (lane < C16) {
+#pragma unroll
+            for (int t = 0; t < C16; ++t) L.Tt[s][t] = z[t] * be[s];
+        }
+    }
+    wave_sync();
+
+    // ---- chunk-mixing operands (float32 16x16x4 MFMA; step st takes token
+    //      4 st + g from lane group g):
+    //      W chain, row m = token m: A = Gamma_{C-1,m} T[m][4 st + k]
+    //      O chain, row m = token m: A = (Lq T)[m][4 st + k] on X, identity on Y ----
+    float CW[4], CO[4];
+    {
+        const float gct = L.gamC[n];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const int s = 4 * st + g;
+            CW[st] = gct * L.Tt[s][n];
+            float r2 = 0.f;
+#pragma unroll
+            for (int u = 0; u < C16; ++u) r2 = fmaf(L.u.m.Lq[n][u], L.Tt[s][u], r2);
+            CO[st] = r2;
+        }
+    }
+    float gam_r[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) gam_r[r] = L.gam[4 * r + g];
+    const float gamC = L.gam[C16 - 1];
+
+    // K^T as the update's A operand: row i = 16 rt + n, k index 4 g + e is token 4 g + e
+    s16x4 AU[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+        const int i = 16 * rt + n;
+        s16x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = (short)L.kq[4 * g + e][i];
+        AU[rt] = x;
+    }
+    wave_sync();  // the chunk matrices are dead from here on: their LDS holds outputs
+
+    float *obase = a.out + tile_row * DK;
+    const uint32_t o_tok = tok_stride * DK * 4u;
+
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        asm volatile("" ::: "memory");
+        const int j = 16 * cb + n;
+        const int slot = cb % PF;
+        const float s = sring[slot];
+        f32x4 acc[NRT];
+        ring[slot].codes_f32(acc);
+        if (cb + PF < NCB) {
+            ring[slot].load(codes, cb + PF, lane);
+            sring[slot] = scl[j + 16 * PF];
+        }
+
+        // P_K[r] = KAPPA k_{4r+g} . c_j,  P_Q[r] = KAPPA q_{4r+g} . c_j
+        f32x4 PK = {0.f, 0.f, 0.f, 0.f}, PQ = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            u32x4 w = {pk_bf16(acc[2 * ks][0], acc[2 * ks][1]), pk_bf16(acc[2 * ks][2], acc[2 * ks][3]),
+                       pk_bf16(acc[2 * ks + 1][0], acc[2 * ks + 1][1]),
+                       pk_bf16(acc[2 * ks + 1][2], acc[2 * ks + 1][3])};
+            const bf16x8 Bc = __builtin_bit_cast(bf16x8, w);
+            PK = mfma_bf16_k32(ap_slice(0, ks), Bc, PK);
+            PQ = mfma_bf16_k32(ap_slice(1, ks), Bc, PQ);
+        }
+        const float sk = s * (1.f / KAPPA);
+        const float sig_raw = gamC * s;
+        const bool tiny = s > 0.f && !(sig_raw >= 1.17549435e-38f);
+        const float sig = ((s > 0.f && !tiny) ? sig_raw : 1.f) * (1.f / KAPPA);
+        if (__builtin_amdgcn_ballot_w64(tiny)) {
+            const float m0 = tiny ? sig_raw : 1.f;
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) acc[rt] *= m0;
+        }
+        const float inv_sig = __builtin_amdgcn_rcpf(sig);
+        float X[4], Y[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float sg = gam_r[r] * sk;
+            X[r] = fmaf(-sg, PK[r], bf2f(L.v[4 * r + g][j]));
+            Y[r] = sg * PQ[r];
+        }
+        f32x4 W = {0.f, 0.f, 0.f, 0.f}, O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            W = mfma_f32_k4(CW[st], X[st] * inv_sig, W);
+            O = mfma_f32_k4(CO[st], X[st], O);
+        }
+#pragma unroll
+        for (int st = 0; st < 4; ++st) O = mfma_f32_k4(n == 4 * st + g ? 1.f : 0.f, Y[st], O);
+
+        // outputs: tokens 4 g + r of column j; flush 16 rows x 128 bytes every two blocks
+#pragma unroll
+        for (int r = 0; r < 4; ++r) L.u.o[4 * g + r][j % OCOL16] = O[r];
+        if (cb % 2 == 1) {
+            wave_sync();
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int t = (lane >> 3) + 8 * half, c4 = (lane & 7) * 4;
+                const f32x4 x = *(const f32x4 *)&L.u.o[t][c4];
+                if (t < n_tok)
+                    __builtin_nontemporal_store(
+                        x, at((f32x4 *)obase, (uint32_t)t * o_tok + (uint32_t)(16 * cb - 16 + c4) * 4u));
+            }
+        }
+
+        // W (tokens 4 g + r, units of sig) split into three bf16 parts
+        const uint32_t hi01 = pk_bf16(W[0], W[1]), hi23 = pk_bf16(W[2], W[3]);
+        const float r0 = W[0] - lo_f32(hi01), r1 = W[1] - hi_f32(hi01);
+        const float r2 = W[2] - lo_f32(hi23), r3 = W[3] - hi_f32(hi23);
+        const uint32_t md01 = pk_bf16(r0, r1), md23 = pk_bf16(r2, r3);
+        const uint32_t lo01 = pk_bf16(r0 - lo_f32(md01), r1 - hi_f32(md01));
+        const uint32_t lo23 = pk_bf16(r2 - lo_f32(md23), r3 - hi_f32(md23));
+        const s16x4 BH = __builtin_bit_cast(s16x4, u32x2{hi01, hi23});
+        const s16x4 BM = __builtin_bit_cast(s16x4, u32x2{md01, md23});
+        const s16x4 BL = __builtin_bit_cast(s16x4, u32x2{lo01, lo23});
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+            acc[rt] = mfma_bf16_k16(AU[rt], BH, acc[rt]);
+            acc[rt] = mfma_bf16_k16(AU[rt], BM, acc[rt]);
+            acc[rt] = mfma_bf16_k16(AU[rt], BL, acc[rt]);
+        }
+
+        // ---- re-encode the column ----
+        float am = 0.f;
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) am = fmaxf(am, fabsf(acc[rt][r]));
+        am = xor_max(am, 16);
+        am = xor_max(am, 32);
+        const float absmax = am * sig;
+        const float s_new = absmax * (1.f / QMAX);
+        const float ratio = s_new > 0.f ? sig * __builtin_amdgcn_rcpf(s_new) : 0.f;
+        uint32_t y[NRT][4];
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y[rt][r] = __float_as_uint(fmaf(acc[rt][r], ratio, 12582912.f));
+        Loader<DK, BITS> outc;
+        if constexpr (BITS == 4) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const uint32_t lo = gather_low_bytes(y[2 * ks][0], y[2 * ks][1], y[2 * ks][2], y[2 * ks][3]);
+                const uint32_t hi = gather_low_bytes(y[2 * ks + 1][0], y[2 * ks + 1][1],
+                                                     y[2 * ks + 1][2], y[2 * ks + 1][3]);
+                outc.d[ks] = (lo & 0x0f0f0f0fu) | ((hi << 4) & 0xf0f0f0f0u);
+            }
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) outc.d[rt] = gather_low_bytes(y[rt][0], y[rt][1], y[rt][2], y[rt][3]);
+        }
+        outc.store(codes, cb, lane);
+        if (g == 0) scl[j] = s_new;
+    }
+}
+
+template <int DK>
+__global__ void __launch_bounds__(64 * TPB16) decode_mfma16_kernel(MfmaArgs a) {
+    __shared__ Tile16Lds tl[TPB16];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int w = blockIdx.x * TPB16 + wave;
+    if (w >= a.tiles) return;
+    const int b = w / a.p.H, h = w - b * a.p.H;
+    const int m = a.p.head_map[h];
+    if ((m >> 16) == 8)
+        process_tile16<DK, 8>(a, tl[wave], b, h, m & 0xffff, lane);
+    else
+        process_tile16<DK, 4>(a, tl[wave], b, h, m & 0xffff, lane);
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma16(const MfmaArgs &a, hipStream_t s) {
+    dim3 grid((a.tiles + TPB16 - 1) / TPB16), block(64 * TPB16);
+    if (a.p.dk == 128)
+        hipLaunchKernelGGL(decode_mfma16_kernel<128>, grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL(decode_mfma16_kernel<64>, grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace pace

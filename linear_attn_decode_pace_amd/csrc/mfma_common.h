@@ -1,0 +1,181 @@
+// Device helpers shared by the fused decode kernels (decode_mfma.hip for
+// chunks of up to 8 tokens, decode_mfma16.hip for 9..16): operand types, bf16
+// packing, MFMA wrappers, the code loader / unpacker and byte packing.
+#pragma once
+
+#include "pace_mfma.h"
+
+namespace pace {
+
+struct MfmaArgs {
+    PoolView p;
+    const uint16_t *q, *k, *v;
+    const float *alpha, *beta;
+    float *out;
+    const int32_t *heads8;  // slot -> head, 8-bit pool
+    const int32_t *heads4;  // slot -> head, 4-bit pool
+    int n_tok;
+    int tiles8;  // B * n8: work items below this are 8-bit tiles
+    int tiles;   // B * H
+};
+
+// the 16-token chunk kernel (decode_mfma16.hip), for 9..16 tokens per call
+hipError_t launch_decode_mfma16(const MfmaArgs &a, hipStream_t s);
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Debug builds may define PACE_MFMA_TRACE(slot, lane, value) to record
+// intermediates of the first work item; it is a no-op otherwise.
+#ifndef PACE_MFMA_TRACE
+#define PACE_MFMA_TRACE(slot, lane, value) \
+    do {                                    \
+    } while (0)
+#endif
+
+// column blocks of codes kept in flight ahead of the one being processed
+#ifndef PACE_MFMA_PREFETCH
+#define PACE_MFMA_PREFETCH 2
+#endif
+
+
+__device__ inline float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ inline uint32_t pk_bf16(float lo, float hi) {
+    f32x2 x = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+__device__ inline float lo_f32(uint32_t pk) { return __uint_as_float(pk << 16); }
+__device__ inline float hi_f32(uint32_t pk) { return __uint_as_float(pk & 0xffff0000u); }
+
+// Order this wavefront's LDS accesses (no workgroup barrier: waves of a block
+// are independent; LDS operations of one wave execute in issue order).
+__device__ inline void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+__device__ inline f32x4 mfma_bf16_k32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline f32x4 mfma_bf16_k16(s16x4 a, s16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ inline f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ inline float xor_max(float x, int mask) {
+    return fmaxf(x, __shfl_xor(x, mask));
+}
+
+// low bytes of four words -> one word
+__device__ inline uint32_t gather_low_bytes(uint32_t y0, uint32_t y1, uint32_t y2, uint32_t y3) {
+    uint32_t a = __builtin_amdgcn_perm(y1, y0, 0x0c0c0400u);  // [y0.b0, y1.b0, 0, 0]
+    uint32_t b = __builtin_amdgcn_perm(y3, y2, 0x04000c0cu);  // [0, 0, y2.b0, y3.b0]
+    return a | b;
+}
+
+template <int DK>
+struct CodeChunk;
+template <>
+struct CodeChunk<128> {
+    static constexpr int NKS = 4, NRT = 8;
+};
+template <>
+struct CodeChunk<64> {
+    static constexpr int NKS = 2, NRT = 4;
+};
+
+template <int DK, int BITS>
+struct Loader {
+    // Codes are streamed: read once and written once per period, with a pool
+    // far larger than the last-level cache, so loads and stores are
+    // non-temporal.
+    // dwords a lane holds per column block: 4-bit: one per k-slice; 8-bit: one per row tile
+    static constexpr int ND = BITS == 4 ? DK / 32 : DK / 16;
+    uint32_t d[ND];
+    __device__ inline void load(const uint8_t *codes, int cb, int lane) {
+        if constexpr (BITS == 4) {
+            const uint8_t *p = codes + (size_t)cb * (64 * DK / 8) + (size_t)lane * (DK / 8);
+            if constexpr (DK == 128) {
+                u32x4 x = __builtin_nontemporal_load((const u32x4 *)p);
+                d[0] = x[0], d[1] = x[1], d[2] = x[2], d[3] = x[3];
+            } else {
+                u32x2 x = __builtin_nontemporal_load((const u32x2 *)p);
+                d[0] = x[0], d[1] = x[1];
+            }
+        } else {
+            const uint8_t *p = codes + (size_t)cb * (64 * DK / 4) + (size_t)lane * 16;
+#pragma unroll
+            for (int qd = 0; qd < DK / 64; ++qd) {
+                u32x4 x = __builtin_nontemporal_load((const u32x4 *)(p + qd * 1024));
+                d[4 * qd + 0] = x[0], d[4 * qd + 1] = x[1], d[4 * qd + 2] = x[2], d[4 * qd + 3] = x[3];
+            }
+        }
+    }
+    __device__ inline void store(uint8_t *codes, int cb, int lane) const {
+        if constexpr (BITS == 4) {
+            uint8_t *p = codes + (size_t)cb * (64 * DK / 8) + (size_t)lane * (DK / 8);
+            if constexpr (DK == 128) {
+                u32x4 x = {d[0], d[1], d[2], d[3]};
+                __builtin_nontemporal_store(x, (u32x4 *)p);
+            } else {
+                u32x2 x = {d[0], d[1]};
+                __builtin_nontemporal_store(x, (u32x2 *)p);
+            }
+        } else {
+            uint8_t *p = codes + (size_t)cb * (64 * DK / 4) + (size_t)lane * 16;
+#pragma unroll
+            for (int qd = 0; qd < DK / 64; ++qd) {
+                u32x4 x = {d[4 * qd], d[4 * qd + 1], d[4 * qd + 2], d[4 * qd + 3]};
+                __builtin_nontemporal_store(x, (u32x4 *)(p + qd * 1024));
+            }
+        }
+    }
+    // KAPPA * code of (row tile rt, row r in the lane's group) as float: 4-bit
+    // codes are moved to the high nibble of their byte (a signed byte worth
+    // 16 c), so one sign-extending byte conversion reads each of them
+    static constexpr float KAPPA = BITS == 4 ? 16.f : 1.f;
+    __device__ inline void codes_f32(f32x4 *acc) const {
+        if constexpr (BITS == 4) {
+#pragma unroll
+            for (int ks = 0; ks < ND; ++ks) {
+                const uint32_t lo = (d[ks] << 4) & 0xf0f0f0f0u;  // row tile 2 ks
+                const uint32_t hi = d[ks] & 0xf0f0f0f0u;         // row tile 2 ks + 1
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    acc[2 * ks][r] = (float)(int)__builtin_amdgcn_sbfe(lo, 8 * r, 8);
+                    acc[2 * ks + 1][r] = (float)(int)__builtin_amdgcn_sbfe(hi, 8 * r, 8);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < ND; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[rt][r] = (float)(int)__builtin_amdgcn_sbfe(d[rt], 8 * r, 8);
+        }
+    }
+};
+
+// byte-offset access from a wave-uniform base: keeps per-lane address math in
+// 32 bits (the base lives in scalar registers)
+template <class T>
+__device__ inline T *at(T *base, uint32_t byte_off) {
+    return (T *)((char *)base + byte_off);
+}
+template <class T>
+__device__ inline const T *at(const T *base, uint32_t byte_off) {
+    return (const T *)((const char *)base + byte_off);
+}
+
+}  // namespace
+}  // namespace pace

@@ -1,4 +1,5 @@
-// Fused MFMA decode kernel for gfx950 (decode_mfma.hip).
+// Fused MFMA decode kernels for gfx950 (decode_mfma.hip: chunks of up to 8
+// tokens; decode_mfma16.hip: 9..16).
 #pragma once
 
 #include "pace_layout.h"

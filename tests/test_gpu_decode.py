@@ -43,3 +43,16 @@ def test_all_heads_int8():
 def test_f32_inputs_d128():
     w = inputs.ragged("f32-d128", 104, B=2, H=3, n_int8=1, dtype=inputs.DT_F32, steps=16)
     run_case(w, 5, default_calls(w))
+
+
+def test_long_periods_ragged():
+    # calls of 9..16 tokens (the 16-token chunk kernel) interleaved with
+    # shorter ones, odd batch and head counts, 2 of 5 heads at 8 bits
+    w = inputs.ragged("long-periods", 105, B=3, H=5, n_int8=2, n_outliers=8, period=16, steps=64)
+    calls = [(0, 16), (16, 25), (25, 37), (37, 45), (45, 58), (58, 64)]
+    run_case(w, 6, calls)
+
+
+def test_d64_long_periods():
+    w = inputs.ragged("d64-long", 106, B=4, H=4, dk=64, dv=64, n_int8=1, period=16, steps=48)
+    run_case(w, 7, [(0, 16), (16, 26), (26, 42), (42, 48)])
