@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define PACE_ABI_VERSION 1
+#define PACE_ABI_VERSION 2
 
 /* status codes */
 #define PACE_OK 0
@@ -85,7 +85,15 @@ extern "C" {
 #define PACE_READ_DEQUANT 1 /* dst: device float32 [B, H, d_k, d_v] = c_ij * s_j; scales_dst may be NULL */
 #define PACE_READ_RAW 2     /* dst: device bytes [pace_raw_bytes()]; scales_dst must be NULL */
 
-/* config flags (none defined yet; must be 0) */
+/* config flags */
+/* PACE_STATS_ERR: every encode (the PACE_INIT_F32 encode at alloc and the
+ * period-end encode of each pace_decode_period call) also records, per column,
+ * the squared round-trip error sum_i (M_ij - c_ij s_j)^2 and sum_i M_ij^2 of the
+ * high-precision state M it encodes; pace_quant_stats sums them per head.
+ * Costs B * H * d_v * 8 bytes of device memory and that much extra writing per
+ * encode.  Requires heads <= PACE_STATS_MAX_HEADS. */
+#define PACE_STATS_ERR 0x1u
+#define PACE_STATS_MAX_HEADS 256
 
 typedef struct pace_state pace_state; /* opaque; owns the device pools */
 
@@ -97,7 +105,7 @@ typedef struct pace_config {
     int32_t period;           /* k: most tokens one pace_decode_period call may apply, 1..64 */
     int32_t in_dtype;         /* PACE_DTYPE_F32 or PACE_DTYPE_BF16: element type of q, k, v */
     const uint8_t *head_bits; /* host [H]: bit width of each head, 4 or 8; copied at alloc */
-    uint32_t flags;           /* must be 0 */
+    uint32_t flags;           /* 0 or PACE_STATS_ERR */
 } pace_config;
 
 typedef struct pace_stats {
@@ -112,6 +120,17 @@ typedef struct pace_stats {
     uint64_t periods;          /* pace_decode_period calls applied since alloc */
     uint64_t tokens;           /* tokens applied since alloc */
     uint64_t zero_columns;     /* stored columns whose scale is 0 */
+    /* with PACE_STATS_ERR (err_tracked = 1), per head h < heads, over every
+     * sequence b and entry (i, j) of the state M of the last encode:
+     * err_sq[h] = sum (M_ij - c_ij s_j)^2 and ref_sq[h] = sum M_ij^2, so that
+     * err_sq / ref_sq is that head's relative squared round-trip error (the
+     * column quantizer's fidelity: 'PACE: A New 4-Bit Recurrent State
+     * Quantization Method ...', section 'Channel-Aligned Encoding').  Zero
+     * after PACE_INIT_ZERO or PACE_INIT_RAW until the first decode call.
+     * Without the flag: err_tracked = 0 and both arrays are zero. */
+    int32_t err_tracked;
+    double err_sq[PACE_STATS_MAX_HEADS];
+    double ref_sq[PACE_STATS_MAX_HEADS];
 } pace_stats;
 
 /* ABI version this library was built with (PACE_ABI_VERSION). */
@@ -176,7 +195,8 @@ int pace_read_state(const pace_state *st, int what, void *dst, float *scales_dst
 
 /*
  * Storage accounting and counters of a handle.  out is host memory.  Counts
- * zero columns on the device, so it waits for `stream`.
+ * zero columns (and, with PACE_STATS_ERR, sums the error statistics) on the
+ * device, so it waits for `stream`.
  * Errors: EINVAL, EDEVICE.
  */
 int pace_quant_stats(const pace_state *st, pace_stats *out, void *stream);

@@ -91,7 +91,7 @@ __device__ inline void tile_sync() {
         __syncthreads();
 }
 
-template <int DK, int BITS, int WPT>
+template <int DK, int BITS, int WPT, bool ERR>
 __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int b, int h,
                              int slot, int lane, int q, bool trace) {
 #define TRACE(slot_, v_)                                        \
@@ -448,11 +448,12 @@ __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int
         }
         outc.store(codes, cb, lane);
         if (g == 0) scl[j] = s_new;
+        if constexpr (ERR) column_error<NRT>(acc, y, sig, s_new, a.p.colerr + (tile_row * DK + j) * 2, g);
     }
 #undef TRACE
 }
 
-template <int DK>
+template <int DK, bool ERR>
 __global__ void __launch_bounds__(256) decode_mfma_kernel(MfmaArgs a) {
     constexpr int WPT = Split<DK>::WPT;
     constexpr int TPB = WPT == 1 ? 4 : 1;  // tiles per workgroup
@@ -470,9 +471,9 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(MfmaArgs a) {
     const int b = w / a.p.H, h = w - b * a.p.H;
     const int m = a.p.head_map[h];  // slot | bits << 16 (scalar load)
     if ((m >> 16) == 8)
-        process_tile<DK, 8, WPT>(a, tl[tib], wo[wave], b, h, m & 0xffff, lane, q, w == 0 && q == 0);
+        process_tile<DK, 8, WPT, ERR>(a, tl[tib], wo[wave], b, h, m & 0xffff, lane, q, w == 0 && q == 0);
     else
-        process_tile<DK, 4, WPT>(a, tl[tib], wo[wave], b, h, m & 0xffff, lane, q, w == 0 && q == 0);
+        process_tile<DK, 4, WPT, ERR>(a, tl[tib], wo[wave], b, h, m & 0xffff, lane, q, w == 0 && q == 0);
 }
 
 }  // namespace
@@ -501,14 +502,21 @@ hipError_t launch_decode_mfma(const PoolView &p, const int32_t *heads8, const in
     a.tiles8 = p.B * p.n8;
     a.tiles = p.B * p.H;
     if (n_tok > CH) return launch_decode_mfma16(a, s);
+    const bool err = p.colerr != nullptr;
     if (p.dk == 128) {
         constexpr int WPT = Split<128>::WPT, TPB = WPT == 1 ? 4 : 1;
-        hipLaunchKernelGGL(decode_mfma_kernel<128>, dim3((a.tiles + TPB - 1) / TPB),
-                           dim3(64 * WPT * TPB), 0, s, a);
+        const dim3 grid((a.tiles + TPB - 1) / TPB), block(64 * WPT * TPB);
+        if (err)
+            hipLaunchKernelGGL((decode_mfma_kernel<128, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((decode_mfma_kernel<128, false>), grid, block, 0, s, a);
     } else {
         constexpr int WPT = Split<64>::WPT, TPB = WPT == 1 ? 4 : 1;
-        hipLaunchKernelGGL(decode_mfma_kernel<64>, dim3((a.tiles + TPB - 1) / TPB),
-                           dim3(64 * WPT * TPB), 0, s, a);
+        const dim3 grid((a.tiles + TPB - 1) / TPB), block(64 * WPT * TPB);
+        if (err)
+            hipLaunchKernelGGL((decode_mfma_kernel<64, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((decode_mfma_kernel<64, false>), grid, block, 0, s, a);
     }
     return hipGetLastError();
 }

@@ -44,7 +44,7 @@ struct alignas(16) Tile16Lds {
 
 constexpr int TPB16 = 2;  // tiles (waves) per workgroup
 
-template <int DK, int BITS>
+template <int DK, int BITS, bool ERR>
 __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, int slot, int lane) {
     constexpr int NKS = CodeChunk<DK>::NKS;  // k-slices of 32 rows
     constexpr int NRT = CodeChunk<DK>::NRT;  // row tiles of 16 rows
@@ -344,10 +344,11 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
         }
         outc.store(codes, cb, lane);
         if (g == 0) scl[j] = s_new;
+        if constexpr (ERR) column_error<NRT>(acc, y, sig, s_new, a.p.colerr + (tile_row * DK + j) * 2, g);
     }
 }
 
-template <int DK>
+template <int DK, bool ERR>
 __global__ void __launch_bounds__(64 * TPB16) decode_mfma16_kernel(MfmaArgs a) {
     __shared__ Tile16Lds tl[TPB16];
     const int lane = threadIdx.x & 63;
@@ -357,19 +358,27 @@ __global__ void __launch_bounds__(64 * TPB16) decode_mfma16_kernel(MfmaArgs a) {
     const int b = w / a.p.H, h = w - b * a.p.H;
     const int m = a.p.head_map[h];
     if ((m >> 16) == 8)
-        process_tile16<DK, 8>(a, tl[wave], b, h, m & 0xffff, lane);
+        process_tile16<DK, 8, ERR>(a, tl[wave], b, h, m & 0xffff, lane);
     else
-        process_tile16<DK, 4>(a, tl[wave], b, h, m & 0xffff, lane);
+        process_tile16<DK, 4, ERR>(a, tl[wave], b, h, m & 0xffff, lane);
 }
 
 }  // namespace
 
 hipError_t launch_decode_mfma16(const MfmaArgs &a, hipStream_t s) {
     dim3 grid((a.tiles + TPB16 - 1) / TPB16), block(64 * TPB16);
-    if (a.p.dk == 128)
-        hipLaunchKernelGGL(decode_mfma16_kernel<128>, grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL(decode_mfma16_kernel<64>, grid, block, 0, s, a);
+    const bool err = a.p.colerr != nullptr;
+    if (a.p.dk == 128) {
+        if (err)
+            hipLaunchKernelGGL((decode_mfma16_kernel<128, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((decode_mfma16_kernel<128, false>), grid, block, 0, s, a);
+    } else {
+        if (err)
+            hipLaunchKernelGGL((decode_mfma16_kernel<64, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((decode_mfma16_kernel<64, false>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 

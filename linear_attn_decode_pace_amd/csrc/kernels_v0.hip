@@ -42,8 +42,11 @@ __device__ inline void load_column(const uint8_t *codes, int bits, int j, float 
 
 // Per-column quantizer: s = absmax / qmax (float32, correctly rounded),
 // c = rint(M / s) with round-half-even, clamped to +-qmax; s = 0 -> codes 0.
+// err (NULL: skipped) receives the sums over the column of (M - c s)^2 and M^2.
 template <int DK>
-__device__ inline float store_column(uint8_t *codes, int bits, int j, const float M[DK]) {
+__device__ inline float store_column(uint8_t *codes, int bits, int j, const float M[DK],
+                                     float *err) {
+    float e2 = 0.f, m2 = 0.f;
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < DK; ++i) amax = fmaxf(amax, fabsf(M[i]));
@@ -61,6 +64,11 @@ __device__ inline float store_column(uint8_t *codes, int bits, int j, const floa
                 c0 = (int)fminf(fmaxf(rintf(M[i] / s), -7.f), 7.f);
                 c1 = (int)fminf(fmaxf(rintf(M[i2] / s), -7.f), 7.f);
             }
+            if (err) {
+                const float d0 = M[i] - (float)c0 * s, d1 = M[i2] - (float)c1 * s;
+                e2 += d0 * d0 + d1 * d1;
+                m2 += M[i] * M[i] + M[i2] * M[i2];
+            }
             int sh;
             size_t o = loc4(DK, i, j, &sh);
             codes[o] = (uint8_t)((c0 & 15) | ((c1 & 15) << 4));
@@ -71,7 +79,16 @@ __device__ inline float store_column(uint8_t *codes, int bits, int j, const floa
             int c = 0;
             if (s > 0.f) c = (int)fminf(fmaxf(rintf(M[i] / s), -127.f), 127.f);
             codes[loc8(DK, i, j)] = (uint8_t)(int8_t)c;
+            if (err) {
+                const float d = M[i] - (float)c * s;
+                e2 += d * d;
+                m2 += M[i] * M[i];
+            }
         }
+    }
+    if (err) {
+        err[0] = e2;
+        err[1] = m2;
     }
     return s;
 }
@@ -118,7 +135,8 @@ __global__ void decode_v0_kernel(PoolView p, int n_tok, const void *q, const voi
     float M[DK];
     load_column<DK>(codes, bits, j, sc[j], M);
     apply_tokens<DK>(M, sk, sq, n_tok, p.B, p.H, p.dv, b, h, j, q, k, v, alpha, beta, out, bf16);
-    sc[j] = store_column<DK>(codes, bits, j, M);
+    sc[j] = store_column<DK>(codes, bits, j, M,
+                             p.colerr ? p.colerr + ((size_t)tile * p.dv + j) * 2 : nullptr);
 }
 
 template <int DK>
@@ -130,7 +148,8 @@ __global__ void encode_f32_kernel(PoolView p, const float *src) {
     float M[DK];
 #pragma unroll
     for (int i = 0; i < DK; ++i) M[i] = m[(size_t)i * p.dv + j];
-    p.scales[(size_t)tile * p.dv + j] = store_column<DK>(codes, bits, j, M);
+    p.scales[(size_t)tile * p.dv + j] = store_column<DK>(
+        codes, bits, j, M, p.colerr ? p.colerr + ((size_t)tile * p.dv + j) * 2 : nullptr);
 }
 
 template <int DK>
@@ -180,6 +199,33 @@ __global__ void count_zero_kernel(const float *scales, size_t n, unsigned long l
         mine += scales[i] == 0.f;
     for (int off = 32; off > 0; off >>= 1) mine += __shfl_xor(mine, off);
     if ((threadIdx.x & 63) == 0 && mine) atomicAdd(counter, (unsigned long long)mine);
+}
+
+// one block per head; float64 sums over sequences and columns
+__global__ void reduce_colerr_kernel(const float *colerr, int B, int H, int dv, double *out) {
+    __shared__ double part[2][4];
+    const int h = blockIdx.x;
+    double e = 0.0, m = 0.0;
+    for (long long idx = threadIdx.x; idx < (long long)B * dv; idx += blockDim.x) {
+        const long long b = idx / dv, j = idx - b * dv;
+        const float *x = colerr + (((size_t)b * H + h) * dv + j) * 2;
+        e += (double)x[0];
+        m += (double)x[1];
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+        e += __shfl_xor(e, off);
+        m += __shfl_xor(m, off);
+    }
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        part[0][wave] = e;
+        part[1][wave] = m;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        out[2 * h] = part[0][0] + part[0][1] + part[0][2] + part[0][3];
+        out[2 * h + 1] = part[1][0] + part[1][1] + part[1][2] + part[1][3];
+    }
 }
 
 }  // namespace
@@ -235,6 +281,12 @@ hipError_t launch_count_zero_scales(const PoolView &p, unsigned long long *count
     int blocks = (int)((n + 255) / 256);
     if (blocks > 4096) blocks = 4096;
     hipLaunchKernelGGL(count_zero_kernel, dim3(blocks), dim3(256), 0, s, p.scales, n, counter);
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce_colerr(const PoolView &p, double *out, hipStream_t s) {
+    hipLaunchKernelGGL(reduce_colerr_kernel, dim3(p.H), dim3(256), 0, s, p.colerr, p.B, p.H, p.dv,
+                       out);
     return hipGetLastError();
 }
 

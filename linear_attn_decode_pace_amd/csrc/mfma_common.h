@@ -166,6 +166,31 @@ struct Loader {
     }
 };
 
+// Error statistics of one column at its re-encode: sums over the column's rows
+// of (M - c s_new)^2 and M^2, with M = acc * sig and c read back from the
+// rounding sum y = acc * ratio + 1.5 * 2^23 (exact: |acc * ratio| <= qmax);
+// the four lane groups of the column are combined and lanes g == 0 store.
+template <int NRT>
+__device__ inline void column_error(const f32x4 *acc, const uint32_t (*y)[4], float sig,
+                                    float s_new, float *dst, int g) {
+    float e2 = 0.f, m2 = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float m = acc[rt][r] * sig;
+            const float c = __uint_as_float(y[rt][r]) - 12582912.f;
+            const float d = fmaf(-c, s_new, m);
+            e2 = fmaf(d, d, e2);
+            m2 = fmaf(m, m, m2);
+        }
+    e2 += __shfl_xor(e2, 16);
+    m2 += __shfl_xor(m2, 16);
+    e2 += __shfl_xor(e2, 32);
+    m2 += __shfl_xor(m2, 32);
+    if (g == 0) *(f32x2 *)dst = f32x2{e2, m2};
+}
+
 // byte-offset access from a wave-uniform base: keeps per-lane address math in
 // 32 bits (the base lives in scalar registers)
 template <class T>

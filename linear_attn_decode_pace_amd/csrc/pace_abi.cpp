@@ -27,6 +27,8 @@ struct pace_state {
     uint8_t *codes8 = nullptr;
     float *scales = nullptr;
     unsigned long long *d_counter = nullptr;
+    float *colerr = nullptr;  // PACE_STATS_ERR: [B, H, d_v, 2]
+    double *d_err = nullptr;  // PACE_STATS_ERR: [H, 2] per-head sums
     size_t bytes4 = 0, bytes8 = 0, bytes_scales = 0;
     uint64_t periods = 0, tokens = 0;
 
@@ -36,6 +38,7 @@ struct pace_state {
         p.codes8 = codes8;
         p.scales = scales;
         p.head_map = d_map;
+        p.colerr = colerr;
         p.B = cfg.batch;
         p.H = cfg.heads;
         p.dk = cfg.d_k;
@@ -117,7 +120,9 @@ PACE_API int pace_state_alloc(const pace_config *cfg, int init_kind, const void 
     if (rc) return rc;
     if (cfg->period < 1 || cfg->period > 64) return fail(PACE_EUNSUPPORTED, "period must be 1..64");
     if ((rc = check_dtype(cfg->in_dtype))) return rc;
-    if (cfg->flags != 0) return fail(PACE_EINVAL, "flags must be 0");
+    if (cfg->flags & ~PACE_STATS_ERR) return fail(PACE_EINVAL, "unknown flags 0x%x", cfg->flags);
+    if ((cfg->flags & PACE_STATS_ERR) && cfg->heads > PACE_STATS_MAX_HEADS)
+        return fail(PACE_EINVAL, "PACE_STATS_ERR takes at most %d heads", PACE_STATS_MAX_HEADS);
     if (!cfg->head_bits) return fail(PACE_EINVAL, "head_bits must not be NULL");
     for (int h = 0; h < cfg->heads; ++h)
         if (cfg->head_bits[h] != 4 && cfg->head_bits[h] != 8)
@@ -161,6 +166,8 @@ PACE_API int pace_state_alloc(const pace_config *cfg, int init_kind, const void 
         if (st->scales) (void)hipFree(st->scales);
         if (st->d_map) (void)hipFree(st->d_map);
         if (st->d_counter) (void)hipFree(st->d_counter);
+        if (st->colerr) (void)hipFree(st->colerr);
+        if (st->d_err) (void)hipFree(st->d_err);
         delete st;
         (void)code;
         return hip_fail(err, what);
@@ -176,6 +183,15 @@ PACE_API int pace_state_alloc(const pace_config *cfg, int init_kind, const void 
         return cleanup(0, "hipMalloc(head map)", e);
     if ((e = hipMalloc((void **)&st->d_counter, sizeof(unsigned long long))) != hipSuccess)
         return cleanup(0, "hipMalloc(counter)", e);
+    const size_t bytes_err = (size_t)cfg->batch * cfg->heads * cfg->d_v * 2 * sizeof(float);
+    if (cfg->flags & PACE_STATS_ERR) {
+        if ((e = hipMalloc((void **)&st->colerr, bytes_err)) != hipSuccess)
+            return cleanup(0, "hipMalloc(error statistics)", e);
+        if ((e = hipMalloc((void **)&st->d_err, 2 * sizeof(double) * cfg->heads)) != hipSuccess)
+            return cleanup(0, "hipMalloc(error sums)", e);
+        if (init_kind != PACE_INIT_F32 && (e = hipMemsetAsync(st->colerr, 0, bytes_err, s)) != hipSuccess)
+            return cleanup(0, "zero error statistics", e);
+    }
     if ((e = hipMemcpyAsync(st->d_map, st->map.data(), sizeof(int32_t) * st->map.size(),
                             hipMemcpyHostToDevice, s)) != hipSuccess)
         return cleanup(0, "copy head map", e);
@@ -215,6 +231,8 @@ PACE_API int pace_state_free(pace_state *st) {
     if (st->scales) (void)hipFree(st->scales);
     if (st->d_map) (void)hipFree(st->d_map);
     if (st->d_counter) (void)hipFree(st->d_counter);
+    if (st->colerr) (void)hipFree(st->colerr);
+    if (st->d_err) (void)hipFree(st->d_err);
     delete st;
     if (e != hipSuccess) return hip_fail(e, "pace_state_free");
     return ok();
@@ -306,9 +324,24 @@ PACE_API int pace_quant_stats(const pace_state *st, pace_stats *out, void *strea
     if (e == hipSuccess) e = pace::launch_count_zero_scales(st->view(), st->d_counter, s);
     if (e == hipSuccess)
         e = hipMemcpyAsync(&zeros, st->d_counter, sizeof zeros, hipMemcpyDeviceToHost, s);
+    std::vector<double> err;
+    if (st->colerr) {
+        err.resize(2 * (size_t)c.heads);
+        if (e == hipSuccess) e = pace::launch_reduce_colerr(st->view(), st->d_err, s);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(err.data(), st->d_err, sizeof(double) * err.size(),
+                               hipMemcpyDeviceToHost, s);
+    }
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_fail(e, "quant_stats");
     r.zero_columns = zeros;
+    if (st->colerr) {
+        r.err_tracked = 1;
+        for (int h = 0; h < c.heads; ++h) {
+            r.err_sq[h] = err[2 * h];
+            r.ref_sq[h] = err[2 * h + 1];
+        }
+    }
     *out = r;
     return ok();
 }

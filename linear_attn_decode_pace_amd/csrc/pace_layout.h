@@ -36,6 +36,9 @@ struct PoolView {
     uint8_t *codes8;
     float *scales;
     const int32_t *head_map;  // device [H]: slot | (bits << 16)
+    // device float32 [B, H, d_v, 2] or NULL: per column, the sums over its
+    // rows of (M - c s)^2 and M^2 at the column's last encode (error statistics)
+    float *colerr;
     int B, H, dk, dv, n4, n8;
 };
 
@@ -81,5 +84,8 @@ hipError_t launch_read(const PoolView &p, int what, void *dst, float *scales_dst
                        hipStream_t s);
 hipError_t launch_count_zero_scales(const PoolView &p, unsigned long long *counter,
                                     hipStream_t s);
+// per head h: out[2 h] = sum of colerr[b, h, j, 0], out[2 h + 1] = sum of
+// colerr[b, h, j, 1] over b and j, in float64
+hipError_t launch_reduce_colerr(const PoolView &p, double *out, hipStream_t s);
 
 }  // namespace pace

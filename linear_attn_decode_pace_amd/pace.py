@@ -34,6 +34,9 @@ PACE_READ_CODES = 0
 PACE_READ_DEQUANT = 1
 PACE_READ_RAW = 2
 
+PACE_STATS_ERR = 0x1
+PACE_STATS_MAX_HEADS = 256
+
 EXPORTED = ("pace_abi_version", "pace_last_error", "pace_state_alloc", "pace_state_free",
             "pace_state_config", "pace_raw_bytes", "pace_decode_period", "pace_read_state",
             "pace_quant_stats", "pace_prefill_f32")
@@ -59,10 +62,15 @@ class pace_stats(ctypes.Structure):
                 ("bytes_fp16_equiv", ctypes.c_uint64), ("bytes_int8_equiv", ctypes.c_uint64),
                 ("heads4", ctypes.c_int32), ("heads8", ctypes.c_int32),
                 ("periods", ctypes.c_uint64), ("tokens", ctypes.c_uint64),
-                ("zero_columns", ctypes.c_uint64)]
+                ("zero_columns", ctypes.c_uint64), ("err_tracked", ctypes.c_int32),
+                ("err_sq", ctypes.c_double * PACE_STATS_MAX_HEADS),
+                ("ref_sq", ctypes.c_double * PACE_STATS_MAX_HEADS)]
 
-    def as_dict(self):
-        return {name: getattr(self, name) for name, _ in self._fields_}
+    def as_dict(self, heads: int = PACE_STATS_MAX_HEADS):
+        d = {name: getattr(self, name) for name, _ in self._fields_}
+        d["err_sq"] = list(self.err_sq)[:heads]
+        d["ref_sq"] = list(self.ref_sq)[:heads]
+        return d
 
 
 def _load():
@@ -171,7 +179,7 @@ def pace_read_state(st: int, what: int, dst, scales_dst=None, stream=None) -> No
 def pace_quant_stats(st: int, stream=None) -> dict:
     s = pace_stats()
     _check(LIB.pace_quant_stats(st, ctypes.byref(s), _stream(stream)))
-    return s.as_dict()
+    return s.as_dict(pace_state_config(st)["heads"])
 
 
 def pace_prefill_f32(batch: int, heads: int, d_k: int, d_v: int, n_tok: int, in_dtype: int,

@@ -54,12 +54,12 @@ class State:
 
     def __init__(self, w: inputs.Workload, head_bits: Sequence[int],
                  init_kind: int = pace.PACE_INIT_ZERO, init: Optional[torch.Tensor] = None,
-                 period: Optional[int] = None, stream=None):
+                 period: Optional[int] = None, stream=None, flags: int = 0):
         self.w = w
         self.head_bits = np.asarray(head_bits, dtype=np.uint8)
         self.period = w.period if period is None else period
         self.handle = pace.pace_state_alloc(w.B, w.H, w.dk, w.dv, self.period, dtype_code(w),
-                                            list(self.head_bits), init_kind, init, 0, stream)
+                                            list(self.head_bits), init_kind, init, flags, stream)
 
     def free(self):
         if self.handle:

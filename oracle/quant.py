@@ -71,6 +71,17 @@ def quotients(M: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return np.where(s64 > 0, np.asarray(M, dtype=np.float64) / safe, 0.0)
 
 
+def roundtrip_error(M: np.ndarray, bits):
+    """Squared round-trip error of encoding states M [..., d_k, d_v]:
+    returns (sum (M - decode(encode(M)))**2, sum M**2), each summed over the
+    last two axes (one value per state).  Their ratio is the state's relative
+    squared quantization error under the column quantizer above."""
+    M = np.asarray(M, dtype=np.float64)
+    c, s = encode(M, bits)
+    d = M - decode(c, s)
+    return np.sum(d * d, axis=(-2, -1)), np.sum(M * M, axis=(-2, -1))
+
+
 def tie_distance(x: np.ndarray) -> np.ndarray:
     """Distance of each quotient from the nearest half-integer (rounding tie)."""
     return np.abs(np.abs(x - np.floor(x)) - 0.5)

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert pace.pace_abi_version() == 1
+    assert pace.pace_abi_version() == 2
 
 
 def _cfg(**kw):
@@ -36,11 +36,11 @@ def _cfg(**kw):
     return c
 
 
-def _alloc_status(init_kind=pace.PACE_INIT_ZERO, init=None, **kw):
+def _alloc_status(init_kind=pace.PACE_INIT_ZERO, init=None, flags=0, **kw):
     c = _cfg(**kw)
-    hb = (ctypes.c_uint8 * len(c["head_bits"]))(*c["head_bits"])
+    hb = (ctypes.c_uint8 * max(1, len(c["head_bits"])))(*c["head_bits"])
     cfg = pace.pace_config(c["batch"], c["heads"], c["d_k"], c["d_v"], c["period"], c["in_dtype"],
-                           ctypes.cast(hb, ctypes.POINTER(ctypes.c_uint8)), 0)
+                           ctypes.cast(hb, ctypes.POINTER(ctypes.c_uint8)), flags)
     out = ctypes.c_void_p()
     return pace.LIB.pace_state_alloc(ctypes.byref(cfg), init_kind, init, None, ctypes.byref(out))
 
@@ -59,6 +59,38 @@ def _alloc_status(init_kind=pace.PACE_INIT_ZERO, init=None, **kw):
 def test_alloc_rejects_bad_config(kw, status):
     assert _alloc_status(**kw) == status
     assert pace.pace_last_error() != ""
+
+
+def test_alloc_rejects_bad_flags():
+    assert _alloc_status(flags=2) == pace.PACE_EINVAL
+    many = pace.PACE_STATS_MAX_HEADS + 1
+    assert _alloc_status(flags=pace.PACE_STATS_ERR, heads=many, head_bits=[4] * many) == pace.PACE_EINVAL
+    assert "PACE_STATS_ERR" in pace.pace_last_error()
+
+
+def test_stats_struct_matches_header():
+    # the binding's pace_stats mirrors the C struct: same fields, same size
+    src = open(os.path.join(ROOT, "include", "pace.h")).read()
+    body = re.search(r"typedef struct pace_stats \{(.*?)\} pace_stats;", src, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    names = re.findall(r"\b([a-z0-9_]+)(?:\[[A-Z_]+\])?;", body)
+    assert names == [n for n, _ in pace.pace_stats._fields_]
+    # sizes and offsets as the C compiler lays the struct out
+    import subprocess
+    import tempfile
+    fields = [n for n, _ in pace.pace_stats._fields_]
+    prog = "#include <stddef.h>\n#include <stdio.h>\n#include \"pace.h\"\nint main(void) {\n"
+    prog += '    printf("%zu\\n", sizeof(pace_stats));\n'
+    prog += "".join(f'    printf("%zu\\n", offsetof(pace_stats, {n}));\n' for n in fields)
+    prog += "    return 0;\n}\n"
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "layout.c"), os.path.join(d, "layout")
+        open(src, "w").write(prog)
+        subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), src, "-o", exe], check=True)
+        got = [int(x) for x in subprocess.run([exe], check=True, capture_output=True,
+                                              text=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(pace.pace_stats)
+    assert got[1:] == [getattr(pace.pace_stats, n).offset for n in fields]
 
 
 def test_alloc_rejects_bad_init():

@@ -155,3 +155,62 @@ def test_decode_rejects_too_many_tokens():
     with pytest.raises(pace.PaceError) as e:
         st.decode(tok, out)
     assert e.value.status == pace.PACE_EINVAL
+
+
+def _head_sums(per_tile, w):
+    return per_tile.reshape(w.B, w.H).sum(axis=0)
+
+
+@pytest.mark.parametrize("name,kw,n_tok", [
+    ("err-k8", dict(B=3, H=5, n_int8=2, n_outliers=8), 8),          # 8-token fused kernel
+    ("err-k12", dict(B=3, H=5, n_int8=2, period=16), 12),            # 16-token fused kernel
+    ("err-f32", dict(B=2, H=3, n_int8=1, dtype=inputs.DT_F32), 8),   # per-column kernel
+    ("err-d64", dict(B=4, H=4, dk=64, dv=64, n_int8=1), 8),
+])
+def test_error_statistics(name, kw, n_tok):
+    # per-head sum (M - c s)^2 and sum M^2 of the state each encode quantized:
+    # the initial encode of the warm state, then the period-end encode
+    import torch
+    from linear_attn_decode_pace_amd import pace, runtime
+    w = inputs.ragged(name, 210, **kw)
+    seed = 3
+    say(f"[case] error statistics {name}")
+    bits = inputs.head_bits(w, seed)
+    bits_t = np.tile(bits, w.B)
+    n = w.B * w.H
+    M0 = runtime.warmup_state(w, seed)
+    st = runtime.State(w, bits, pace.PACE_INIT_F32, M0, flags=pace.PACE_STATS_ERR)
+    s = st.stats()
+    assert s["err_tracked"] == 1
+    M0g = M0.reshape(n, w.dk, w.dv).cpu().numpy().astype(np.float64)
+    e, r = quant.roundtrip_error(M0g, bits_t)
+    np.testing.assert_allclose(s["err_sq"], _head_sums(e, w), rtol=1e-4)
+    np.testing.assert_allclose(s["ref_sq"], _head_sums(r, w), rtol=1e-5)
+
+    codes, scales = st.read_codes()
+    codes = codes.reshape(n, w.dk, w.dv).cpu().numpy()
+    scales = scales.reshape(n, w.dv).cpu().numpy()
+    tok = inputs.tokens(w, seed, inputs.SEG_DECODE, 0, n_tok)
+    out = runtime.out_buffer(w, n_tok)
+    st.decode(runtime.DeviceTokens(tok), out)
+    torch.cuda.synchronize()
+    _, _, _, Mpre = opace.period(codes, scales, bits_t, *tok_tiles(tok, np.arange(n), w.H))
+    e, r = quant.roundtrip_error(Mpre, bits_t)
+    s = st.stats()
+    np.testing.assert_allclose(s["err_sq"], _head_sums(e, w), rtol=1e-3)
+    np.testing.assert_allclose(s["ref_sq"], _head_sums(r, w), rtol=1e-4)
+    st.free()
+
+
+def test_error_statistics_off_and_zero_init():
+    from linear_attn_decode_pace_amd import pace, runtime
+    say("[case] error statistics without the flag / zero init")
+    st, _ = _state(W, 0)
+    s = st.stats()
+    assert s["err_tracked"] == 0 and not any(s["err_sq"]) and not any(s["ref_sq"])
+    st.free()
+    z = runtime.State(W, inputs.head_bits(W, 0), pace.PACE_INIT_ZERO, flags=pace.PACE_STATS_ERR)
+    s = z.stats()
+    assert s["err_tracked"] == 1 and len(s["err_sq"]) == W.H
+    assert not any(s["err_sq"]) and not any(s["ref_sq"])
+    z.free()

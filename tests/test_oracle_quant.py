@@ -121,3 +121,30 @@ def test_storage_ratios_against_the_pages():
     ratio = (mix["heads4"] * int4 + mix["heads8"] * int8) / ((mix["heads4"] + mix["heads8"]) * int8)
     assert abs(ratio - r["printed"]) <= r["tolerance"]
     assert abs(ratio - 1344 / 2112) < 1e-12
+
+
+def test_roundtrip_error_hand_computed():
+    # 4 bits; column 0: absmax 7 -> s = 1, 3.5 ties to 4 (error 0.5);
+    # column 1: zero; column 2: absmax 7/8 -> s = 1/8, -1/16 ties to -0
+    M = np.array([[7.0, 0.0, -1 / 16],
+                  [3.5, 0.0, 7 / 8]])[None]
+    e, r = quant.roundtrip_error(M, 4)
+    assert e.tolist() == [0.25 + 1 / 256]
+    assert r.tolist() == [49 + 12.25 + 1 / 256 + 49 / 64]
+    # 8 bits: s = 1, 0.5 -> 0 and 1.5 -> 2 (both ties to even)
+    e8, r8 = quant.roundtrip_error(np.array([[127.0], [0.5], [1.5]])[None], 8)
+    assert e8.tolist() == [0.5] and r8.tolist() == [16129 + 0.25 + 2.25]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_roundtrip_error_bounds(bits):
+    rng = np.random.default_rng(5)
+    M = rng.standard_normal((6, 32, 16)) * rng.uniform(0.1, 10, (6, 1, 16))
+    e, r = quant.roundtrip_error(M, bits)
+    c, s = quant.encode(M, bits)
+    # every entry within half a step of its code: err <= d_k * sum_j s_j^2 / 4
+    assert np.all(e <= 32 * np.sum(s.astype(np.float64) ** 2, axis=-1) / 4 * (1 + 1e-12))
+    assert np.all(e > 0) and np.allclose(r, np.sum(M * M, axis=(1, 2)))
+    # a decoded state encodes without error
+    e2, _ = quant.roundtrip_error(quant.decode(c, s), bits)
+    assert np.all(e2 == 0)
