@@ -464,7 +464,7 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(MfmaArgs a) {
     // scalar-cache load, not a dependent vector load at the head of the tile)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int tib = wave / WPT, q = wave - tib * WPT;
-    const int w = blockIdx.x * TPB + tib;
+    const int w = xcd_block(blockIdx.x, a.xcd_run, a.xcd_full) * TPB + tib;
     if (w >= a.tiles) return;  // whole tiles only: every wave of a workgroup agrees when WPT > 1
     // sequence-major order: the heads of one sequence are neighbours, so
     // workgroups on a CU mix 4-bit and 8-bit tiles and read whole input rows
@@ -503,6 +503,7 @@ hipError_t launch_decode_mfma(const PoolView &p, const int32_t *heads8, const in
     a.tiles = p.B * p.H;
     if (n_tok > CH) return launch_decode_mfma16(a, s);
     const bool err = p.colerr != nullptr;
+    set_xcd_order(a, (p.dk == 128 ? Split<128>::WPT : Split<64>::WPT) == 1 ? 4 : 1);
     if (p.dk == 128) {
         constexpr int WPT = Split<128>::WPT, TPB = WPT == 1 ? 4 : 1;
         const dim3 grid((a.tiles + TPB - 1) / TPB), block(64 * WPT * TPB);

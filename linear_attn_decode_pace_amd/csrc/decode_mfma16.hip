@@ -353,7 +353,7 @@ __global__ void __launch_bounds__(64 * TPB16) decode_mfma16_kernel(MfmaArgs a) {
     __shared__ Tile16Lds tl[TPB16];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int w = blockIdx.x * TPB16 + wave;
+    const int w = xcd_block(blockIdx.x, a.xcd_run, a.xcd_full) * TPB16 + wave;
     if (w >= a.tiles) return;
     const int b = w / a.p.H, h = w - b * a.p.H;
     const int m = a.p.head_map[h];
@@ -365,7 +365,9 @@ __global__ void __launch_bounds__(64 * TPB16) decode_mfma16_kernel(MfmaArgs a) {
 
 }  // namespace
 
-hipError_t launch_decode_mfma16(const MfmaArgs &a, hipStream_t s) {
+hipError_t launch_decode_mfma16(const MfmaArgs &args, hipStream_t s) {
+    MfmaArgs a = args;
+    set_xcd_order(a, TPB16);
     dim3 grid((a.tiles + TPB16 - 1) / TPB16), block(64 * TPB16);
     const bool err = a.p.colerr != nullptr;
     if (a.p.dk == 128) {

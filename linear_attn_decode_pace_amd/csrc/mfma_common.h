@@ -15,9 +15,42 @@ struct MfmaArgs {
     const int32_t *heads8;  // slot -> head, 8-bit pool
     const int32_t *heads4;  // slot -> head, 4-bit pool
     int n_tok;
-    int tiles8;  // B * n8: work items below this are 8-bit tiles
-    int tiles;   // B * H
+    int tiles8;     // B * n8: work items below this are 8-bit tiles
+    int tiles;      // B * H
+    int xcd_run;    // K: workgroups per XCD run (see xcd_block)
+    int xcd_full;   // workgroups covered by whole groups of 8 K
 };
+
+// Workgroup order.  The dispatcher hands workgroup i to XCD i % 8, and each
+// XCD reaches memory through its own L2 and fabric port, so the launch runs at
+// the pace of the XCD with the most bytes.  Heads of different bit widths move
+// different bytes, so a plain order loads XCDs unevenly whenever the head mix
+// repeats with the XCD count (e.g. four-tile workgroups over 16 heads: XCDs 3
+// and 7 always get heads 12..15).  Instead XCD x takes a run of K consecutive
+// workgroups out of every group of 8 K, with K chosen so that K workgroups
+// cover whole sequences: every XCD then carries the same head mix, and all
+// XCDs still work inside one window of the pools.  Workgroups past the last
+// whole group keep their place.
+inline int xcd_run_for(int heads, int tiles_per_wg) {
+    int a = heads, b = tiles_per_wg;
+    while (b) {
+        const int t = a % b;
+        a = b;
+        b = t;
+    }
+    return heads / a;  // lcm(heads, tiles_per_wg) / tiles_per_wg
+}
+inline void set_xcd_order(MfmaArgs &a, int tiles_per_wg) {
+    const int K = xcd_run_for(a.p.H, tiles_per_wg);
+    const long long whole_wgs = a.tiles / tiles_per_wg;
+    a.xcd_run = K;
+    a.xcd_full = (int)(whole_wgs / (8ll * K) * (8ll * K));
+}
+__device__ inline int xcd_block(int i, int K, int full) {
+    if (i >= full) return i;
+    const int G = i / (8 * K), p = i - G * 8 * K;
+    return G * 8 * K + (p & 7) * K + (p >> 3);
+}
 
 // the 16-token chunk kernel (decode_mfma16.hip), for 9..16 tokens per call
 hipError_t launch_decode_mfma16(const MfmaArgs &a, hipStream_t s);
