@@ -1,0 +1,88 @@
+"""Buffered per-step decode with periodic rounding (float64 reference).
+
+Test infrastructure only, like the rest of ``oracle/``.
+
+The serving form of periodic rounding: each decode step brings one token per
+state; the token goes into a small buffer of the tokens since the last encode,
+and every k-th token the state is updated in high precision and re-encoded
+('PACE: four-bit recurrent state by rounding less often', flowchart 'Fewer
+roundings, less compounded error': new tokens -> small buffer -> every k
+tokens a chunked high-precision update -> per-column encode -> stored state;
+TL;DR point (1)).  The output of a step is read from the high-precision state
+the period holds after that token: the stored state decoded, with the buffered
+tokens and the new one applied in order (the same reading as ``pace.py``).
+
+Readings where the pages are silent:
+
+* The buffer holds at most k - 1 tokens: the k-th token of a period triggers
+  the encode and leaves the buffer empty.
+* Each state has its own buffer fill, so states can sit at different phases
+  of their periods (a state skipped by a step keeps its buffer).
+* ``flush`` ends every partial period early: buffered tokens are applied and
+  the state is encoded, as a shorter final period would be.
+
+This is written as its own loop over the buffer, separately from
+``pace.period`` (which applies a whole period in one call); the tests pin the
+two against each other.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import gdn, quant
+
+
+class Buffered:
+    """n states, each with its stored codes and scales and its own buffer."""
+
+    def __init__(self, codes, scales, bits, period: int):
+        if period < 1:
+            raise ValueError("period must be >= 1")
+        self.codes = np.array(codes, dtype=np.int16)
+        self.scales = np.array(scales, dtype=np.float32)
+        self.bits = np.broadcast_to(np.asarray(bits), self.codes.shape[:1]).copy()
+        self.period = period
+        n = self.codes.shape[0]
+        self.buf = [[] for _ in range(n)]  # per state: list of (k, v, alpha, beta)
+        self.last_pre = [None] * n           # high-precision state of each state's last encode
+
+    @property
+    def fill(self) -> np.ndarray:
+        return np.array([len(b) for b in self.buf])
+
+    def _state(self, i: int) -> np.ndarray:
+        """Stored state i decoded, with its buffered tokens applied in order."""
+        M = quant.decode(self.codes[i:i + 1], self.scales[i:i + 1])
+        for k, v, a, b in self.buf[i]:
+            M = gdn.step(M, np.zeros_like(k)[None], k[None], v[None], np.array([a]), np.array([b]))[0]
+        return M
+
+    def _encode(self, i: int, M: np.ndarray) -> None:
+        c, s = quant.encode(M, self.bits[i:i + 1])
+        self.codes[i], self.scales[i] = c[0], s[0]
+        self.last_pre[i] = M[0]
+        self.buf[i] = []
+
+    def step(self, q, k, v, alpha, beta, active=None) -> np.ndarray:
+        """One token per state: q, k [n, d_k], v [n, d_v], alpha, beta [n]
+        (float64 values); active [n] bool or None (all).  Returns the outputs
+        [n, d_v] (NaN for inactive states)."""
+        n = self.codes.shape[0]
+        act = np.ones(n, dtype=bool) if active is None else np.asarray(active, dtype=bool)
+        out = np.full((n, v.shape[1]), np.nan)
+        for i in np.nonzero(act)[0]:
+            M = self._state(i)
+            M, o = gdn.step(M, q[i][None], k[i][None], v[i][None], np.array([alpha[i]]),
+                            np.array([beta[i]]))
+            out[i] = o[0]
+            if len(self.buf[i]) + 1 == self.period:
+                self._encode(i, M)
+            else:
+                self.buf[i].append((np.array(k[i]), np.array(v[i]), float(alpha[i]), float(beta[i])))
+        return out
+
+    def flush(self) -> None:
+        """Apply and encode every non-empty buffer (a shorter final period)."""
+        for i in range(self.codes.shape[0]):
+            if self.buf[i]:
+                self._encode(i, self._state(i))
