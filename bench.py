@@ -59,6 +59,21 @@ def algorithmic_bytes(w: inputs.Workload, n_tok: int, head_bits) -> int:
     return w.B * (2 * state + n_tok * per_seq_tok)
 
 
+def algorithmic_bytes_step(w: inputs.Workload, head_bits) -> float:
+    """Mean bytes of one per-step decode call over a period of k = w.period
+    calls: the stored state is read by every call and written by the last;
+    call f reads the f buffered tokens (k_t, v_t, alpha_t, beta_t) and every
+    call but the last appends its own; each call reads its q/k/v/alpha/beta and
+    writes its float32 outputs."""
+    e_in = 2 if w.dtype == inputs.DT_BF16 else 4
+    k = w.period
+    state = sum(w.dk * w.dv * int(b) // 8 + 4 * w.dv for b in head_bits)
+    buf_tok = w.H * ((w.dk + w.dv) * e_in + 8)
+    io_tok = w.H * ((w.dk * 2 + w.dv) * e_in + 8 + 4 * w.dv)
+    per_period = (k + 1) * state + (k * (k - 1) // 2 + (k - 1)) * buf_tok + k * io_tok
+    return w.B * per_period / k
+
+
 def kernel_sha() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -134,6 +149,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=inputs.HEADLINE.name, choices=sorted(inputs.WORKLOADS))
+    ap.add_argument("--mode", default="period", choices=("period", "step"),
+                    help="period: one call per period of k tokens; step: one call per token "
+                         "(PACE_STEP_BUFFER handle), every sequence active")
     ap.add_argument("--period", type=int, default=None, help="override the workload's period")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--ring", type=int, default=4, help="distinct input periods resident in HBM")
@@ -176,10 +194,16 @@ def main() -> int:
 
     M0 = torch.zeros((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
     runtime.prefill(w, runtime.DeviceTokens(warm_tok), M0)
-    st = runtime.State(w, head_bits, pace.PACE_INIT_F32, M0)
+    step_mode = args.mode == "step"
+    st = runtime.State(w, head_bits, pace.PACE_INIT_F32, M0,
+                       flags=pace.PACE_STEP_BUFFER if step_mode else 0)
     del M0
     ring = [runtime.DeviceTokens(tk) for tk in ring_tok]
-    out = runtime.out_buffer(w, C)
+    if step_mode:   # one token per call: the ring's periods cut into tokens
+        ring = [r.slice(t, t + 1) for r in ring for t in range(C)]
+        ring_n = len(ring)
+    out = runtime.out_buffer(w, 1 if step_mode else C)
+    call = st.step if step_mode else st.decode
     torch.cuda.synchronize()
     log(f"state and {ring_n} input periods resident ({sum(r.nbytes for r in ring) / 1e9:.2f} GB)")
 
@@ -192,7 +216,7 @@ def main() -> int:
         del src, dst
 
     for i in range(args.warmup):
-        st.decode(ring[i % ring_n], out)
+        call(ring[i % ring_n], out)
     torch.cuda.synchronize()
 
     K = args.steps
@@ -204,7 +228,7 @@ def main() -> int:
     start.record()
     for i in range(K):
         ev[i][0].record()
-        st.decode(ring[(args.warmup + i) % ring_n], out)
+        call(ring[(args.warmup + i) % ring_n], out)
         ev[i][1].record()
     end.record()
     torch.cuda.synchronize()
@@ -213,10 +237,11 @@ def main() -> int:
     launch_ms = sum(a.elapsed_time(b) for a, b in ev) / K
     log(f"timed {K} steps: {total_ms:.3f} ms on the device, {t_wall * 1e3:.1f} ms wall")
 
-    nbytes = algorithmic_bytes(w, C, head_bits)
+    nbytes = algorithmic_bytes_step(w, head_bits) if step_mode else algorithmic_bytes(w, C, head_bits)
     achieved = nbytes / (launch_ms * 1e-3) / 1e9
     sha = kernel_sha()
-    value = w.B * C * K / (total_ms * 1e-3)
+    tokens_per_call = 1 if step_mode else C
+    value = w.B * tokens_per_call * K / (total_ms * 1e-3)
     res = {
         "metric": "decode token-steps/s per GDN layer (seqs x tokens) + achieved HBM GB/s vs peak",
         "value": value,
@@ -233,11 +258,12 @@ def main() -> int:
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "d_k": w.dk, "d_v": w.dv,
                    "period": C, "heads_int8": int((head_bits == 8).sum()),
                    "inputs": w.dtype, "outlier_channels": w.n_outliers,
-                   "decode_steps": K * C, "input_ring_periods": ring_n,
+                   "mode": args.mode, "decode_steps": K * tokens_per_call,
+                   "input_ring_calls": ring_n,
                    "start_state": f"{warm[2]} {'prompt' if w.prompt else 'warm-up'} tokens from zero"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": traffic_from_profile(w.name, sha, nbytes),
+                     "traffic": None if step_mode else traffic_from_profile(w.name, sha, nbytes),
                      "algorithmic_bytes_per_launch": nbytes, "launch_ms": launch_ms,
                      "kernel_sha": sha},
     }

@@ -94,6 +94,18 @@ extern "C" {
  * encode.  Requires heads <= PACE_STATS_MAX_HEADS. */
 #define PACE_STATS_ERR 0x1u
 #define PACE_STATS_MAX_HEADS 256
+/* PACE_STEP_BUFFER: the handle decodes one token per call (pace_decode_step)
+ * instead of one period per call.  Every (sequence, head) state gets a buffer
+ * of up to period - 1 tokens (its k_t, v_t in in_dtype and alpha_t, beta_t in
+ * float32) and a fill count; the token that completes a period applies the
+ * buffer and itself to the decoded state and re-encodes it, every other token
+ * is appended to the buffer.  This is the serving form of periodic rounding:
+ * 'PACE: four-bit recurrent state by rounding less often', flowchart (new
+ * tokens -> small buffer -> every k tokens a high-precision update -> encode).
+ * Buffer bytes: B * H * (period - 1) * ((d_k + d_v) * elem + 8), plus
+ * B * H * 4 for the fill counts (pace_stats.bytes_step_buffer).  Such a
+ * handle rejects pace_decode_period. */
+#define PACE_STEP_BUFFER 0x2u
 
 typedef struct pace_state pace_state; /* opaque; owns the device pools */
 
@@ -105,7 +117,7 @@ typedef struct pace_config {
     int32_t period;           /* k: most tokens one pace_decode_period call may apply, 1..64 */
     int32_t in_dtype;         /* PACE_DTYPE_F32 or PACE_DTYPE_BF16: element type of q, k, v */
     const uint8_t *head_bits; /* host [H]: bit width of each head, 4 or 8; copied at alloc */
-    uint32_t flags;           /* 0 or PACE_STATS_ERR */
+    uint32_t flags;           /* 0 or an OR of PACE_STATS_ERR, PACE_STEP_BUFFER */
 } pace_config;
 
 typedef struct pace_stats {
@@ -118,8 +130,11 @@ typedef struct pace_stats {
     int32_t heads4;            /* heads in the 4-bit pool */
     int32_t heads8;            /* heads in the 8-bit pool */
     uint64_t periods;          /* pace_decode_period calls applied since alloc */
-    uint64_t tokens;           /* tokens applied since alloc */
+    uint64_t tokens;           /* tokens applied since alloc: n_tok per pace_decode_period,
+                                  1 per pace_decode_step (whatever its active mask) */
     uint64_t zero_columns;     /* stored columns whose scale is 0 */
+    uint64_t bytes_step_buffer; /* device bytes of the per-step token buffer and fill counts
+                                  (0 without PACE_STEP_BUFFER) */
     /* with PACE_STATS_ERR (err_tracked = 1), per head h < heads, over every
      * sequence b and entry (i, j) of the state M of the last encode:
      * err_sq[h] = sum (M_ij - c_ij s_j)^2 and ref_sq[h] = sum M_ij^2, so that
@@ -175,7 +190,8 @@ int pace_raw_bytes(const pace_state *st, uint64_t *out);
  *   alpha, beta: device float32 [n_tok, B, H], 4-byte aligned; alpha is the
  *          gate (0 < alpha <= 1 expected), beta the write strength.
  *   out:   device float32 [n_tok, B, H, d_v], 16-byte aligned; may not alias inputs.
- * Errors: EINVAL (null handle or pointer, n_tok out of range, misalignment),
+ * Errors: EINVAL (null handle or pointer, n_tok out of range, misalignment,
+ *         a handle allocated with PACE_STEP_BUFFER),
  *         EDEVICE (launch failure or an earlier asynchronous fault).
  */
 int pace_decode_period(pace_state *st, int32_t n_tok, const void *q, const void *k,
@@ -183,11 +199,46 @@ int pace_decode_period(pace_state *st, int32_t n_tok, const void *q, const void 
                        void *stream);
 
 /*
+ * One decode step of a PACE_STEP_BUFFER handle: one token for every active
+ * sequence.  For each (sequence, head) state with f tokens buffered, the
+ * output is read from the stored state decoded with the f buffered tokens and
+ * then this token applied in order, in float32 (the high-precision state the
+ * period holds after this token).  If f + 1 = period the state is re-encoded
+ * and its buffer emptied; otherwise the token is appended to the buffer and
+ * the stored codes are left unchanged (read, not written).  Outputs equal
+ * those of pace_decode_period fed the same tokens a period at a time.
+ *   q, k:   device [B, H, d_k], in_dtype, 16-byte aligned.
+ *   v:      device [B, H, d_v], in_dtype, 16-byte aligned.
+ *   alpha, beta: device float32 [B, H].
+ *   active: device uint8 [B] (0 = this sequence takes no token this step:
+ *           its state, buffer and output rows are left untouched), or NULL
+ *           for all sequences.  Sequences can so sit at different phases.
+ *   out:    device float32 [B, H, d_v], 16-byte aligned.
+ * Errors: EINVAL (null or misaligned pointer, a handle without
+ *         PACE_STEP_BUFFER), EDEVICE.
+ */
+int pace_decode_step(pace_state *st, const void *q, const void *k, const void *v,
+                     const float *alpha, const float *beta, const uint8_t *active,
+                     float *out, void *stream);
+
+/*
+ * End every partial period of a PACE_STEP_BUFFER handle: each state with a
+ * non-empty buffer has its buffered tokens applied and is re-encoded (as a
+ * shorter final period); its buffer is emptied.  Call before
+ * pace_read_state or a raw checkpoint when the buffered tokens must be part
+ * of the stored state.  No outputs.
+ * Errors: EINVAL (a handle without PACE_STEP_BUFFER), EDEVICE.
+ */
+int pace_flush_steps(pace_state *st, void *stream);
+
+/*
  * Read the stored state (see PACE_READ_*).  dst and scales_dst are device
  * pointers sized as documented above.  The raw image is the library's own
  * device layout (4-bit pool, then 8-bit pool, then scales) and is meant only
  * to be handed back to pace_state_alloc(PACE_INIT_RAW) for a handle of the
- * same configuration (checkpoint / resume).
+ * same configuration (checkpoint / resume).  For a PACE_STEP_BUFFER handle
+ * this is the state as of each sequence's last encode (buffered tokens are
+ * not included; see pace_flush_steps).
  * Errors: EINVAL, EDEVICE.
  */
 int pace_read_state(const pace_state *st, int what, void *dst, float *scales_dst,

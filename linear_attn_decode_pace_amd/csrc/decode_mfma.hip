@@ -91,7 +91,7 @@ __device__ inline void tile_sync() {
         __syncthreads();
 }
 
-template <int DK, int BITS, int WPT, bool ERR>
+template <int DK, int BITS, int WPT, bool ERR, bool STEP>
 __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int b, int h,
                              int slot, int lane, int q, bool trace) {
 #define TRACE(slot_, v_)                                        \
@@ -105,10 +105,18 @@ __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int
     static_assert(CPW % 2 == 0, "outputs are flushed every two column blocks");
     constexpr float QMAX = BITS == 4 ? 7.f : 127.f;
     const int g = lane >> 4, n = lane & 15;
-    const int n_tok = a.n_tok;
     const uint32_t tok_stride = (uint32_t)a.p.B * (uint32_t)a.p.H;  // (sequence, head) rows per token
     const size_t tile_row = (size_t)b * a.p.H + h;
     const int cb0 = q * CPW;
+    // STEP (a PACE_STEP_BUFFER step): the chunk is the state's f buffered
+    // tokens plus the step's own token f; only token f's output is written,
+    // and the state is updated and re-encoded only when token f ends a period
+    static_assert(!STEP || WPT == 1, "steps run one wave per tile");
+    const int f = STEP ? __builtin_amdgcn_readfirstlane(a.step.fill[tile_row]) : 0;
+    const int n_tok = STEP ? f + 1 : a.n_tok;
+    const bool pend = !STEP || n_tok == a.step.period;
+    uint16_t *sbuf = STEP ? (uint16_t *)a.step.kv + tile_row * a.step.slots * (2 * DK) : nullptr;
+    float *sab = STEP ? a.step.ab + tile_row * a.step.slots * 2 : nullptr;
 
     uint8_t *codes = BITS == 4
         ? a.p.codes4 + ((size_t)b * a.p.n4 + slot) * tile_code_bytes(DK, DK, 4)
@@ -139,17 +147,29 @@ __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int
             const int row = c / CPR, col = (c % CPR) * 8;
             const int t = row & 7, which = row >> 3;
             val[it] = u32x4{0u, 0u, 0u, 0u};
-            if (row < 24 && t < n_tok)
+            if constexpr (STEP) {
+                // token f from the step's inputs [B, H, d]; earlier tokens (k, v
+                // only: their outputs are not needed) from the buffer
+                if (row < 24 && t == f)
+                    val[it] = __builtin_nontemporal_load(at((const u32x4 *)srcs[which], (uint32_t)col * 2u));
+                else if (row < 24 && t < f && which != 1)
+                    val[it] = *at((const u32x4 *)sbuf,
+                                  (uint32_t)(t * 2 * DK + (which == 2 ? DK : 0) + col) * 2u);
+            } else if (row < 24 && t < n_tok) {
                 val[it] = __builtin_nontemporal_load(
                     at((const u32x4 *)srcs[which], (uint32_t)(t * tok_stride * DK + col) * 2u));
+            }
         }
         float ab = 0.f;
         if (q == 0 && lane < 16) {
             const int t = lane & 7;
             const bool is_beta = lane >= 8;
             ab = is_beta ? 0.f : 1.f;
-            if (t < n_tok)
-                ab = *at(is_beta ? a.beta + tile_row : a.alpha + tile_row, (uint32_t)t * tok_stride * 4u);
+            if (STEP && t < f)
+                ab = sab[2 * t + is_beta];
+            else if (t < n_tok)
+                ab = *at(is_beta ? a.beta + tile_row : a.alpha + tile_row,
+                         STEP ? 0u : (uint32_t)t * tok_stride * 4u);
         }
 #pragma unroll
         for (int it = 0; it < NL; ++it) {
@@ -159,6 +179,9 @@ __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int
             if (row < 24) {
                 uint16_t *dst = which < 2 ? &L.kq[which * 8 + t][col] : &L.v[t][col];
                 *(u32x4 *)dst = val[it];
+                // a token that does not end its period joins the buffer (slot f)
+                if (STEP && !pend && t == f && which != 1)
+                    *at((u32x4 *)sbuf, (uint32_t)(t * 2 * DK + (which == 2 ? DK : 0) + col) * 2u) = val[it];
             }
         }
         if (q == 0 && lane < 16) {
@@ -166,6 +189,7 @@ __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int
                 L.beta[lane & 7] = ab;
             else
                 L.alpha[lane & 7] = ab;
+            if (STEP && !pend && (lane & 7) == f) sab[2 * f + (lane >> 3)] = ab;
         }
     }
     tile_sync<WPT>();
@@ -389,9 +413,12 @@ __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int
             wave_sync();
             const int t = lane >> 3, c4 = (lane & 7) * 4;
             const f32x4 x = *(const f32x4 *)&WO_lds.o[t][c4];
-            if (t < n_tok)
+            if (STEP ? t == f : t < n_tok)
                 __builtin_nontemporal_store(
-                    x, at((f32x4 *)obase, (uint32_t)t * o_tok + (uint32_t)(16 * cb - 16 + c4) * 4u));
+                    x, at((f32x4 *)obase, (STEP ? 0u : (uint32_t)t * o_tok) + (uint32_t)(16 * cb - 16 + c4) * 4u));
+        }
+        if constexpr (STEP) {
+            if (!pend) continue;  // mid-period step: the stored state is only read
         }
 
         // W split into three bf16 parts (hi + mid + lo)
@@ -450,10 +477,13 @@ __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int
         if (g == 0) scl[j] = s_new;
         if constexpr (ERR) column_error<NRT>(acc, y, sig, s_new, a.p.colerr + (tile_row * DK + j) * 2, g);
     }
+    if constexpr (STEP) {
+        if (lane == 0) a.step.fill[tile_row] = pend ? 0 : n_tok;
+    }
 #undef TRACE
 }
 
-template <int DK, bool ERR>
+template <int DK, bool ERR, bool STEP>
 __global__ void __launch_bounds__(256) decode_mfma_kernel(MfmaArgs a) {
     constexpr int WPT = Split<DK>::WPT;
     constexpr int TPB = WPT == 1 ? 4 : 1;  // tiles per workgroup
@@ -469,11 +499,12 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(MfmaArgs a) {
     // sequence-major order: the heads of one sequence are neighbours, so
     // workgroups on a CU mix 4-bit and 8-bit tiles and read whole input rows
     const int b = w / a.p.H, h = w - b * a.p.H;
+    if (STEP && a.step.active && !a.step.active[b]) return;  // this sequence takes no token
     const int m = a.p.head_map[h];  // slot | bits << 16 (scalar load)
     if ((m >> 16) == 8)
-        process_tile<DK, 8, WPT, ERR>(a, tl[tib], wo[wave], b, h, m & 0xffff, lane, q, w == 0 && q == 0);
+        process_tile<DK, 8, WPT, ERR, STEP>(a, tl[tib], wo[wave], b, h, m & 0xffff, lane, q, w == 0 && q == 0);
     else
-        process_tile<DK, 4, WPT, ERR>(a, tl[tib], wo[wave], b, h, m & 0xffff, lane, q, w == 0 && q == 0);
+        process_tile<DK, 4, WPT, ERR, STEP>(a, tl[tib], wo[wave], b, h, m & 0xffff, lane, q, w == 0 && q == 0);
 }
 
 }  // namespace
@@ -485,10 +516,12 @@ bool mfma_supported(int dk, int dv, int n_tok, int in_bf16, long long rows_per_t
            (long long)2 * CH * rows_per_token * dk * 4 < (1ll << 31);
 }
 
-hipError_t launch_decode_mfma(const PoolView &p, const int32_t *heads8, const int32_t *heads4,
-                              int n_tok, const void *q, const void *k, const void *v,
-                              const float *alpha, const float *beta, float *out, hipStream_t s) {
-    MfmaArgs a;
+namespace {
+
+MfmaArgs make_args(const PoolView &p, const int32_t *heads8, const int32_t *heads4, int n_tok,
+                   const void *q, const void *k, const void *v, const float *alpha,
+                   const float *beta, float *out) {
+    MfmaArgs a = {};
     a.p = p;
     a.q = (const uint16_t *)q;
     a.k = (const uint16_t *)k;
@@ -501,25 +534,52 @@ hipError_t launch_decode_mfma(const PoolView &p, const int32_t *heads8, const in
     a.n_tok = n_tok;
     a.tiles8 = p.B * p.n8;
     a.tiles = p.B * p.H;
-    if (n_tok > CH) return launch_decode_mfma16(a, s);
+    return a;
+}
+
+template <bool STEP>
+hipError_t launch(MfmaArgs &a, hipStream_t s) {
+    const PoolView &p = a.p;
     const bool err = p.colerr != nullptr;
     set_xcd_order(a, (p.dk == 128 ? Split<128>::WPT : Split<64>::WPT) == 1 ? 4 : 1);
     if (p.dk == 128) {
         constexpr int WPT = Split<128>::WPT, TPB = WPT == 1 ? 4 : 1;
         const dim3 grid((a.tiles + TPB - 1) / TPB), block(64 * WPT * TPB);
         if (err)
-            hipLaunchKernelGGL((decode_mfma_kernel<128, true>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((decode_mfma_kernel<128, true, STEP>), grid, block, 0, s, a);
         else
-            hipLaunchKernelGGL((decode_mfma_kernel<128, false>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((decode_mfma_kernel<128, false, STEP>), grid, block, 0, s, a);
     } else {
         constexpr int WPT = Split<64>::WPT, TPB = WPT == 1 ? 4 : 1;
         const dim3 grid((a.tiles + TPB - 1) / TPB), block(64 * WPT * TPB);
         if (err)
-            hipLaunchKernelGGL((decode_mfma_kernel<64, true>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((decode_mfma_kernel<64, true, STEP>), grid, block, 0, s, a);
         else
-            hipLaunchKernelGGL((decode_mfma_kernel<64, false>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((decode_mfma_kernel<64, false, STEP>), grid, block, 0, s, a);
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const PoolView &p, const int32_t *heads8, const int32_t *heads4,
+                              int n_tok, const void *q, const void *k, const void *v,
+                              const float *alpha, const float *beta, float *out, hipStream_t s) {
+    MfmaArgs a = make_args(p, heads8, heads4, n_tok, q, k, v, alpha, beta, out);
+    if (n_tok > CH) return launch_decode_mfma16(a, s);
+    return launch<false>(a, s);
+}
+
+bool mfma_step_supported(int dk, int dv, int period, int in_bf16, long long rows_per_token) {
+    return period <= CH && mfma_supported(dk, dv, period, in_bf16, rows_per_token);
+}
+
+hipError_t launch_step_mfma(const PoolView &p, const StepView &sv, const int32_t *heads8,
+                            const int32_t *heads4, const void *q, const void *k, const void *v,
+                            const float *alpha, const float *beta, float *out, hipStream_t s) {
+    MfmaArgs a = make_args(p, heads8, heads4, 0, q, k, v, alpha, beta, out);
+    a.step = sv;
+    return launch<true>(a, s);
 }
 
 }  // namespace pace

@@ -12,6 +12,7 @@
 // byte it reads or writes belongs to its column only (see pace_layout.h) and
 // decode can update the pool in place without synchronisation between threads.
 #include "pace_layout.h"
+#include "pace_step.h"
 
 namespace pace {
 namespace {
@@ -201,6 +202,100 @@ __global__ void count_zero_kernel(const float *scales, size_t n, unsigned long l
     if ((threadIdx.x & 63) == 0 && mine) atomicAdd(counter, (unsigned long long)mine);
 }
 
+// ---- per-step decode (PACE_STEP_BUFFER) ----------------------------------
+
+__device__ inline void copy_in(void *dst, size_t di, const void *src, size_t si, int bf16) {
+    if (bf16)
+        ((uint16_t *)dst)[di] = ((const uint16_t *)src)[si];
+    else
+        ((float *)dst)[di] = ((const float *)src)[si];
+}
+
+// Apply buffered tokens 0..f-1 of state `tile` and then, if cur_k != NULL, the
+// step's own token (whose output is written); column j per thread, as
+// apply_tokens.
+template <int DK>
+__device__ inline void apply_buffered(float M[DK], float *sk, float *sq, const StepView &sv,
+                                      int tile, int dv, int j, int f, const void *q,
+                                      const void *cur_k, const void *v, const float *alpha,
+                                      const float *beta, float *out, int bf16) {
+    const size_t row = (size_t)DK + dv;  // elements per buffered token
+    const int last = cur_k ? f : f - 1;
+    for (int t = 0; t <= last; ++t) {
+        const bool cur = t == f;
+        const size_t slot = (size_t)tile * sv.slots + t;
+        __syncthreads();
+        for (int i = threadIdx.x; i < DK; i += blockDim.x) {
+            sk[i] = cur ? ld_in(cur_k, (size_t)tile * DK + i, bf16) : ld_in(sv.kv, slot * row + i, bf16);
+            if (cur) sq[i] = ld_in(q, (size_t)tile * DK + i, bf16);
+        }
+        __syncthreads();
+        const float a = cur ? alpha[tile] : sv.ab[2 * slot];
+        const float bt = cur ? beta[tile] : sv.ab[2 * slot + 1];
+        const float vj = cur ? ld_in(v, (size_t)tile * dv + j, bf16) : ld_in(sv.kv, slot * row + DK + j, bf16);
+        float d = 0.f;
+#pragma unroll
+        for (int i = 0; i < DK; ++i) d = fmaf(sk[i], M[i], d);
+        float o = 0.f;
+#pragma unroll
+        for (int i = 0; i < DK; ++i) {
+            float bk = bt * sk[i];
+            M[i] = a * (M[i] - bk * d) + bk * vj;
+            o = fmaf(sq[i], M[i], o);
+        }
+        if (cur) out[(size_t)tile * dv + j] = o;
+    }
+}
+
+template <int DK>
+__global__ void step_v0_kernel(PoolView p, StepView sv, const void *q, const void *k,
+                               const void *v, const float *alpha, const float *beta, float *out,
+                               int bf16) {
+    __shared__ float sk[DK], sq[DK];
+    const int tile = blockIdx.x, b = tile / p.H, h = tile % p.H, j = threadIdx.x;
+    if (sv.active && !sv.active[b]) return;
+    const int f = sv.fill[tile];
+    int bits;
+    uint8_t *codes = tile_codes(p, b, h, &bits);
+    float *sc = p.scales + (size_t)tile * p.dv;
+    float M[DK];
+    load_column<DK>(codes, bits, j, sc[j], M);
+    apply_buffered<DK>(M, sk, sq, sv, tile, p.dv, j, f, q, k, v, alpha, beta, out, bf16);
+    // every thread has read fill[tile] before the first barrier inside apply_buffered
+    if (f + 1 == sv.period) {
+        sc[j] = store_column<DK>(codes, bits, j, M,
+                                 p.colerr ? p.colerr + ((size_t)tile * p.dv + j) * 2 : nullptr);
+        if (j == 0) sv.fill[tile] = 0;
+    } else {
+        const size_t slot = (size_t)tile * sv.slots + f, row = (size_t)DK + p.dv;
+        for (int i = j; i < DK; i += blockDim.x) copy_in(sv.kv, slot * row + i, k, (size_t)tile * DK + i, bf16);
+        copy_in(sv.kv, slot * row + DK + j, v, (size_t)tile * p.dv + j, bf16);
+        if (j == 0) {
+            sv.ab[2 * slot] = alpha[tile];
+            sv.ab[2 * slot + 1] = beta[tile];
+            sv.fill[tile] = f + 1;
+        }
+    }
+}
+
+template <int DK>
+__global__ void flush_v0_kernel(PoolView p, StepView sv, int bf16) {
+    __shared__ float sk[DK], sq[DK];
+    const int tile = blockIdx.x, b = tile / p.H, h = tile % p.H, j = threadIdx.x;
+    const int f = sv.fill[tile];
+    if (f == 0) return;
+    int bits;
+    uint8_t *codes = tile_codes(p, b, h, &bits);
+    float *sc = p.scales + (size_t)tile * p.dv;
+    float M[DK];
+    load_column<DK>(codes, bits, j, sc[j], M);
+    apply_buffered<DK>(M, sk, sq, sv, tile, p.dv, j, f, nullptr, nullptr, nullptr, nullptr,
+                       nullptr, nullptr, bf16);
+    sc[j] = store_column<DK>(codes, bits, j, M,
+                             p.colerr ? p.colerr + ((size_t)tile * p.dv + j) * 2 : nullptr);
+    if (j == 0) sv.fill[tile] = 0;
+}
+
 // one block per head; float64 sums over sequences and columns
 __global__ void reduce_colerr_kernel(const float *colerr, int B, int H, int dv, double *out) {
     __shared__ double part[2][4];
@@ -287,6 +382,28 @@ hipError_t launch_count_zero_scales(const PoolView &p, unsigned long long *count
 hipError_t launch_reduce_colerr(const PoolView &p, double *out, hipStream_t s) {
     hipLaunchKernelGGL(reduce_colerr_kernel, dim3(p.H), dim3(256), 0, s, p.colerr, p.B, p.H, p.dv,
                        out);
+    return hipGetLastError();
+}
+
+hipError_t launch_step_v0(const PoolView &p, const StepView &sv, const void *q, const void *k,
+                          const void *v, const float *alpha, const float *beta, float *out,
+                          int in_bf16, hipStream_t s) {
+    dim3 grid(p.B * p.H), block(p.dv);
+    if (p.dk == 128)
+        hipLaunchKernelGGL(step_v0_kernel<128>, grid, block, 0, s, p, sv, q, k, v, alpha, beta,
+                           out, in_bf16);
+    else
+        hipLaunchKernelGGL(step_v0_kernel<64>, grid, block, 0, s, p, sv, q, k, v, alpha, beta,
+                           out, in_bf16);
+    return hipGetLastError();
+}
+
+hipError_t launch_flush_v0(const PoolView &p, const StepView &sv, int in_bf16, hipStream_t s) {
+    dim3 grid(p.B * p.H), block(p.dv);
+    if (p.dk == 128)
+        hipLaunchKernelGGL(flush_v0_kernel<128>, grid, block, 0, s, p, sv, in_bf16);
+    else
+        hipLaunchKernelGGL(flush_v0_kernel<64>, grid, block, 0, s, p, sv, in_bf16);
     return hipGetLastError();
 }
 

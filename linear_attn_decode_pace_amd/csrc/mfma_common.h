@@ -4,6 +4,7 @@
 #pragma once
 
 #include "pace_mfma.h"
+#include "pace_step.h"
 
 namespace pace {
 
@@ -19,6 +20,7 @@ struct MfmaArgs {
     int tiles;      // B * H
     int xcd_run;    // K: workgroups per XCD run (see xcd_block)
     int xcd_full;   // workgroups covered by whole groups of 8 K
+    StepView step;  // per-step decode only (PACE_STEP_BUFFER)
 };
 
 // Workgroup order.  The dispatcher hands workgroup i to XCD i % 8, and each

@@ -13,6 +13,7 @@
 #include "../../include/pace.h"
 #include "pace_layout.h"
 #include "pace_mfma.h"
+#include "pace_step.h"
 
 #define PACE_API extern "C" __attribute__((visibility("default")))
 
@@ -29,7 +30,10 @@ struct pace_state {
     unsigned long long *d_counter = nullptr;
     float *colerr = nullptr;  // PACE_STATS_ERR: [B, H, d_v, 2]
     double *d_err = nullptr;  // PACE_STATS_ERR: [H, 2] per-head sums
-    size_t bytes4 = 0, bytes8 = 0, bytes_scales = 0;
+    void *step_kv = nullptr;       // PACE_STEP_BUFFER: [B * H][period - 1][d_k + d_v] in_dtype
+    float *step_ab = nullptr;      // PACE_STEP_BUFFER: [B * H][period - 1][2]
+    int32_t *step_fill = nullptr;  // PACE_STEP_BUFFER: [B * H]
+    size_t bytes4 = 0, bytes8 = 0, bytes_scales = 0, bytes_step = 0;
     uint64_t periods = 0, tokens = 0;
 
     pace::PoolView view() const {
@@ -47,6 +51,17 @@ struct pace_state {
         p.n8 = n8;
         return p;
     }
+    pace::StepView step_view(const uint8_t *active) const {
+        pace::StepView v;
+        v.kv = step_kv;
+        v.ab = step_ab;
+        v.fill = step_fill;
+        v.active = active;
+        v.slots = cfg.period - 1;
+        v.period = cfg.period;
+        return v;
+    }
+    bool stepped() const { return (cfg.flags & PACE_STEP_BUFFER) != 0; }
 };
 
 namespace {
@@ -120,7 +135,7 @@ PACE_API int pace_state_alloc(const pace_config *cfg, int init_kind, const void 
     if (rc) return rc;
     if (cfg->period < 1 || cfg->period > 64) return fail(PACE_EUNSUPPORTED, "period must be 1..64");
     if ((rc = check_dtype(cfg->in_dtype))) return rc;
-    if (cfg->flags & ~PACE_STATS_ERR) return fail(PACE_EINVAL, "unknown flags 0x%x", cfg->flags);
+    if (cfg->flags & ~(PACE_STATS_ERR | PACE_STEP_BUFFER)) return fail(PACE_EINVAL, "unknown flags 0x%x", cfg->flags);
     if ((cfg->flags & PACE_STATS_ERR) && cfg->heads > PACE_STATS_MAX_HEADS)
         return fail(PACE_EINVAL, "PACE_STATS_ERR takes at most %d heads", PACE_STATS_MAX_HEADS);
     if (!cfg->head_bits) return fail(PACE_EINVAL, "head_bits must not be NULL");
@@ -168,6 +183,9 @@ PACE_API int pace_state_alloc(const pace_config *cfg, int init_kind, const void 
         if (st->d_counter) (void)hipFree(st->d_counter);
         if (st->colerr) (void)hipFree(st->colerr);
         if (st->d_err) (void)hipFree(st->d_err);
+        if (st->step_kv) (void)hipFree(st->step_kv);
+        if (st->step_ab) (void)hipFree(st->step_ab);
+        if (st->step_fill) (void)hipFree(st->step_fill);
         delete st;
         (void)code;
         return hip_fail(err, what);
@@ -191,6 +209,20 @@ PACE_API int pace_state_alloc(const pace_config *cfg, int init_kind, const void 
             return cleanup(0, "hipMalloc(error sums)", e);
         if (init_kind != PACE_INIT_F32 && (e = hipMemsetAsync(st->colerr, 0, bytes_err, s)) != hipSuccess)
             return cleanup(0, "zero error statistics", e);
+    }
+    if (cfg->flags & PACE_STEP_BUFFER) {
+        const size_t states = (size_t)cfg->batch * cfg->heads, slots = (size_t)cfg->period - 1;
+        const size_t elem = cfg->in_dtype == PACE_DTYPE_BF16 ? 2 : 4;
+        const size_t b_kv = states * slots * (cfg->d_k + cfg->d_v) * elem, b_ab = states * slots * 8;
+        st->bytes_step = b_kv + b_ab + states * 4;
+        if (slots && (e = hipMalloc(&st->step_kv, b_kv)) != hipSuccess)
+            return cleanup(0, "hipMalloc(step buffer)", e);
+        if (slots && (e = hipMalloc((void **)&st->step_ab, b_ab)) != hipSuccess)
+            return cleanup(0, "hipMalloc(step buffer gates)", e);
+        if ((e = hipMalloc((void **)&st->step_fill, states * 4)) != hipSuccess)
+            return cleanup(0, "hipMalloc(step fill)", e);
+        if ((e = hipMemsetAsync(st->step_fill, 0, states * 4, s)) != hipSuccess)
+            return cleanup(0, "zero step fill", e);
     }
     if ((e = hipMemcpyAsync(st->d_map, st->map.data(), sizeof(int32_t) * st->map.size(),
                             hipMemcpyHostToDevice, s)) != hipSuccess)
@@ -233,6 +265,9 @@ PACE_API int pace_state_free(pace_state *st) {
     if (st->d_counter) (void)hipFree(st->d_counter);
     if (st->colerr) (void)hipFree(st->colerr);
     if (st->d_err) (void)hipFree(st->d_err);
+    if (st->step_kv) (void)hipFree(st->step_kv);
+    if (st->step_ab) (void)hipFree(st->step_ab);
+    if (st->step_fill) (void)hipFree(st->step_fill);
     delete st;
     if (e != hipSuccess) return hip_fail(e, "pace_state_free");
     return ok();
@@ -254,6 +289,8 @@ PACE_API int pace_decode_period(pace_state *st, int32_t n_tok, const void *q, co
                                 const void *v, const float *alpha, const float *beta,
                                 float *out, void *stream) {
     if (!st) return fail(PACE_EINVAL, "null state handle");
+    if (st->stepped())
+        return fail(PACE_EINVAL, "a PACE_STEP_BUFFER handle decodes with pace_decode_step");
     if (n_tok < 1 || n_tok > st->cfg.period)
         return fail(PACE_EINVAL, "n_tok = %d outside 1..period (%d)", n_tok, st->cfg.period);
     int rc = check_tokens(n_tok, st->cfg.in_dtype, q, k, v, alpha, beta);
@@ -272,6 +309,38 @@ PACE_API int pace_decode_period(pace_state *st, int32_t n_tok, const void *q, co
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     st->periods += 1;
     st->tokens += (uint64_t)n_tok;
+    return ok();
+}
+
+PACE_API int pace_decode_step(pace_state *st, const void *q, const void *k, const void *v,
+                              const float *alpha, const float *beta, const uint8_t *active,
+                              float *out, void *stream) {
+    if (!st) return fail(PACE_EINVAL, "null state handle");
+    if (!st->stepped()) return fail(PACE_EINVAL, "the handle was not allocated with PACE_STEP_BUFFER");
+    int rc = check_tokens(1, st->cfg.in_dtype, q, k, v, alpha, beta);
+    if (rc) return rc;
+    if (!out || !aligned(out, 16)) return fail(PACE_EINVAL, "out must be a 16-byte aligned device pointer");
+    hipStream_t s = (hipStream_t)stream;
+    const int bf16 = st->cfg.in_dtype == PACE_DTYPE_BF16;
+    const pace::StepView sv = st->step_view(active);
+    hipError_t e;
+    if (pace::mfma_step_supported(st->cfg.d_k, st->cfg.d_v, st->cfg.period, bf16,
+                                  (long long)st->cfg.batch * st->cfg.heads))
+        e = pace::launch_step_mfma(st->view(), sv, st->d_map + st->cfg.heads,
+                                   st->d_map + st->cfg.heads + st->n8, q, k, v, alpha, beta, out, s);
+    else
+        e = pace::launch_step_v0(st->view(), sv, q, k, v, alpha, beta, out, bf16, s);
+    if (e != hipSuccess) return hip_fail(e, "step launch");
+    st->tokens += 1;
+    return ok();
+}
+
+PACE_API int pace_flush_steps(pace_state *st, void *stream) {
+    if (!st) return fail(PACE_EINVAL, "null state handle");
+    if (!st->stepped()) return fail(PACE_EINVAL, "the handle was not allocated with PACE_STEP_BUFFER");
+    hipError_t e = pace::launch_flush_v0(st->view(), st->step_view(nullptr),
+                                         st->cfg.in_dtype == PACE_DTYPE_BF16, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "flush launch");
     return ok();
 }
 
@@ -335,6 +404,7 @@ PACE_API int pace_quant_stats(const pace_state *st, pace_stats *out, void *strea
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_fail(e, "quant_stats");
     r.zero_columns = zeros;
+    r.bytes_step_buffer = st->bytes_step;
     if (st->colerr) {
         r.err_tracked = 1;
         for (int h = 0; h < c.heads; ++h) {

@@ -35,11 +35,12 @@ PACE_READ_DEQUANT = 1
 PACE_READ_RAW = 2
 
 PACE_STATS_ERR = 0x1
+PACE_STEP_BUFFER = 0x2
 PACE_STATS_MAX_HEADS = 256
 
 EXPORTED = ("pace_abi_version", "pace_last_error", "pace_state_alloc", "pace_state_free",
             "pace_state_config", "pace_raw_bytes", "pace_decode_period", "pace_read_state",
-            "pace_quant_stats", "pace_prefill_f32")
+            "pace_quant_stats", "pace_prefill_f32", "pace_decode_step", "pace_flush_steps")
 
 
 class PaceError(RuntimeError):
@@ -62,7 +63,8 @@ class pace_stats(ctypes.Structure):
                 ("bytes_fp16_equiv", ctypes.c_uint64), ("bytes_int8_equiv", ctypes.c_uint64),
                 ("heads4", ctypes.c_int32), ("heads8", ctypes.c_int32),
                 ("periods", ctypes.c_uint64), ("tokens", ctypes.c_uint64),
-                ("zero_columns", ctypes.c_uint64), ("err_tracked", ctypes.c_int32),
+                ("zero_columns", ctypes.c_uint64), ("bytes_step_buffer", ctypes.c_uint64),
+                ("err_tracked", ctypes.c_int32),
                 ("err_sq", ctypes.c_double * PACE_STATS_MAX_HEADS),
                 ("ref_sq", ctypes.c_double * PACE_STATS_MAX_HEADS)]
 
@@ -95,6 +97,8 @@ def _load():
         "pace_quant_stats": ([vp, ctypes.POINTER(pace_stats), vp], ctypes.c_int),
         "pace_prefill_f32": ([i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp],
                              ctypes.c_int),
+        "pace_decode_step": ([vp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+        "pace_flush_steps": ([vp, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -170,6 +174,15 @@ def pace_raw_bytes(st: int) -> int:
 def pace_decode_period(st: int, n_tok: int, q, k, v, alpha, beta, out, stream=None) -> None:
     _check(LIB.pace_decode_period(st, n_tok, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                   _ptr(beta), _ptr(out), _stream(stream)))
+
+
+def pace_decode_step(st: int, q, k, v, alpha, beta, out, active=None, stream=None) -> None:
+    _check(LIB.pace_decode_step(st, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                _ptr(active), _ptr(out), _stream(stream)))
+
+
+def pace_flush_steps(st: int, stream=None) -> None:
+    _check(LIB.pace_flush_steps(st, _stream(stream)))
 
 
 def pace_read_state(st: int, what: int, dst, scales_dst=None, stream=None) -> None:

@@ -76,6 +76,18 @@ class State:
         pace.pace_decode_period(self.handle, tok.T, tok.q, tok.k, tok.v, tok.alpha, tok.beta,
                                 out, stream)
 
+    def step(self, tok: DeviceTokens, out: torch.Tensor, active: Optional[torch.Tensor] = None,
+             stream=None):
+        """One decode step of a PACE_STEP_BUFFER handle: tok holds one token
+        ([1, B, H, d]); active is a device uint8 [B] mask or None."""
+        if tok.T != 1:
+            raise ValueError("a step takes exactly one token")
+        pace.pace_decode_step(self.handle, tok.q, tok.k, tok.v, tok.alpha, tok.beta, out,
+                              active, stream)
+
+    def flush_steps(self, stream=None):
+        pace.pace_flush_steps(self.handle, stream)
+
     def read_codes(self, stream=None):
         w = self.w
         codes = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.int8, device="cuda")

@@ -62,7 +62,7 @@ def test_alloc_rejects_bad_config(kw, status):
 
 
 def test_alloc_rejects_bad_flags():
-    assert _alloc_status(flags=2) == pace.PACE_EINVAL
+    assert _alloc_status(flags=4) == pace.PACE_EINVAL
     many = pace.PACE_STATS_MAX_HEADS + 1
     assert _alloc_status(flags=pace.PACE_STATS_ERR, heads=many, head_bits=[4] * many) == pace.PACE_EINVAL
     assert "PACE_STATS_ERR" in pace.pace_last_error()
@@ -106,6 +106,8 @@ def test_null_arguments():
     assert pace.LIB.pace_read_state(None, 0, 16, 16, None) == pace.PACE_EINVAL
     assert pace.LIB.pace_quant_stats(None, None, None) == pace.PACE_EINVAL
     assert pace.LIB.pace_raw_bytes(None, None) == pace.PACE_EINVAL
+    assert pace.LIB.pace_decode_step(None, 16, 16, 16, 16, 16, None, 16, None) == pace.PACE_EINVAL
+    assert pace.LIB.pace_flush_steps(None, None) == pace.PACE_EINVAL
     assert pace.LIB.pace_state_free(None) == pace.PACE_OK
 
 
