@@ -21,6 +21,22 @@ Readings where the pages are silent:
 * ``flush`` ends every partial period early: buffered tokens are applied and
   the state is encoded, as a shorter final period would be.
 
+Adaptive period (``tau`` given; the same page, section 'Research angle':
+round when the accumulated update norm crosses a threshold instead of every
+k tokens).  Reading taken:
+
+* The update norm of token t is the Frobenius norm of its write into the
+  state, ||k_t|| * ||u_t|| with u_t = beta_t (v_t - alpha_t M_{t-1}^T k_t)
+  (M_t = alpha_t M_{t-1} + k_t u_t^T); the accumulated norm A is their sum
+  over the buffered tokens.
+* The threshold is relative: tau * R, with R = ||decode(stored)||_F of the
+  state as of its last encode (0 for a zero state).
+* A step closes the period (applies the buffer and its own token, encodes)
+  when the buffer is full (period - 1 tokens: ``period`` is the maximum
+  period) or when A > tau * R already holds for the buffered tokens: the
+  decision is taken before the step's own write is known, so a token whose
+  write crosses the threshold makes the next token close the period.
+
 This is written as its own loop over the buffer, separately from
 ``pace.period`` (which applies a whole period in one call); the tests pin the
 two against each other.
@@ -35,9 +51,11 @@ from . import gdn, quant
 class Buffered:
     """n states, each with its stored codes and scales and its own buffer."""
 
-    def __init__(self, codes, scales, bits, period: int):
+    def __init__(self, codes, scales, bits, period: int, tau=None):
         if period < 1:
             raise ValueError("period must be >= 1")
+        if tau is not None and not tau > 0:
+            raise ValueError("tau must be positive")
         self.codes = np.array(codes, dtype=np.int16)
         self.scales = np.array(scales, dtype=np.float32)
         self.bits = np.broadcast_to(np.asarray(bits), self.codes.shape[:1]).copy()
@@ -45,6 +63,23 @@ class Buffered:
         n = self.codes.shape[0]
         self.buf = [[] for _ in range(n)]  # per state: list of (k, v, alpha, beta)
         self.last_pre = [None] * n           # high-precision state of each state's last encode
+        self.tau = tau
+        self.A = np.zeros(n)                 # accumulated update norm of the buffered tokens
+        self.R = np.array([self._norm(i) for i in range(n)])
+
+    def _norm(self, i: int) -> float:
+        return float(np.linalg.norm(quant.decode(self.codes[i], self.scales[i])))
+
+    def closes(self, i: int) -> bool:
+        """Whether the next token of state i ends its period."""
+        if len(self.buf[i]) + 1 == self.period:
+            return True
+        return self.tau is not None and self.A[i] > self.tau * self.R[i]
+
+    def margin(self, i: int) -> float:
+        """A - tau R relative to tau R (how far the adaptive decision is from its threshold)."""
+        t = self.tau * self.R[i]
+        return (self.A[i] - t) / t if t > 0 else np.inf
 
     @property
     def fill(self) -> np.ndarray:
@@ -62,22 +97,29 @@ class Buffered:
         self.codes[i], self.scales[i] = c[0], s[0]
         self.last_pre[i] = M[0]
         self.buf[i] = []
+        self.A[i] = 0.0
+        self.R[i] = self._norm(i)
 
-    def step(self, q, k, v, alpha, beta, active=None) -> np.ndarray:
+    def step(self, q, k, v, alpha, beta, active=None, decide=None) -> np.ndarray:
         """One token per state: q, k [n, d_k], v [n, d_v], alpha, beta [n]
-        (float64 values); active [n] bool or None (all).  Returns the outputs
-        [n, d_v] (NaN for inactive states)."""
+        (float64 values); active [n] bool or None (all).  ``decide`` [n] bool,
+        if given, replaces the adaptive decision of each state (for callers
+        matching another implementation where A sits on the threshold).
+        Returns the outputs [n, d_v] (NaN for inactive states)."""
         n = self.codes.shape[0]
         act = np.ones(n, dtype=bool) if active is None else np.asarray(active, dtype=bool)
         out = np.full((n, v.shape[1]), np.nan)
         for i in np.nonzero(act)[0]:
-            M = self._state(i)
-            M, o = gdn.step(M, q[i][None], k[i][None], v[i][None], np.array([alpha[i]]),
+            M0 = self._state(i)
+            M, o = gdn.step(M0, q[i][None], k[i][None], v[i][None], np.array([alpha[i]]),
                             np.array([beta[i]]))
             out[i] = o[0]
-            if len(self.buf[i]) + 1 == self.period:
+            close = self.closes(i) if decide is None else bool(decide[i])
+            if close:
                 self._encode(i, M)
             else:
+                u = beta[i] * (v[i] - alpha[i] * (k[i] @ M0[0]))
+                self.A[i] += np.linalg.norm(k[i]) * np.linalg.norm(u)
                 self.buf[i].append((np.array(k[i]), np.array(v[i]), float(alpha[i]), float(beta[i])))
         return out
 

@@ -93,3 +93,71 @@ def test_buffer_never_holds_a_full_period():
     for t in range(12):
         st.step(q[t], k[t], v[t], a[t], b[t])
         assert st.fill.max() <= period - 1
+
+
+def _adaptive_run(period, tau, T=14, seed=11):
+    rng = np.random.default_rng(seed)
+    n, dk, dv = 3, 8, 8
+    bits = np.array([4, 8, 4])
+    M0 = rng.standard_normal((n, dk, dv))
+    toks = _tokens(rng, T, n, dk, dv)
+    c0, s0 = quant.encode(M0, bits)
+    st = buffered.Buffered(c0, s0, bits, period, tau=tau)
+    outs = [st.step(*(x[t] for x in toks)) for t in range(T)]
+    return M0, bits, toks, st, np.stack(outs)
+
+
+def test_adaptive_never_crossing_is_the_fixed_period():
+    M0, bits, toks, st, outs = _adaptive_run(period=5, tau=1e30)
+    O, hist, _ = opace.run(M0, bits, *toks, 5)
+    np.testing.assert_allclose(outs, O, rtol=1e-12, atol=1e-12)
+    st.flush()
+    np.testing.assert_array_equal(st.codes, hist[-1][0])
+
+
+def test_adaptive_tiny_threshold_is_period_two():
+    # any buffered write crosses tau * R: the second token of each period closes it
+    M0, bits, toks, st, outs = _adaptive_run(period=6, tau=1e-30)
+    O, hist, _ = opace.run(M0, bits, *toks, 2)
+    np.testing.assert_allclose(outs, O, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(st.codes, hist[-1][0])
+    np.testing.assert_array_equal(st.scales, hist[-1][1])
+
+
+def test_update_norm_is_the_write_into_the_state():
+    # A grows by ||M_t - alpha_t M_{t-1}||_F (the token's write), computed here
+    # from the recurrence itself; R is the decoded stored state's norm
+    rng = np.random.default_rng(2)
+    n, d = 2, 8
+    c, s = quant.encode(rng.standard_normal((n, d, d)), 4)
+    st = buffered.Buffered(c, s, 4, 8, tau=1e30)
+    np.testing.assert_allclose(st.R, np.linalg.norm(quant.decode(c, s), axis=(1, 2)))
+    q, k, v, a, b = _tokens(rng, 3, n, d, d)
+    M = quant.decode(c, s)
+    A = np.zeros(n)
+    for t in range(3):
+        Mn, _ = gdn.step(M, q[t], k[t], v[t], a[t], b[t])
+        A += np.linalg.norm(Mn - a[t][:, None, None] * M, axis=(1, 2))
+        st.step(q[t], k[t], v[t], a[t], b[t])
+        np.testing.assert_allclose(st.A, A, rtol=1e-12)
+        M = Mn
+
+
+def test_adaptive_threshold_between_periods():
+    # a moderate threshold gives periods between 2 and the maximum, and
+    # every close happens exactly when A > tau R held before the step
+    rng = np.random.default_rng(9)
+    n, d, kmax, tau = 4, 8, 8, 0.5
+    c, s = quant.encode(rng.standard_normal((n, d, d)), 4)
+    st = buffered.Buffered(c, s, 4, kmax, tau=tau)
+    q, k, v, a, b = _tokens(rng, 40, n, d, d)
+    lengths = []
+    for t in range(40):
+        fill = st.fill.copy()
+        expect = [(fill[i] + 1 == kmax) or (st.A[i] > tau * st.R[i]) for i in range(n)]
+        st.step(q[t], k[t], v[t], a[t], b[t])
+        for i in range(n):
+            assert (st.fill[i] == 0) == expect[i]
+            if expect[i]:
+                lengths.append(fill[i] + 1)
+    assert 2 <= min(lengths) and max(lengths) <= kmax and len(set(lengths)) > 1
