@@ -59,18 +59,19 @@ def algorithmic_bytes(w: inputs.Workload, n_tok: int, head_bits) -> int:
     return w.B * (2 * state + n_tok * per_seq_tok)
 
 
-def algorithmic_bytes_step(w: inputs.Workload, head_bits) -> float:
+def algorithmic_bytes_step(w: inputs.Workload, head_bits, k_eff=None) -> float:
     """Mean bytes of one per-step decode call over a period of k = w.period
     calls: the stored state is read by every call and written by the last;
     call f reads the f buffered tokens (k_t, v_t, alpha_t, beta_t) and every
     call but the last appends its own; each call reads its q/k/v/alpha/beta and
-    writes its float32 outputs."""
+    writes its float32 outputs.  An adaptive period passes its measured mean
+    length as k_eff (the model then treats every period as that long)."""
     e_in = 2 if w.dtype == inputs.DT_BF16 else 4
-    k = w.period
+    k = w.period if k_eff is None else k_eff
     state = sum(w.dk * w.dv * int(b) // 8 + 4 * w.dv for b in head_bits)
     buf_tok = w.H * ((w.dk + w.dv) * e_in + 8)
     io_tok = w.H * ((w.dk * 2 + w.dv) * e_in + 8 + 4 * w.dv)
-    per_period = (k + 1) * state + (k * (k - 1) // 2 + (k - 1)) * buf_tok + k * io_tok
+    per_period = (k + 1) * state + (k * (k - 1) / 2 + (k - 1)) * buf_tok + k * io_tok
     return w.B * per_period / k
 
 
@@ -152,6 +153,9 @@ def main() -> int:
     ap.add_argument("--mode", default="period", choices=("period", "step"),
                     help="period: one call per period of k tokens; step: one call per token "
                          "(PACE_STEP_BUFFER handle), every sequence active")
+    ap.add_argument("--adapt-tau", type=float, default=0.0,
+                    help="step mode: adaptive period with this threshold (the workload's period "
+                         "is the maximum)")
     ap.add_argument("--period", type=int, default=None, help="override the workload's period")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--ring", type=int, default=4, help="distinct input periods resident in HBM")
@@ -195,8 +199,10 @@ def main() -> int:
     M0 = torch.zeros((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
     runtime.prefill(w, runtime.DeviceTokens(warm_tok), M0)
     step_mode = args.mode == "step"
-    st = runtime.State(w, head_bits, pace.PACE_INIT_F32, M0,
-                       flags=pace.PACE_STEP_BUFFER if step_mode else 0)
+    adaptive = step_mode and args.adapt_tau > 0
+    flags = (pace.PACE_STEP_BUFFER if step_mode else 0) | (pace.PACE_ADAPTIVE if adaptive else 0)
+    st = runtime.State(w, head_bits, pace.PACE_INIT_F32, M0, flags=flags,
+                       adapt_tau=args.adapt_tau if adaptive else 0.0)
     del M0
     ring = [runtime.DeviceTokens(tk) for tk in ring_tok]
     if step_mode:   # one token per call: the ring's periods cut into tokens
@@ -237,7 +243,19 @@ def main() -> int:
     launch_ms = sum(a.elapsed_time(b) for a, b in ev) / K
     log(f"timed {K} steps: {total_ms:.3f} ms on the device, {t_wall * 1e3:.1f} ms wall")
 
-    nbytes = algorithmic_bytes_step(w, head_bits) if step_mode else algorithmic_bytes(w, C, head_bits)
+    k_eff = None
+    if adaptive:
+        # realised mean period: replay the timed steps untimed, counting the
+        # states each step re-encodes (fill back to 0)
+        closes = 0
+        for i in range(K):
+            call(ring[(args.warmup + K + i) % ring_n], out)
+            fill, _ = st.read_step()
+            closes += int((fill == 0).sum().item())
+        k_eff = K * w.B * w.H / max(1, closes)
+        log(f"adaptive period: mean period {k_eff:.2f} tokens over {K} steps")
+    nbytes = algorithmic_bytes_step(w, head_bits, k_eff) if step_mode else \
+        algorithmic_bytes(w, C, head_bits)
     achieved = nbytes / (launch_ms * 1e-3) / 1e9
     sha = kernel_sha()
     tokens_per_call = 1 if step_mode else C
@@ -259,6 +277,8 @@ def main() -> int:
                    "period": C, "heads_int8": int((head_bits == 8).sum()),
                    "inputs": w.dtype, "outlier_channels": w.n_outliers,
                    "mode": args.mode, "decode_steps": K * tokens_per_call,
+                   "adapt_tau": args.adapt_tau if adaptive else None,
+                   "mean_period": k_eff,
                    "input_ring_calls": ring_n,
                    "start_state": f"{warm[2]} {'prompt' if w.prompt else 'warm-up'} tokens from zero"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -84,6 +84,9 @@ extern "C" {
 #define PACE_READ_CODES 0   /* dst: device int8 [B, H, d_k, d_v]; scales_dst: device float32 [B, H, d_v] */
 #define PACE_READ_DEQUANT 1 /* dst: device float32 [B, H, d_k, d_v] = c_ij * s_j; scales_dst may be NULL */
 #define PACE_READ_RAW 2     /* dst: device bytes [pace_raw_bytes()]; scales_dst must be NULL */
+#define PACE_READ_STEP 3    /* PACE_STEP_BUFFER handles: dst: device int32 [B, H] buffered tokens
+                               per state; scales_dst: device float32 [B, H, 2] = (A, R) of
+                               PACE_ADAPTIVE (zeros without it), or NULL */
 
 /* config flags */
 /* PACE_STATS_ERR: every encode (the PACE_INIT_F32 encode at alloc and the
@@ -106,6 +109,16 @@ extern "C" {
  * B * H * 4 for the fill counts (pace_stats.bytes_step_buffer).  Such a
  * handle rejects pace_decode_period. */
 #define PACE_STEP_BUFFER 0x2u
+/* PACE_ADAPTIVE (with PACE_STEP_BUFFER): the period becomes adaptive ('PACE:
+ * four-bit recurrent state by rounding less often', section 'Research angle':
+ * round when the accumulated update norm crosses a threshold).  Each state
+ * keeps A, the sum over its buffered tokens of the norm of their write into
+ * the state, ||k_t|| * ||u_t|| with u_t = beta_t (v_t - alpha_t M_{t-1}^T k_t),
+ * and R, the Frobenius norm of its stored state as of its last encode.  A
+ * step closes the period (applies the buffer and its own token, re-encodes)
+ * when its buffer is full (cfg.period is then the maximum period) or when
+ * A > adapt_tau * R already holds before the step.  Costs B * H * 8 bytes. */
+#define PACE_ADAPTIVE 0x4u
 
 typedef struct pace_state pace_state; /* opaque; owns the device pools */
 
@@ -117,7 +130,8 @@ typedef struct pace_config {
     int32_t period;           /* k: most tokens one pace_decode_period call may apply, 1..64 */
     int32_t in_dtype;         /* PACE_DTYPE_F32 or PACE_DTYPE_BF16: element type of q, k, v */
     const uint8_t *head_bits; /* host [H]: bit width of each head, 4 or 8; copied at alloc */
-    uint32_t flags;           /* 0 or an OR of PACE_STATS_ERR, PACE_STEP_BUFFER */
+    uint32_t flags;           /* 0 or an OR of PACE_STATS_ERR, PACE_STEP_BUFFER, PACE_ADAPTIVE */
+    float adapt_tau;          /* PACE_ADAPTIVE: threshold tau, finite and > 0; otherwise ignored */
 } pace_config;
 
 typedef struct pace_stats {

@@ -114,7 +114,17 @@ __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int
     static_assert(!STEP || WPT == 1, "steps run one wave per tile");
     const int f = STEP ? __builtin_amdgcn_readfirstlane(a.step.fill[tile_row]) : 0;
     const int n_tok = STEP ? f + 1 : a.n_tok;
-    const bool pend = !STEP || n_tok == a.step.period;
+    // adaptive period: the step also closes the period once the buffered
+    // tokens' summed write norms A exceed tau R (R: the stored state's norm
+    // at its last encode)
+    const bool adaptive = STEP && a.step.tau > 0.f;
+    float adapt_A = 0.f, adapt_R = 0.f;
+    if (adaptive) {
+        adapt_A = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.step.adapt[2 * tile_row])));
+        adapt_R = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.step.adapt[2 * tile_row + 1])));
+    }
+    const bool pend = !STEP || n_tok == a.step.period || (adaptive && adapt_A > a.step.tau * adapt_R);
+    float uacc = 0.f, racc = 0.f;  // adaptive: sum of u_f^2 (mid-period) or of (c s)^2 (encode)
     uint16_t *sbuf = STEP ? (uint16_t *)a.step.kv + tile_row * a.step.slots * (2 * DK) : nullptr;
     float *sab = STEP ? a.step.ab + tile_row * a.step.slots * 2 : nullptr;
 
@@ -418,6 +428,12 @@ __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int
                     x, at((f32x4 *)obase, (STEP ? 0u : (uint32_t)t * o_tok) + (uint32_t)(16 * cb - 16 + c4) * 4u));
         }
         if constexpr (STEP) {
+            if (adaptive && !pend) {
+                // this token's write u_f (column j): row f of W, held by lane group f / 4
+                const int r = f & 3;
+                const float u = r == 0 ? WO[0] : r == 1 ? WO[1] : r == 2 ? WO[2] : WO[3];
+                if (g == (f >> 2)) uacc = fmaf(u, u, uacc);
+            }
             if (!pend) continue;  // mid-period step: the stored state is only read
         }
 
@@ -476,8 +492,34 @@ __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int
         outc.store(codes, cb, lane);
         if (g == 0) scl[j] = s_new;
         if constexpr (ERR) column_error<NRT>(acc, y, sig, s_new, a.p.colerr + (tile_row * DK + j) * 2, g);
+        if constexpr (STEP) {
+            if (adaptive) {
+                float cc = 0.f;
+#pragma unroll
+                for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float c = __uint_as_float(y[rt][r]) - 12582912.f;
+                        cc = fmaf(c, c, cc);
+                    }
+                racc = fmaf(cc, s_new * s_new, racc);
+            }
+        }
     }
     if constexpr (STEP) {
+        if (adaptive) {
+            float v = pend ? racc : uacc;
+#pragma unroll
+            for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
+            if (lane == 0) {
+                if (pend) {
+                    a.step.adapt[2 * tile_row] = 0.f;
+                    a.step.adapt[2 * tile_row + 1] = sqrtf(v);   // ||decode(new stored)||_F
+                } else {
+                    a.step.adapt[2 * tile_row] = adapt_A + sqrtf(L.kk[f][f]) * sqrtf(v);
+                }
+            }
+        }
         if (lane == 0) a.step.fill[tile_row] = pend ? 0 : n_tok;
     }
 #undef TRACE

@@ -43,11 +43,12 @@ __device__ inline void load_column(const uint8_t *codes, int bits, int j, float 
 
 // Per-column quantizer: s = absmax / qmax (float32, correctly rounded),
 // c = rint(M / s) with round-half-even, clamped to +-qmax; s = 0 -> codes 0.
-// err (NULL: skipped) receives the sums over the column of (M - c s)^2 and M^2.
+// err (NULL: skipped) receives the sums over the column of (M - c s)^2 and M^2;
+// deq2 (NULL: skipped) the sum of (c s)^2.
 template <int DK>
 __device__ inline float store_column(uint8_t *codes, int bits, int j, const float M[DK],
-                                     float *err) {
-    float e2 = 0.f, m2 = 0.f;
+                                     float *err, float *deq2 = nullptr) {
+    float e2 = 0.f, m2 = 0.f, q2 = 0.f;
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < DK; ++i) amax = fmaxf(amax, fabsf(M[i]));
@@ -70,6 +71,7 @@ __device__ inline float store_column(uint8_t *codes, int bits, int j, const floa
                 e2 += d0 * d0 + d1 * d1;
                 m2 += M[i] * M[i] + M[i2] * M[i2];
             }
+            q2 += (float)(c0 * c0 + c1 * c1);
             int sh;
             size_t o = loc4(DK, i, j, &sh);
             codes[o] = (uint8_t)((c0 & 15) | ((c1 & 15) << 4));
@@ -85,12 +87,14 @@ __device__ inline float store_column(uint8_t *codes, int bits, int j, const floa
                 e2 += d * d;
                 m2 += M[i] * M[i];
             }
+            q2 += (float)(c * c);
         }
     }
     if (err) {
         err[0] = e2;
         err[1] = m2;
     }
+    if (deq2) *deq2 = q2 * s * s;
     return s;
 }
 
@@ -214,11 +218,14 @@ __device__ inline void copy_in(void *dst, size_t di, const void *src, size_t si,
 // Apply buffered tokens 0..f-1 of state `tile` and then, if cur_k != NULL, the
 // step's own token (whose output is written); column j per thread, as
 // apply_tokens.
+// u_cur (if not NULL) receives this thread's entry u_j = beta (v_j - alpha d_j)
+// of the step token's write.
 template <int DK>
 __device__ inline void apply_buffered(float M[DK], float *sk, float *sq, const StepView &sv,
                                       int tile, int dv, int j, int f, const void *q,
                                       const void *cur_k, const void *v, const float *alpha,
-                                      const float *beta, float *out, int bf16) {
+                                      const float *beta, float *out, int bf16,
+                                      float *u_cur = nullptr) {
     const size_t row = (size_t)DK + dv;  // elements per buffered token
     const int last = cur_k ? f : f - 1;
     for (int t = 0; t <= last; ++t) {
@@ -243,30 +250,65 @@ __device__ inline void apply_buffered(float M[DK], float *sk, float *sq, const S
             M[i] = a * (M[i] - bk * d) + bk * vj;
             o = fmaf(sq[i], M[i], o);
         }
-        if (cur) out[(size_t)tile * dv + j] = o;
+        if (cur) {
+            out[(size_t)tile * dv + j] = o;
+            if (u_cur) *u_cur = bt * (vj - a * d);
+        }
     }
+}
+
+// sum of x over the block's threads (blockDim.x <= 256), returned to every thread
+__device__ inline float block_sum(float x, float *red) {
+    for (int m = 32; m > 0; m >>= 1) x += __shfl_xor(x, m);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    float t = 0.f;
+    for (int w = 0; w < (int)(blockDim.x + 63) / 64; ++w) t += red[w];
+    return t;
 }
 
 template <int DK>
 __global__ void step_v0_kernel(PoolView p, StepView sv, const void *q, const void *k,
                                const void *v, const float *alpha, const float *beta, float *out,
                                int bf16) {
-    __shared__ float sk[DK], sq[DK];
+    __shared__ float sk[DK], sq[DK], red[4];
     const int tile = blockIdx.x, b = tile / p.H, h = tile % p.H, j = threadIdx.x;
     if (sv.active && !sv.active[b]) return;
     const int f = sv.fill[tile];
+    const bool adaptive = sv.tau > 0.f;
+    const float A = adaptive ? sv.adapt[2 * tile] : 0.f, R = adaptive ? sv.adapt[2 * tile + 1] : 0.f;
+    const bool close = f + 1 == sv.period || (adaptive && A > sv.tau * R);
     int bits;
     uint8_t *codes = tile_codes(p, b, h, &bits);
     float *sc = p.scales + (size_t)tile * p.dv;
     float M[DK];
     load_column<DK>(codes, bits, j, sc[j], M);
-    apply_buffered<DK>(M, sk, sq, sv, tile, p.dv, j, f, q, k, v, alpha, beta, out, bf16);
-    // every thread has read fill[tile] before the first barrier inside apply_buffered
-    if (f + 1 == sv.period) {
+    float u = 0.f;
+    apply_buffered<DK>(M, sk, sq, sv, tile, p.dv, j, f, q, k, v, alpha, beta, out, bf16, &u);
+    // every thread has read fill[tile] and adapt[] before the first barrier inside apply_buffered
+    if (close) {
+        float q2 = 0.f;
         sc[j] = store_column<DK>(codes, bits, j, M,
-                                 p.colerr ? p.colerr + ((size_t)tile * p.dv + j) * 2 : nullptr);
+                                 p.colerr ? p.colerr + ((size_t)tile * p.dv + j) * 2 : nullptr, &q2);
+        if (adaptive) {
+            const float r2 = block_sum(q2, red);
+            if (j == 0) {
+                sv.adapt[2 * tile] = 0.f;
+                sv.adapt[2 * tile + 1] = sqrtf(r2);
+            }
+        }
         if (j == 0) sv.fill[tile] = 0;
     } else {
+        if (adaptive) {
+            // A += ||k_f|| ||u_f||; sk still holds k_f
+            const float u2 = block_sum(u * u, red);
+            if (j == 0) {
+                float k2 = 0.f;
+                for (int i = 0; i < DK; ++i) k2 = fmaf(sk[i], sk[i], k2);
+                sv.adapt[2 * tile] = A + sqrtf(k2) * sqrtf(u2);
+            }
+        }
         const size_t slot = (size_t)tile * sv.slots + f, row = (size_t)DK + p.dv;
         for (int i = j; i < DK; i += blockDim.x) copy_in(sv.kv, slot * row + i, k, (size_t)tile * DK + i, bf16);
         copy_in(sv.kv, slot * row + DK + j, v, (size_t)tile * p.dv + j, bf16);
@@ -280,7 +322,7 @@ __global__ void step_v0_kernel(PoolView p, StepView sv, const void *q, const voi
 
 template <int DK>
 __global__ void flush_v0_kernel(PoolView p, StepView sv, int bf16) {
-    __shared__ float sk[DK], sq[DK];
+    __shared__ float sk[DK], sq[DK], red[4];
     const int tile = blockIdx.x, b = tile / p.H, h = tile % p.H, j = threadIdx.x;
     const int f = sv.fill[tile];
     if (f == 0) return;
@@ -291,9 +333,36 @@ __global__ void flush_v0_kernel(PoolView p, StepView sv, int bf16) {
     load_column<DK>(codes, bits, j, sc[j], M);
     apply_buffered<DK>(M, sk, sq, sv, tile, p.dv, j, f, nullptr, nullptr, nullptr, nullptr,
                        nullptr, nullptr, bf16);
+    float q2 = 0.f;
     sc[j] = store_column<DK>(codes, bits, j, M,
-                             p.colerr ? p.colerr + ((size_t)tile * p.dv + j) * 2 : nullptr);
+                             p.colerr ? p.colerr + ((size_t)tile * p.dv + j) * 2 : nullptr, &q2);
+    if (sv.tau > 0.f) {
+        const float r2 = block_sum(q2, red);
+        if (j == 0) {
+            sv.adapt[2 * tile] = 0.f;
+            sv.adapt[2 * tile + 1] = sqrtf(r2);
+        }
+    }
     if (j == 0) sv.fill[tile] = 0;
+}
+
+// adapt[2 t] = 0, adapt[2 t + 1] = ||decode(stored state t)||_F
+template <int DK>
+__global__ void adapt_init_kernel(PoolView p, float *adapt) {
+    __shared__ float red[4];
+    const int tile = blockIdx.x, b = tile / p.H, h = tile % p.H, j = threadIdx.x;
+    int bits;
+    const uint8_t *codes = tile_codes(p, b, h, &bits);
+    float M[DK];
+    load_column<DK>(codes, bits, j, p.scales[(size_t)tile * p.dv + j], M);
+    float m2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < DK; ++i) m2 = fmaf(M[i], M[i], m2);
+    const float r2 = block_sum(m2, red);
+    if (j == 0) {
+        adapt[2 * tile] = 0.f;
+        adapt[2 * tile + 1] = sqrtf(r2);
+    }
 }
 
 // one block per head; float64 sums over sequences and columns
@@ -404,6 +473,15 @@ hipError_t launch_flush_v0(const PoolView &p, const StepView &sv, int in_bf16, h
         hipLaunchKernelGGL(flush_v0_kernel<128>, grid, block, 0, s, p, sv, in_bf16);
     else
         hipLaunchKernelGGL(flush_v0_kernel<64>, grid, block, 0, s, p, sv, in_bf16);
+    return hipGetLastError();
+}
+
+hipError_t launch_adapt_init(const PoolView &p, float *adapt, hipStream_t s) {
+    dim3 grid(p.B * p.H), block(p.dv);
+    if (p.dk == 128)
+        hipLaunchKernelGGL(adapt_init_kernel<128>, grid, block, 0, s, p, adapt);
+    else
+        hipLaunchKernelGGL(adapt_init_kernel<64>, grid, block, 0, s, p, adapt);
     return hipGetLastError();
 }
 

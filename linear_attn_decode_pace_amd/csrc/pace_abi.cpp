@@ -33,6 +33,7 @@ struct pace_state {
     void *step_kv = nullptr;       // PACE_STEP_BUFFER: [B * H][period - 1][d_k + d_v] in_dtype
     float *step_ab = nullptr;      // PACE_STEP_BUFFER: [B * H][period - 1][2]
     int32_t *step_fill = nullptr;  // PACE_STEP_BUFFER: [B * H]
+    float *adapt = nullptr;        // PACE_ADAPTIVE: [B * H][2] = (A, R)
     size_t bytes4 = 0, bytes8 = 0, bytes_scales = 0, bytes_step = 0;
     uint64_t periods = 0, tokens = 0;
 
@@ -59,6 +60,8 @@ struct pace_state {
         v.active = active;
         v.slots = cfg.period - 1;
         v.period = cfg.period;
+        v.adapt = adapt;
+        v.tau = adapt ? cfg.adapt_tau : 0.f;
         return v;
     }
     bool stepped() const { return (cfg.flags & PACE_STEP_BUFFER) != 0; }
@@ -135,7 +138,13 @@ PACE_API int pace_state_alloc(const pace_config *cfg, int init_kind, const void 
     if (rc) return rc;
     if (cfg->period < 1 || cfg->period > 64) return fail(PACE_EUNSUPPORTED, "period must be 1..64");
     if ((rc = check_dtype(cfg->in_dtype))) return rc;
-    if (cfg->flags & ~(PACE_STATS_ERR | PACE_STEP_BUFFER)) return fail(PACE_EINVAL, "unknown flags 0x%x", cfg->flags);
+    if (cfg->flags & ~(PACE_STATS_ERR | PACE_STEP_BUFFER | PACE_ADAPTIVE))
+        return fail(PACE_EINVAL, "unknown flags 0x%x", cfg->flags);
+    if (cfg->flags & PACE_ADAPTIVE) {
+        if (!(cfg->flags & PACE_STEP_BUFFER)) return fail(PACE_EINVAL, "PACE_ADAPTIVE needs PACE_STEP_BUFFER");
+        if (!(cfg->adapt_tau > 0.f) || !(cfg->adapt_tau < 3.0e38f))
+            return fail(PACE_EINVAL, "adapt_tau must be finite and > 0");
+    }
     if ((cfg->flags & PACE_STATS_ERR) && cfg->heads > PACE_STATS_MAX_HEADS)
         return fail(PACE_EINVAL, "PACE_STATS_ERR takes at most %d heads", PACE_STATS_MAX_HEADS);
     if (!cfg->head_bits) return fail(PACE_EINVAL, "head_bits must not be NULL");
@@ -186,6 +195,7 @@ PACE_API int pace_state_alloc(const pace_config *cfg, int init_kind, const void 
         if (st->step_kv) (void)hipFree(st->step_kv);
         if (st->step_ab) (void)hipFree(st->step_ab);
         if (st->step_fill) (void)hipFree(st->step_fill);
+        if (st->adapt) (void)hipFree(st->adapt);
         delete st;
         (void)code;
         return hip_fail(err, what);
@@ -223,6 +233,9 @@ PACE_API int pace_state_alloc(const pace_config *cfg, int init_kind, const void 
             return cleanup(0, "hipMalloc(step fill)", e);
         if ((e = hipMemsetAsync(st->step_fill, 0, states * 4, s)) != hipSuccess)
             return cleanup(0, "zero step fill", e);
+        if ((cfg->flags & PACE_ADAPTIVE) && (e = hipMalloc((void **)&st->adapt, states * 8)) != hipSuccess)
+            return cleanup(0, "hipMalloc(adaptive period)", e);
+        st->bytes_step += st->adapt ? states * 8 : 0;
     }
     if ((e = hipMemcpyAsync(st->d_map, st->map.data(), sizeof(int32_t) * st->map.size(),
                             hipMemcpyHostToDevice, s)) != hipSuccess)
@@ -249,6 +262,8 @@ PACE_API int pace_state_alloc(const pace_config *cfg, int init_kind, const void 
         if ((e = hipMemcpyAsync(st->scales, src, st->bytes_scales, hipMemcpyDeviceToDevice, s)) != hipSuccess)
             return cleanup(0, "raw copy scales", e);
     }
+    if (st->adapt && (e = pace::launch_adapt_init(st->view(), st->adapt, s)) != hipSuccess)
+        return cleanup(0, "adaptive period init", e);
     // the host copy of the head map must outlive the async copy: wait for it
     if ((e = hipStreamSynchronize(s)) != hipSuccess) return cleanup(0, "initialisation", e);
     *out = st;
@@ -268,6 +283,7 @@ PACE_API int pace_state_free(pace_state *st) {
     if (st->step_kv) (void)hipFree(st->step_kv);
     if (st->step_ab) (void)hipFree(st->step_ab);
     if (st->step_fill) (void)hipFree(st->step_fill);
+    if (st->adapt) (void)hipFree(st->adapt);
     delete st;
     if (e != hipSuccess) return hip_fail(e, "pace_state_free");
     return ok();
@@ -366,6 +382,13 @@ PACE_API int pace_read_state(const pace_state *st, int what, void *dst, float *s
         d += st->bytes8;
         if (e == hipSuccess)
             e = hipMemcpyAsync(d, st->scales, st->bytes_scales, hipMemcpyDeviceToDevice, s);
+    } else if (what == PACE_READ_STEP) {
+        if (!st->stepped()) return fail(PACE_EINVAL, "PACE_READ_STEP needs a PACE_STEP_BUFFER handle");
+        const size_t states = (size_t)st->cfg.batch * st->cfg.heads;
+        e = hipMemcpyAsync(dst, st->step_fill, states * 4, hipMemcpyDeviceToDevice, s);
+        if (e == hipSuccess && scales_dst)
+            e = st->adapt ? hipMemcpyAsync(scales_dst, st->adapt, states * 8, hipMemcpyDeviceToDevice, s)
+                          : hipMemsetAsync(scales_dst, 0, states * 8, s);
     } else {
         return fail(PACE_EINVAL, "unknown read kind %d", what);
     }

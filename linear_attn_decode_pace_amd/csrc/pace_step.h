@@ -13,13 +13,19 @@ struct StepView {
     int32_t *fill;          // [B * H]: tokens buffered per state (0 .. slots)
     const uint8_t *active;  // device [B], or NULL: sequences taking a token this step
     int slots;              // period - 1
-    int period;
+    int period;             // the maximum period when adaptive
+    // adaptive period (tau > 0): per state A (summed write norms of the
+    // buffered tokens) and R (norm of the stored state at its last encode)
+    float *adapt;           // [B * H][2], or NULL when tau == 0
+    float tau;              // 0: fixed period
 };
 
 hipError_t launch_step_v0(const PoolView &p, const StepView &sv, const void *q, const void *k,
                           const void *v, const float *alpha, const float *beta, float *out,
                           int in_bf16, hipStream_t s);
 hipError_t launch_flush_v0(const PoolView &p, const StepView &sv, int in_bf16, hipStream_t s);
+// adapt[2 t] = 0, adapt[2 t + 1] = ||decode(stored state t)||_F for every state
+hipError_t launch_adapt_init(const PoolView &p, float *adapt, hipStream_t s);
 
 // True when the fused kernel covers a step of this shape (rows_per_token = B * H).
 bool mfma_step_supported(int dk, int dv, int period, int in_bf16, long long rows_per_token);

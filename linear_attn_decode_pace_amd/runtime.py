@@ -54,12 +54,14 @@ class State:
 
     def __init__(self, w: inputs.Workload, head_bits: Sequence[int],
                  init_kind: int = pace.PACE_INIT_ZERO, init: Optional[torch.Tensor] = None,
-                 period: Optional[int] = None, stream=None, flags: int = 0):
+                 period: Optional[int] = None, stream=None, flags: int = 0,
+                 adapt_tau: float = 0.0):
         self.w = w
         self.head_bits = np.asarray(head_bits, dtype=np.uint8)
         self.period = w.period if period is None else period
         self.handle = pace.pace_state_alloc(w.B, w.H, w.dk, w.dv, self.period, dtype_code(w),
-                                            list(self.head_bits), init_kind, init, flags, stream)
+                                            list(self.head_bits), init_kind, init, flags, stream,
+                                            adapt_tau)
 
     def free(self):
         if self.handle:
@@ -87,6 +89,14 @@ class State:
 
     def flush_steps(self, stream=None):
         pace.pace_flush_steps(self.handle, stream)
+
+    def read_step(self, stream=None):
+        """Buffered tokens per state [B, H] (int32) and (A, R) [B, H, 2]."""
+        w = self.w
+        fill = torch.empty((w.B, w.H), dtype=torch.int32, device="cuda")
+        ar = torch.empty((w.B, w.H, 2), dtype=torch.float32, device="cuda")
+        pace.pace_read_state(self.handle, pace.PACE_READ_STEP, fill, ar, stream)
+        return fill, ar
 
     def read_codes(self, stream=None):
         w = self.w

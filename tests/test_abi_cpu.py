@@ -40,7 +40,8 @@ def _alloc_status(init_kind=pace.PACE_INIT_ZERO, init=None, flags=0, **kw):
     c = _cfg(**kw)
     hb = (ctypes.c_uint8 * max(1, len(c["head_bits"])))(*c["head_bits"])
     cfg = pace.pace_config(c["batch"], c["heads"], c["d_k"], c["d_v"], c["period"], c["in_dtype"],
-                           ctypes.cast(hb, ctypes.POINTER(ctypes.c_uint8)), flags)
+                           ctypes.cast(hb, ctypes.POINTER(ctypes.c_uint8)), flags,
+                           c.get("adapt_tau", 0.0))
     out = ctypes.c_void_p()
     return pace.LIB.pace_state_alloc(ctypes.byref(cfg), init_kind, init, None, ctypes.byref(out))
 
@@ -62,7 +63,11 @@ def test_alloc_rejects_bad_config(kw, status):
 
 
 def test_alloc_rejects_bad_flags():
-    assert _alloc_status(flags=4) == pace.PACE_EINVAL
+    assert _alloc_status(flags=8) == pace.PACE_EINVAL
+    assert _alloc_status(flags=pace.PACE_ADAPTIVE, adapt_tau=0.5) == pace.PACE_EINVAL   # needs steps
+    both = pace.PACE_ADAPTIVE | pace.PACE_STEP_BUFFER
+    for tau in (0.0, -1.0, float("inf"), float("nan")):
+        assert _alloc_status(flags=both, adapt_tau=tau) == pace.PACE_EINVAL
     many = pace.PACE_STATS_MAX_HEADS + 1
     assert _alloc_status(flags=pace.PACE_STATS_ERR, heads=many, head_bits=[4] * many) == pace.PACE_EINVAL
     assert "PACE_STATS_ERR" in pace.pace_last_error()

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 from linear_attn_decode_pace_amd import inputs
-from oracle import buffered
+from oracle import buffered, quant
 from tests import parity
 from tests.gpu_cases import say, tok_tiles
 
@@ -148,3 +148,91 @@ def test_step_and_period_calls_are_exclusive():
         pace.pace_flush_steps(per.handle)
     per.free()
     stp.free()
+
+
+ADAPT_CASES = [
+    ("adapt-k8", dict(B=3, H=5, n_int8=2, n_outliers=8, period=8, steps=40), 1.0, False),   # fused
+    ("adapt-k8-mask", dict(B=3, H=5, n_int8=2, n_outliers=8, period=8, steps=40), 2.5, True),
+    ("adapt-d64", dict(B=4, H=4, dk=64, dv=64, n_int8=1, period=8, steps=32), 1.0, False),
+    ("adapt-f32", dict(B=2, H=3, n_int8=1, dtype=inputs.DT_F32, period=6, steps=30), 1.0, True),  # per-column
+]
+
+
+@pytest.mark.parametrize("name,kw,tau,masked", ADAPT_CASES)
+def test_adaptive_period_against_buffered_oracle(name, kw, tau, masked):
+    # adaptive period (PACE_ADAPTIVE): every step's close decision, outputs,
+    # encodes and the per-state (A, R) against the oracle; a decision may
+    # differ only where the oracle's A sits within 1e-4 of tau R, and then the
+    # oracle follows the GPU
+    import torch
+    from linear_attn_decode_pace_amd import pace, runtime
+    w = inputs.ragged(name, 230, **kw)
+    seed = 0
+    say(f"[case] adaptive period {name} tau={tau}")
+    n = w.B * w.H
+    idx = np.arange(n)
+    bits = inputs.head_bits(w, seed)
+    bits_t = np.tile(bits, w.B).astype(np.int64)
+    st = runtime.State(w, bits, pace.PACE_INIT_F32, runtime.warmup_state(w, seed),
+                       flags=pace.PACE_STEP_BUFFER | pace.PACE_ADAPTIVE, adapt_tau=tau)
+
+    def read():
+        c, s = st.read_codes()
+        f, ar = st.read_step()
+        return (c.reshape(n, w.dk, w.dv).cpu().numpy(), s.reshape(n, w.dv).cpu().numpy(),
+                f.reshape(n).cpu().numpy(), ar.reshape(n, 2).cpu().numpy().astype(np.float64))
+
+    codes, scales, fill, ar = read()
+    ref = buffered.Buffered(codes, scales, bits_t, w.period, tau=tau)
+    np.testing.assert_allclose(ar[:, 1], ref.R, rtol=1e-5)
+    assert np.all(fill == 0) and np.all(ar[:, 0] == 0)
+    rng = np.random.default_rng(6)
+    lengths, near = [], 0
+    for t in range(w.steps):
+        act = rng.uniform(size=w.B) < 0.7 if masked else np.ones(w.B, dtype=bool)
+        if t < 2:
+            act[:] = True
+        act_t = np.repeat(act, w.H)
+        expect = np.array([ref.closes(i) for i in range(n)])
+        marg = np.array([abs(ref.margin(i)) if ref.tau * ref.R[i] > 0 else np.inf for i in range(n)])
+        fill_before = ref.fill
+        tok = inputs.tokens(w, seed, inputs.SEG_DECODE, t, t + 1)
+        out = runtime.out_buffer(w, 1).fill_(np.nan)
+        st.step(runtime.DeviceTokens(tok), out, torch.as_tensor(act.astype(np.uint8), device="cuda"))
+        nc, ns, nfill, nar = read()
+        closed = act_t & (nfill == 0)
+        bad = act_t & (closed != expect) & (marg >= 1e-4)
+        assert not bad.any(), f"{name} step {t}: close decisions differ at {np.nonzero(bad)[0]}"
+        near += int((act_t & (closed != expect)).sum())
+        q, k, v, a, b = [x[0] for x in tok_tiles(tok, idx, w.H)]
+        o_ref = ref.step(q, k, v, a, b, act_t, decide=closed)
+        o = out.reshape(n, w.dv).cpu().numpy()
+        assert np.all(np.isnan(o[~act_t]))
+        if act_t.any():
+            parity.check_outputs(o[act_t][None], o_ref[act_t][None], f"{name} step {t}")
+        np.testing.assert_array_equal(nfill, ref.fill)
+        if closed.any():
+            lengths += (fill_before[closed] + 1).tolist()
+            pre = np.stack([ref.last_pre[i] for i in np.nonzero(closed)[0]])
+            parity.check_encoded(nc[closed], ns[closed], ref.codes[closed], ref.scales[closed], pre,
+                                 f"{name} step {t} encode")
+            ref.codes[closed], ref.scales[closed] = nc[closed], ns[closed]
+            for i in np.nonzero(closed)[0]:
+                ref.R[i] = ref._norm(i)
+        np.testing.assert_array_equal(nc, ref.codes)
+        np.testing.assert_allclose(nar[:, 1], ref.R, rtol=1e-5)
+        np.testing.assert_allclose(nar[:, 0], ref.A, rtol=1e-4, atol=1e-6 * ref.R.max())
+    say(f"[case] {name}: period lengths {np.bincount(lengths).tolist()}, {near} decisions on the threshold")
+    assert len(set(lengths)) > 1   # the period really adapts
+    partial = ref.fill > 0
+    st.flush_steps()
+    ref.flush()
+    nc, ns, nfill, nar = read()
+    assert np.all(nfill == 0) and np.all(nar[:, 0] == 0)
+    if partial.any():
+        pre = np.stack([ref.last_pre[i] for i in np.nonzero(partial)[0]])
+        parity.check_encoded(nc[partial], ns[partial], ref.codes[partial], ref.scales[partial], pre,
+                             f"{name} flush")
+    # R is the norm of what the GPU stored (tie flips of the flush included)
+    np.testing.assert_allclose(nar[:, 1], np.linalg.norm(quant.decode(nc, ns), axis=(1, 2)), rtol=1e-5)
+    st.free()
