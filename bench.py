@@ -144,15 +144,95 @@ def cpu_baseline(w, seed, warm_tok, periods_tok, head_bits, n_seq):
             "seconds": dt}
 
 
+def prefill_bytes(w: inputs.Workload, n_tok: int, head_bits) -> int:
+    """Bytes of one prefill call at minimum: the prompt's q/k/v/alpha/beta read
+    once, its float32 outputs written once, every code and scale read and
+    written once."""
+    e_in = 2 if w.dtype == inputs.DT_BF16 else 4
+    state = sum(w.dk * w.dv * int(b) // 8 + 4 * w.dv for b in head_bits)
+    per_tok = w.H * ((w.dk * 2 + w.dv) * e_in + 8 + 4 * w.dv)
+    return w.B * (2 * state + n_tok * per_tok)
+
+
+def bench_prefill(args) -> int:
+    """Time pace_prefill_encode over whole prompts (the hand-off workload)."""
+    import torch
+
+    from linear_attn_decode_pace_amd import pace, runtime
+
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only", file=sys.stderr)
+        return 2
+    w = inputs.WORKLOADS[args.workload]
+    T = w.prompt
+    if not T:
+        raise SystemExit(f"{w.name} has no prompt; use --workload prefill-b512")
+    torch.cuda.set_device(0)
+    head_bits = inputs.head_bits(w, args.seed)
+    D = min(T, args.prompt_distinct)
+    t = time.time()
+    blocks = generate(w, args.seed, [(inputs.SEG_PROMPT, t0, min(D, t0 + 64)) for t0 in range(0, D, 64)],
+                      args.workers)
+    log(f"generated {D} distinct prompt tokens in {time.time() - t:.1f} s")
+    # device prompt [T, B, H, d]: the D generated tokens repeated to length T
+    small = runtime.DeviceTokens(inputs.concat(blocks))
+    big = runtime.DeviceTokens.__new__(runtime.DeviceTokens)
+    for name in ("q", "k", "v", "alpha", "beta"):
+        x = getattr(small, name)
+        y = torch.empty((T,) + tuple(x.shape[1:]), dtype=x.dtype, device="cuda")
+        for t0 in range(0, T, D):
+            y[t0:t0 + D].copy_(x[:min(D, T - t0)])
+        setattr(big, name, y)
+    big.T = T
+    del small
+    out = runtime.out_buffer(w, T)
+    st = runtime.State(w, head_bits, pace.PACE_INIT_ZERO)
+    torch.cuda.synchronize()
+    log(f"prompt resident: {big.nbytes / 1e9:.1f} GB inputs, {out.numel() * 4 / 1e9:.1f} GB outputs")
+    for _ in range(max(1, args.warmup)):
+        st.prefill(big, out)
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        ev[i][0].record()
+        st.prefill(big, out)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / K
+    nbytes = prefill_bytes(w, T, head_bits)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "prefill prompt tokens/s into the quantized state (seqs x prompt tokens)",
+        "value": w.B * T / (ms * 1e-3), "unit": "token-steps/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "mode": "prefill", "batch": w.B, "heads": w.H,
+                   "d_k": w.dk, "d_v": w.dv, "prompt_tokens": T, "distinct_prompt_tokens": D,
+                   "heads_int8": int((head_bits == 8).sum()), "inputs": w.dtype},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": nbytes, "launch_ms": ms},
+        "cpu_baseline": None,
+    }
+    st.free()
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=inputs.HEADLINE.name, choices=sorted(inputs.WORKLOADS))
-    ap.add_argument("--mode", default="period", choices=("period", "step"),
+    ap.add_argument("--mode", default="period", choices=("period", "step", "prefill"),
                     help="period: one call per period of k tokens; step: one call per token "
-                         "(PACE_STEP_BUFFER handle), every sequence active")
+                         "(PACE_STEP_BUFFER handle), every sequence active; prefill: one "
+                         "pace_prefill_encode call per prompt (the workload's prompt length)")
+    ap.add_argument("--prompt-distinct", type=int, default=256,
+                    help="prefill mode: distinct prompt tokens generated on the host; the "
+                         "device prompt repeats them to the full length")
     ap.add_argument("--adapt-tau", type=float, default=0.0,
                     help="step mode: adaptive period with this threshold (the workload's period "
                          "is the maximum)")
@@ -167,6 +247,8 @@ def main() -> int:
                     help="also run a plain 1 GiB device-to-device copy (profiler traffic calibration)")
     args = ap.parse_args()
 
+    if args.mode == "prefill":
+        return bench_prefill(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): every (sequence, head) "
               "state is independent, so this layer needs no collective; the single-GPU figure "

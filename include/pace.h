@@ -267,6 +267,26 @@ int pace_read_state(const pace_state *st, int what, void *dst, float *scales_dst
 int pace_quant_stats(const pace_state *st, pace_stats *out, void *stream);
 
 /*
+ * Prefill hand-off: apply a prompt of n_tok tokens (any n_tok >= 1) to every
+ * stored state and encode once at the end, i.e. one period of n_tok tokens
+ * (the stored state decoded -- zero after PACE_INIT_ZERO --, the tokens
+ * applied in order in float32, per-column re-encode).  Chunked kernels keep
+ * the state in high precision across a prompt chunk; this keeps it across
+ * the whole prompt and rounds once ('PACE: four-bit recurrent state by
+ * rounding less often', TL;DR point (1)).
+ *   q, k:  device [n_tok, B, H, d_k]; v: device [n_tok, B, H, d_v]; in_dtype,
+ *          16-byte aligned.  alpha, beta: device float32 [n_tok, B, H].
+ *   out:   device float32 [n_tok, B, H, d_v] (16-byte aligned), or NULL.
+ * bf16 inputs with d_k = d_v = 64 or 128 run the fused kernel (the state stays
+ * on chip for the whole prompt); other shapes run the per-column kernel.
+ * Errors: EINVAL (null or misaligned pointer, n_tok < 1, a PACE_STEP_BUFFER
+ *         handle), EDEVICE.
+ */
+int pace_prefill_encode(pace_state *st, int32_t n_tok, const void *q, const void *k,
+                        const void *v, const float *alpha, const float *beta, float *out,
+                        void *stream);
+
+/*
  * Unquantized float32 gated delta rule over n_tok tokens, in place on a dense
  * float32 state: used to build the state that decode starts from (warm-up
  * tokens, or a prompt streamed in blocks).  The chunked-prefill motivation of

@@ -12,7 +12,8 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libpace.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["pace_abi.cpp", "kernels_v0.hip", "decode_mfma.hip", "decode_mfma16.hip"]
+SOURCES = ["pace_abi.cpp", "kernels_v0.hip", "decode_mfma.hip", "decode_mfma16.hip",
+           "prefill_mfma.hip"]
 ARCH = "gfx950"
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

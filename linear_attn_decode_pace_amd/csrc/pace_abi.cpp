@@ -13,6 +13,7 @@
 #include "../../include/pace.h"
 #include "pace_layout.h"
 #include "pace_mfma.h"
+#include "pace_prefill.h"
 #include "pace_step.h"
 
 #define PACE_API extern "C" __attribute__((visibility("default")))
@@ -323,6 +324,30 @@ PACE_API int pace_decode_period(pace_state *st, int32_t n_tok, const void *q, co
     else
         e = pace::launch_decode_v0(st->view(), n_tok, q, k, v, alpha, beta, out, bf16, s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
+    st->periods += 1;
+    st->tokens += (uint64_t)n_tok;
+    return ok();
+}
+
+PACE_API int pace_prefill_encode(pace_state *st, int32_t n_tok, const void *q, const void *k,
+                                 const void *v, const float *alpha, const float *beta,
+                                 float *out, void *stream) {
+    if (!st) return fail(PACE_EINVAL, "null state handle");
+    if (st->stepped())
+        return fail(PACE_EINVAL, "a PACE_STEP_BUFFER handle decodes with pace_decode_step");
+    if (n_tok < 1) return fail(PACE_EINVAL, "n_tok must be >= 1");
+    int rc = check_tokens(n_tok, st->cfg.in_dtype, q, k, v, alpha, beta);
+    if (rc) return rc;
+    if (out && !aligned(out, 16)) return fail(PACE_EINVAL, "out must be 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    const int bf16 = st->cfg.in_dtype == PACE_DTYPE_BF16;
+    hipError_t e;
+    if (pace::prefill_mfma_supported(st->cfg.d_k, st->cfg.d_v, bf16,
+                                     (long long)st->cfg.batch * st->cfg.heads))
+        e = pace::launch_prefill_mfma(st->view(), n_tok, q, k, v, alpha, beta, out, s);
+    else
+        e = pace::launch_decode_v0(st->view(), n_tok, q, k, v, alpha, beta, out, bf16, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill launch");
     st->periods += 1;
     st->tokens += (uint64_t)n_tok;
     return ok();

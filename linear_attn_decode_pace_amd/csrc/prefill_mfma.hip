@@ -1,0 +1,409 @@
+// Prompt prefill into the quantized state (gfx950): a period of n_tok tokens,
+// any n_tok >= 1, applied to every (sequence, head) state in float32 and
+// encoded once at the end (the prefill hand-off: chunked kernels already keep
+// the state in high precision across a chunk, and periodic rounding extends
+// that to decode: 'PACE: four-bit recurrent state by rounding less often',
+// TL;DR point (1)).
+//
+// One workgroup per state tile, resident for the whole prompt:
+//   * NCB consumer waves (one per 16-column block) hold the tile's float32
+//     state in MFMA accumulator layout (the same lane -> (row, column) map as
+//     the pool layout) from the first token to the final encode;
+//   * one producer wave stages chunk c+1's 16 tokens in LDS and computes the
+//     chunk's token-only matrices (Gram products, gates, UT solve, Lq T)
+//     while the consumers apply chunk c: double-buffered LDS, one workgroup
+//     barrier per chunk.
+// Per chunk and column block (WY / UT form, as the decode kernels):
+//   P = [K; Q] M0 with M0 split exactly enough into three bf16 parts
+//   (hi + mid + lo) so the products keep float32 accuracy; X = V - diag(g) K M0,
+//   Y = diag(g) Q M0; W = diag(G_C) T X and O = Lq T X + Y on float32 MFMA;
+//   M <- g_C M + K^T W (bf16 MFMA, W in three parts).
+// Outputs of a chunk go through LDS and leave as whole 512-byte rows.
+#include "mfma_common.h"
+#include "pace_prefill.h"
+
+namespace pace {
+namespace {
+
+constexpr int CT = 16;      // tokens per chunk
+constexpr int PROW = 136;   // bf16 elements per LDS token row (128 + 8 padding)
+constexpr int OPAD = 132;   // floats per LDS output row
+
+struct alignas(16) ChunkLds {
+    uint16_t kq[2 * CT][PROW];  // rows 0..15: k_t, rows 16..31: q_t (bf16 bits)
+    uint16_t v[CT][PROW];
+    float Tt[CT][CT];   // Tt[s][t] = T[t][s]
+    float LqT[CT][CT];  // (Lq T)[t][s]
+    float gam[CT];      // gamma_t inside the chunk
+    float gamC[CT];     // Gamma_{C-1, t}
+    int n_valid;        // real tokens of the chunk (the rest are identity padding)
+};
+
+struct alignas(16) PrepScratch {
+    float alpha[CT], beta[CT];
+    float kk[CT][CT], qk[CT][CT];
+    float A[CT][CT], Lq[CT][CT];
+};
+
+template <int DK>
+struct PrefillLds {
+    ChunkLds ch[2];
+    PrepScratch ps;
+    alignas(16) float o[CT][OPAD];
+};
+
+struct PrefillArgs {
+    PoolView p;
+    const uint16_t *q, *k, *v;
+    const float *alpha, *beta;
+    float *out;  // NULL: no outputs
+    int n_tok;
+    int tiles;
+};
+
+// Producer: stage chunk `c` and compute its token-only matrices into L.
+template <int DK>
+__device__ void prep_chunk(const PrefillArgs &a, ChunkLds &L, PrepScratch &S, size_t tile_row,
+                           int c, int lane) {
+    constexpr int NKS = DK / 32;
+    const int g = lane >> 4, n = lane & 15;
+    const uint32_t tok_stride = (uint32_t)a.p.B * (uint32_t)a.p.H;
+    const int t0 = CT * c, nv = min(CT, a.n_tok - t0);
+    {
+        constexpr int CPR = DK / 8;             // 16-byte chunks per token row
+        constexpr int NL = 3 * CT * CPR / 64;   // loads per lane
+        const size_t base = ((size_t)t0 * tok_stride + tile_row) * DK;
+        const uint16_t *srcs[3] = {a.k + base, a.q + base, a.v + base};
+        u32x4 val[NL];
+#pragma unroll
+        for (int it = 0; it < NL; ++it) {
+            const int e = lane + 64 * it;
+            const int row = e / CPR, col = (e % CPR) * 8;
+            const int t = row & 15, which = row >> 4;
+            val[it] = u32x4{0u, 0u, 0u, 0u};
+            if (t < nv)
+                val[it] = __builtin_nontemporal_load(
+                    at((const u32x4 *)srcs[which], (uint32_t)(t * tok_stride * DK + col) * 2u));
+        }
+        float ab = 0.f;
+        if (lane < 32) {
+            const int t = lane & 15;
+            const bool is_beta = lane >= 16;
+            ab = is_beta ? 0.f : 1.f;
+            if (t < nv)
+                ab = (is_beta ? a.beta : a.alpha)[((size_t)t0 + t) * tok_stride + tile_row];
+        }
+#pragma unroll
+        for (int it = 0; it < NL; ++it) {
+            const int e = lane + 64 * it;
+            const int row = e / CPR, col = (e % CPR) * 8;
+            const int t = row & 15, which = row >> 4;
+            uint16_t *dst = which < 2 ? &L.kq[which * 16 + t][col] : &L.v[t][col];
+            *(u32x4 *)dst = val[it];
+        }
+        if (lane < 32) (lane >= 16 ? S.beta : S.alpha)[lane & 15] = ab;
+        if (lane == 0) L.n_valid = nv;
+    }
+    wave_sync();
+
+    // Gram products on MFMA: A row m of the K (Q) block is token 4 (m % 4) + m / 4
+    {
+        const int tok_n = 4 * (n & 3) + (n >> 2);
+        f32x4 GK = {0.f, 0.f, 0.f, 0.f}, GQ = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int c0 = 32 * ks + 4 * g, c1 = c0 + 16;
+            const u32x2 k0 = *(const u32x2 *)&L.kq[tok_n][c0], k1 = *(const u32x2 *)&L.kq[tok_n][c1];
+            const u32x2 q0 = *(const u32x2 *)&L.kq[16 + tok_n][c0], q1 = *(const u32x2 *)&L.kq[16 + tok_n][c1];
+            const u32x2 s0 = *(const u32x2 *)&L.kq[n][c0], s1 = *(const u32x2 *)&L.kq[n][c1];
+            const bf16x8 BG = __builtin_bit_cast(bf16x8, u32x4{s0[0], s0[1], s1[0], s1[1]});
+            GK = mfma_bf16_k32(__builtin_bit_cast(bf16x8, u32x4{k0[0], k0[1], k1[0], k1[1]}), BG, GK);
+            GQ = mfma_bf16_k32(__builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]}), BG, GQ);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            S.kk[4 * r + g][n] = GK[r];
+            S.qk[4 * r + g][n] = GQ[r];
+        }
+    }
+    wave_sync();
+
+    // gates as products of alpha; A (strictly lower) and Lq (lower incl. diagonal)
+    {
+        float al[CT];
+#pragma unroll
+        for (int r = 0; r < CT; ++r) al[r] = S.alpha[r];
+        const int t = lane >> 2, s0 = 4 * (lane & 3);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int s = s0 + e;
+            float gts = 1.f;
+#pragma unroll
+            for (int r = 1; r < CT; ++r) gts *= (r > s && r <= t) ? al[r] : 1.f;
+            S.A[t][s] = s < t ? gts * S.kk[t][s] : 0.f;
+            S.Lq[t][s] = s <= t ? gts * S.qk[t][s] : 0.f;
+        }
+        if (lane < CT) {
+            float gm = 1.f, gc = 1.f;
+#pragma unroll
+            for (int r = 0; r < CT; ++r) {
+                gm *= r <= lane ? al[r] : 1.f;
+                gc *= r > lane ? al[r] : 1.f;
+            }
+            L.gam[lane] = gm;
+            L.gamC[lane] = gc;
+        }
+    }
+    wave_sync();
+
+    // UT transform: column s of (I + diag(beta) A)^-1 by forward substitution
+    {
+        const int s = lane & 15;
+        float be[CT], z[CT];
+#pragma unroll
+        for (int r = 0; r < CT; ++r) be[r] = S.beta[r];
+#pragma unroll
+        for (int t = 0; t < CT; ++t) {
+            float sum = 0.f;
+#pragma unroll
+            for (int u = 0; u < t; ++u) sum = fmaf(S.A[t][u], z[u], sum);
+            z[t] = (t == s ? 1.f : 0.f) - be[t] * sum;
+        }
+        if (lane < CT) {
+#pragma unroll
+            for (int t = 0; t < CT; ++t) L.Tt[s][t] = z[t] * be[s];
+        }
+    }
+    wave_sync();
+
+    // Lq T: lane -> row t = lane / 4, columns s = 4 (lane % 4) + e
+    {
+        const int t = lane >> 2, s0 = 4 * (lane & 3);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float r2 = 0.f;
+#pragma unroll
+            for (int u = 0; u < CT; ++u) r2 = fmaf(S.Lq[t][u], L.Tt[s0 + e][u], r2);
+            L.LqT[t][s0 + e] = r2;
+        }
+    }
+}
+
+// bf16 parts (hi, mid, lo) of the four floats x[0..3], as two packed dwords each
+__device__ inline void split3(const f32x4 &x, uint32_t hi[2], uint32_t md[2], uint32_t lo[2]) {
+    hi[0] = pk_bf16(x[0], x[1]);
+    hi[1] = pk_bf16(x[2], x[3]);
+    const float r0 = x[0] - lo_f32(hi[0]), r1 = x[1] - hi_f32(hi[0]);
+    const float r2 = x[2] - lo_f32(hi[1]), r3 = x[3] - hi_f32(hi[1]);
+    md[0] = pk_bf16(r0, r1);
+    md[1] = pk_bf16(r2, r3);
+    lo[0] = pk_bf16(r0 - lo_f32(md[0]), r1 - hi_f32(md[0]));
+    lo[1] = pk_bf16(r2 - lo_f32(md[1]), r3 - hi_f32(md[1]));
+}
+
+template <int DK, int BITS, bool ERR>
+__device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int h, int slot,
+                             int wave, int lane) {
+    constexpr int NKS = DK / 32;  // k-slices of 32 rows
+    constexpr int NRT = DK / 16;  // row tiles of 16 rows
+    constexpr int NCB = DK / 16;  // column blocks = consumer waves
+    constexpr float QMAX = BITS == 4 ? 7.f : 127.f;
+    constexpr float KAPPA = Loader<DK, BITS>::KAPPA;
+    const int g = lane >> 4, n = lane & 15;
+    const size_t tile_row = (size_t)b * a.p.H + h;
+    const uint32_t tok_stride = (uint32_t)a.p.B * (uint32_t)a.p.H;
+    const int n_chunks = (a.n_tok + CT - 1) / CT;
+    const bool producer = wave == NCB;
+    const int cb = wave, j = 16 * cb + n;
+
+    uint8_t *codes = BITS == 4
+        ? a.p.codes4 + ((size_t)b * a.p.n4 + slot) * tile_code_bytes(DK, DK, 4)
+        : a.p.codes8 + ((size_t)b * a.p.n8 + slot) * tile_code_bytes(DK, DK, 8);
+    float *scl = a.p.scales + tile_row * DK;
+
+    // the column block's starting state: the stored codes decoded (zero after
+    // a zero initialisation)
+    f32x4 acc[NRT];
+    if (!producer) {
+        Loader<DK, BITS> ld;
+        ld.load(codes, cb, lane);
+        ld.codes_f32(acc);
+        const float sk = scl[j] * (1.f / KAPPA);
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) acc[rt] *= sk;
+    }
+    if (producer) prep_chunk<DK>(a, L.ch[0], L.ps, tile_row, 0, lane);
+    __syncthreads();
+
+    const int tok_n = 4 * (n & 3) + (n >> 2);
+    for (int c = 0; c < n_chunks; ++c) {
+        ChunkLds &C = L.ch[c & 1];
+        if (producer) {
+            if (c + 1 < n_chunks) prep_chunk<DK>(a, L.ch[(c + 1) & 1], L.ps, tile_row, c + 1, lane);
+        } else {
+            // P = [K; Q] M0 over three bf16 parts of M0
+            f32x4 PK = {0.f, 0.f, 0.f, 0.f}, PQ = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int c0 = 32 * ks + 4 * g, c1 = c0 + 16;
+                const u32x2 k0 = *(const u32x2 *)&C.kq[tok_n][c0], k1 = *(const u32x2 *)&C.kq[tok_n][c1];
+                const u32x2 q0 = *(const u32x2 *)&C.kq[16 + tok_n][c0], q1 = *(const u32x2 *)&C.kq[16 + tok_n][c1];
+                const bf16x8 AK = __builtin_bit_cast(bf16x8, u32x4{k0[0], k0[1], k1[0], k1[1]});
+                const bf16x8 AQ = __builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]});
+                uint32_t h0[2], m0[2], l0[2], h1[2], m1[2], l1[2];
+                split3(acc[2 * ks], h0, m0, l0);
+                split3(acc[2 * ks + 1], h1, m1, l1);
+                const bf16x8 BH = __builtin_bit_cast(bf16x8, u32x4{h0[0], h0[1], h1[0], h1[1]});
+                const bf16x8 BM = __builtin_bit_cast(bf16x8, u32x4{m0[0], m0[1], m1[0], m1[1]});
+                const bf16x8 BL = __builtin_bit_cast(bf16x8, u32x4{l0[0], l0[1], l1[0], l1[1]});
+                PK = mfma_bf16_k32(AK, BH, PK);
+                PQ = mfma_bf16_k32(AQ, BH, PQ);
+                PK = mfma_bf16_k32(AK, BM, PK);
+                PQ = mfma_bf16_k32(AQ, BM, PQ);
+                PK = mfma_bf16_k32(AK, BL, PK);
+                PQ = mfma_bf16_k32(AQ, BL, PQ);
+            }
+            // X, Y for tokens 4 r + g (the P rows this lane holds)
+            float X[4], Y[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float gm = C.gam[4 * r + g];
+                X[r] = fmaf(-gm, PK[r], bf2f(C.v[4 * r + g][j]));
+                Y[r] = gm * PQ[r];
+            }
+            // W (rows = tokens) and O on float32 MFMA; step st takes token 4 st + g
+            f32x4 W = {0.f, 0.f, 0.f, 0.f}, O = {0.f, 0.f, 0.f, 0.f};
+            const float gct = C.gamC[n];
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const int s = 4 * st + g;
+                W = mfma_f32_k4(gct * C.Tt[s][n], X[st], W);
+                O = mfma_f32_k4(C.LqT[n][s], X[st], O);
+            }
+#pragma unroll
+            for (int st = 0; st < 4; ++st) O = mfma_f32_k4(n == 4 * st + g ? 1.f : 0.f, Y[st], O);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) L.o[4 * g + r][j] = O[r];
+
+            // M <- gamma_C M + K^T W, W in three bf16 parts (tokens 4 g + e)
+            const float gC = C.gam[CT - 1];
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) acc[rt] *= gC;
+            uint32_t wh[2], wm[2], wl[2];
+            split3(W, wh, wm, wl);
+            const s16x4 BH = __builtin_bit_cast(s16x4, u32x2{wh[0], wh[1]});
+            const s16x4 BM = __builtin_bit_cast(s16x4, u32x2{wm[0], wm[1]});
+            const s16x4 BL = __builtin_bit_cast(s16x4, u32x2{wl[0], wl[1]});
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) {
+                const int i = 16 * rt + n;
+                s16x4 au;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) au[e] = (short)C.kq[4 * g + e][i];
+                acc[rt] = mfma_bf16_k16(au, BH, acc[rt]);
+                acc[rt] = mfma_bf16_k16(au, BM, acc[rt]);
+                acc[rt] = mfma_bf16_k16(au, BL, acc[rt]);
+            }
+        }
+        __syncthreads();  // chunk c+1 staged, chunk c's outputs complete
+        if (a.out) {
+            // every wave helps flush: rows of DK floats, 16 bytes per lane
+            constexpr int PER_ROW = DK / 4;
+            const int e = wave * 64 + lane;
+            const int t = e / PER_ROW, c4 = (e % PER_ROW) * 4;
+            if (t < C.n_valid) {
+                const f32x4 x = *(const f32x4 *)&L.o[t][c4];
+                __builtin_nontemporal_store(
+                    x, (f32x4 *)(a.out + (((size_t)CT * c + t) * tok_stride + tile_row) * DK + c4));
+            }
+        }
+        __syncthreads();  // the output staging is free again
+    }
+
+    // ---- encode each column block once: absmax, scale, codes ----
+    if (!producer) {
+        float am = 0.f;
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) am = fmaxf(am, fabsf(acc[rt][r]));
+        am = xor_max(am, 16);
+        am = xor_max(am, 32);
+        const float s_new = am * (1.f / QMAX);
+        const float ratio = s_new > 0.f ? __builtin_amdgcn_rcpf(s_new) : 0.f;
+        uint32_t y[NRT][4];
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y[rt][r] = __float_as_uint(fmaf(acc[rt][r], ratio, 12582912.f));
+        Loader<DK, BITS> outc;
+        if constexpr (BITS == 4) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const uint32_t lo = gather_low_bytes(y[2 * ks][0], y[2 * ks][1], y[2 * ks][2], y[2 * ks][3]);
+                const uint32_t hi = gather_low_bytes(y[2 * ks + 1][0], y[2 * ks + 1][1],
+                                                     y[2 * ks + 1][2], y[2 * ks + 1][3]);
+                outc.d[ks] = (lo & 0x0f0f0f0fu) | ((hi << 4) & 0xf0f0f0f0u);
+            }
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) outc.d[rt] = gather_low_bytes(y[rt][0], y[rt][1], y[rt][2], y[rt][3]);
+        }
+        outc.store(codes, cb, lane);
+        if (g == 0) scl[j] = s_new;
+        if constexpr (ERR) column_error<NRT>(acc, y, 1.f, s_new, a.p.colerr + (tile_row * DK + j) * 2, g);
+    }
+}
+
+template <int DK, bool ERR>
+__global__ void __launch_bounds__(64 * (DK / 16 + 1)) prefill_mfma_kernel(PrefillArgs a) {
+    __shared__ PrefillLds<DK> L;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int w = blockIdx.x;  // one tile per workgroup, sequence-major
+    const int b = w / a.p.H, h = w - b * a.p.H;
+    const int m = a.p.head_map[h];
+    if ((m >> 16) == 8)
+        prefill_tile<DK, 8, ERR>(a, L, b, h, m & 0xffff, wave, lane);
+    else
+        prefill_tile<DK, 4, ERR>(a, L, b, h, m & 0xffff, wave, lane);
+}
+
+}  // namespace
+
+bool prefill_mfma_supported(int dk, int dv, int in_bf16, long long rows_per_token) {
+    // per-lane token offsets inside a chunk (16 tokens x rows x d x 2 bytes)
+    // and the output offsets are kept in 32 bits
+    return in_bf16 && dk == dv && (dk == 128 || dk == 64) &&
+           (long long)CT * rows_per_token * dk * 4 < (1ll << 31);
+}
+
+hipError_t launch_prefill_mfma(const PoolView &p, int n_tok, const void *q, const void *k,
+                               const void *v, const float *alpha, const float *beta, float *out,
+                               hipStream_t s) {
+    PrefillArgs a;
+    a.p = p;
+    a.q = (const uint16_t *)q;
+    a.k = (const uint16_t *)k;
+    a.v = (const uint16_t *)v;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.out = out;
+    a.n_tok = n_tok;
+    a.tiles = p.B * p.H;
+    const bool err = p.colerr != nullptr;
+    if (p.dk == 128) {
+        if (err)
+            hipLaunchKernelGGL((prefill_mfma_kernel<128, true>), dim3(a.tiles), dim3(64 * 9), 0, s, a);
+        else
+            hipLaunchKernelGGL((prefill_mfma_kernel<128, false>), dim3(a.tiles), dim3(64 * 9), 0, s, a);
+    } else {
+        if (err)
+            hipLaunchKernelGGL((prefill_mfma_kernel<64, true>), dim3(a.tiles), dim3(64 * 5), 0, s, a);
+        else
+            hipLaunchKernelGGL((prefill_mfma_kernel<64, false>), dim3(a.tiles), dim3(64 * 5), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace pace

@@ -42,7 +42,8 @@ PACE_STATS_MAX_HEADS = 256
 
 EXPORTED = ("pace_abi_version", "pace_last_error", "pace_state_alloc", "pace_state_free",
             "pace_state_config", "pace_raw_bytes", "pace_decode_period", "pace_read_state",
-            "pace_quant_stats", "pace_prefill_f32", "pace_decode_step", "pace_flush_steps")
+            "pace_quant_stats", "pace_prefill_f32", "pace_decode_step", "pace_flush_steps",
+            "pace_prefill_encode")
 
 
 class PaceError(RuntimeError):
@@ -102,6 +103,7 @@ def _load():
                              ctypes.c_int),
         "pace_decode_step": ([vp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "pace_flush_steps": ([vp, vp], ctypes.c_int),
+        "pace_prefill_encode": ([vp, i32, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -183,6 +185,11 @@ def pace_decode_period(st: int, n_tok: int, q, k, v, alpha, beta, out, stream=No
 def pace_decode_step(st: int, q, k, v, alpha, beta, out, active=None, stream=None) -> None:
     _check(LIB.pace_decode_step(st, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                 _ptr(active), _ptr(out), _stream(stream)))
+
+
+def pace_prefill_encode(st: int, n_tok: int, q, k, v, alpha, beta, out=None, stream=None) -> None:
+    _check(LIB.pace_prefill_encode(st, n_tok, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                   _ptr(out), _stream(stream)))
 
 
 def pace_flush_steps(st: int, stream=None) -> None:

@@ -78,6 +78,11 @@ class State:
         pace.pace_decode_period(self.handle, tok.T, tok.q, tok.k, tok.v, tok.alpha, tok.beta,
                                 out, stream)
 
+    def prefill(self, tok: DeviceTokens, out: Optional[torch.Tensor] = None, stream=None):
+        """A prompt of tok.T tokens applied in float32 and encoded once."""
+        pace.pace_prefill_encode(self.handle, tok.T, tok.q, tok.k, tok.v, tok.alpha, tok.beta,
+                                 out, stream)
+
     def step(self, tok: DeviceTokens, out: torch.Tensor, active: Optional[torch.Tensor] = None,
              stream=None):
         """One decode step of a PACE_STEP_BUFFER handle: tok holds one token

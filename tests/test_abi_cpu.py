@@ -113,6 +113,7 @@ def test_null_arguments():
     assert pace.LIB.pace_raw_bytes(None, None) == pace.PACE_EINVAL
     assert pace.LIB.pace_decode_step(None, 16, 16, 16, 16, 16, None, 16, None) == pace.PACE_EINVAL
     assert pace.LIB.pace_flush_steps(None, None) == pace.PACE_EINVAL
+    assert pace.LIB.pace_prefill_encode(None, 1, 16, 16, 16, 16, 16, None, None) == pace.PACE_EINVAL
     assert pace.LIB.pace_state_free(None) == pace.PACE_OK
 
 

@@ -1,0 +1,94 @@
+"""Prefill hand-off (pace_prefill_encode) on the GPU against the oracle: a
+prompt of n_tok tokens applied in float32 to the stored state and encoded
+once, i.e. oracle.pace.period over the whole prompt."""
+import numpy as np
+import pytest
+
+from linear_attn_decode_pace_amd import inputs
+from oracle import quant
+from oracle import pace as opace
+from tests import parity
+from tests.gpu_cases import say, tok_tiles
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, seed, n_tok, warm, sample=None, outputs=True):
+    import torch
+    from linear_attn_decode_pace_amd import pace, runtime
+    n = w.B * w.H
+    idx = np.arange(n) if sample is None else np.asarray(sample)
+    bits = inputs.head_bits(w, seed)
+    bits_t = np.tile(bits, w.B)[idx].astype(np.int64)
+    if warm:
+        st = runtime.State(w, bits, pace.PACE_INIT_F32, runtime.warmup_state(w, seed))
+    else:
+        st = runtime.State(w, bits, pace.PACE_INIT_ZERO)
+    tix = torch.as_tensor(idx, device="cuda")
+
+    def read():
+        c, s = st.read_codes()
+        return (c.reshape(n, w.dk, w.dv)[tix].cpu().numpy(),
+                s.reshape(n, w.dv)[tix].cpu().numpy())
+
+    c0, s0 = read()
+    tok = inputs.tokens(w, seed, inputs.SEG_PROMPT, 0, n_tok)
+    out = runtime.out_buffer(w, n_tok) if outputs else None
+    st.prefill(runtime.DeviceTokens(tok), out)
+    c1, s1 = read()
+    O, rc, rs, Mpre = opace.period(c0, s0, bits_t, *tok_tiles(tok, idx, w.H))
+    what = f"{w.name} prefill {n_tok} tokens"
+    rep = parity.check_encoded(c1, s1, rc, rs, Mpre, what)
+    m = None
+    if outputs:
+        o = out.reshape(n_tok, n, w.dv)[:, tix].cpu().numpy()
+        m = parity.check_outputs(o, O, what)
+    st.free()
+    say(f"[case] {what}: output rel err {m}, flips {rep.flips}")
+    return rep
+
+
+@pytest.mark.parametrize("name,kw,n_tok,warm", [
+    ("pf-mixed", dict(B=2, H=3, n_int8=1, n_outliers=8), 100, False),   # 6 chunks + 4 tokens
+    ("pf-warm", dict(B=3, H=5, n_int8=2, n_outliers=8), 37, True),      # from a warm stored state
+    ("pf-d64", dict(B=4, H=4, dk=64, dv=64, n_int8=1), 50, False),
+    ("pf-one", dict(B=2, H=2, n_int8=1), 1, True),
+    ("pf-f32", dict(B=2, H=3, n_int8=1, dtype=inputs.DT_F32), 40, False),  # per-column kernel
+])
+def test_prefill_encode(name, kw, n_tok, warm):
+    w = inputs.ragged(name, 240, prompt=n_tok, warmup=0 if not warm else 32, **kw)
+    _run(w, 0, n_tok, warm)
+
+
+def test_prefill_encode_4096_tokens_sampled():
+    # the prompt workload's per-tile shape (32 heads, 8 at 8 bits, 4096-token
+    # prompts) on two sequences, checked on sampled tiles of both widths
+    w = inputs.PREFILL.replace(B=2)
+    bits = inputs.head_bits(w, 0)
+    pick = sorted({0, 1, 31, 32, 63} | {int(h) for h in np.nonzero(bits == 8)[0][:3]}
+                  | {32 + int(h) for h in np.nonzero(bits == 4)[0][-3:]})
+    _run(w, 0, 4096, False, sample=np.array(pick))
+
+
+def test_prefill_encode_matches_float_prefill_then_encode():
+    # the same prompt through pace_prefill_f32 + PACE_INIT_F32: both keep the
+    # state in float32, so the stored states agree up to rounding ties
+    import torch
+    from linear_attn_decode_pace_amd import pace, runtime
+    w = inputs.ragged("pf-cross", 241, B=2, H=4, n_int8=1, prompt=64, warmup=0)
+    say("[case] prefill encode vs float prefill + encode")
+    bits = inputs.head_bits(w, 0)
+    tok = runtime.DeviceTokens(inputs.tokens(w, 0, inputs.SEG_PROMPT, 0, 64))
+    a = runtime.State(w, bits, pace.PACE_INIT_ZERO)
+    a.prefill(tok)
+    M = torch.zeros((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    runtime.prefill(w, tok, M)
+    b = runtime.State(w, bits, pace.PACE_INIT_F32, M)
+    da, db = a.read_dequant(), b.read_dequant()
+    rel = (torch.linalg.vector_norm(da - db) / torch.linalg.vector_norm(db)).item()
+    assert rel < 2e-3, rel
+    ca, _ = a.read_codes()
+    cb, _ = b.read_codes()
+    assert (ca != cb).float().mean().item() < 1e-3
+    a.free()
+    b.free()
