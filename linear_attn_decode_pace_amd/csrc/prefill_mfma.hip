@@ -61,49 +61,69 @@ struct PrefillArgs {
     int tiles;
 };
 
-// Producer: stage chunk `c` and compute its token-only matrices into L.
 template <int DK>
-__device__ void prep_chunk(const PrefillArgs &a, ChunkLds &L, PrepScratch &S, size_t tile_row,
-                           int c, int lane) {
-    constexpr int NKS = DK / 32;
-    const int g = lane >> 4, n = lane & 15;
+struct TokenRegs {
+    static constexpr int CPR = DK / 8;            // 16-byte chunks per token row
+    static constexpr int NL = 3 * CT * CPR / 64;  // loads per lane
+    u32x4 val[NL];
+    float ab;
+    int nv;
+};
+
+// Producer, part 1: issue the loads of chunk c's tokens (k, q, v rows, then
+// alpha / beta) into registers; padding tokens are zero (alpha 1, beta 0).
+template <int DK>
+__device__ __attribute__((always_inline)) inline void load_chunk(const PrefillArgs &a, TokenRegs<DK> &R, size_t tile_row, int c,
+                                  int lane) {
+    constexpr int CPR = TokenRegs<DK>::CPR;
     const uint32_t tok_stride = (uint32_t)a.p.B * (uint32_t)a.p.H;
     const int t0 = CT * c, nv = min(CT, a.n_tok - t0);
-    {
-        constexpr int CPR = DK / 8;             // 16-byte chunks per token row
-        constexpr int NL = 3 * CT * CPR / 64;   // loads per lane
-        const size_t base = ((size_t)t0 * tok_stride + tile_row) * DK;
-        const uint16_t *srcs[3] = {a.k + base, a.q + base, a.v + base};
-        u32x4 val[NL];
+    const size_t base = ((size_t)t0 * tok_stride + tile_row) * DK;
 #pragma unroll
-        for (int it = 0; it < NL; ++it) {
-            const int e = lane + 64 * it;
-            const int row = e / CPR, col = (e % CPR) * 8;
-            const int t = row & 15, which = row >> 4;
-            val[it] = u32x4{0u, 0u, 0u, 0u};
-            if (t < nv)
-                val[it] = __builtin_nontemporal_load(
-                    at((const u32x4 *)srcs[which], (uint32_t)(t * tok_stride * DK + col) * 2u));
-        }
-        float ab = 0.f;
-        if (lane < 32) {
-            const int t = lane & 15;
-            const bool is_beta = lane >= 16;
-            ab = is_beta ? 0.f : 1.f;
-            if (t < nv)
-                ab = (is_beta ? a.beta : a.alpha)[((size_t)t0 + t) * tok_stride + tile_row];
-        }
-#pragma unroll
-        for (int it = 0; it < NL; ++it) {
-            const int e = lane + 64 * it;
-            const int row = e / CPR, col = (e % CPR) * 8;
-            const int t = row & 15, which = row >> 4;
-            uint16_t *dst = which < 2 ? &L.kq[which * 16 + t][col] : &L.v[t][col];
-            *(u32x4 *)dst = val[it];
-        }
-        if (lane < 32) (lane >= 16 ? S.beta : S.alpha)[lane & 15] = ab;
-        if (lane == 0) L.n_valid = nv;
+    for (int it = 0; it < TokenRegs<DK>::NL; ++it) {
+        const int e = lane + 64 * it;
+        const int row = e / CPR, col = (e % CPR) * 8;
+        const int t = row & 15;
+        // the 48 rows are k, q, v in blocks of 16: the block is fixed per load
+        constexpr int RPL = 64 / CPR;  // rows per load
+        const int which = (it * RPL) / CT;
+        const uint16_t *src = (which == 0 ? a.k : which == 1 ? a.q : a.v) + base;
+        R.val[it] = u32x4{0u, 0u, 0u, 0u};
+        if (t < nv)
+            R.val[it] = __builtin_nontemporal_load(
+                at((const u32x4 *)src, (uint32_t)(t * tok_stride * DK + col) * 2u));
     }
+    R.ab = 0.f;
+    if (lane < 32) {
+        const int t = lane & 15;
+        const bool is_beta = lane >= 16;
+        R.ab = is_beta ? 0.f : 1.f;
+        if (t < nv) R.ab = (is_beta ? a.beta : a.alpha)[((size_t)t0 + t) * tok_stride + tile_row];
+    }
+    R.nv = nv;
+}
+
+// Producer, part 2: write the loaded chunk into LDS.
+template <int DK>
+__device__ __attribute__((always_inline)) inline void stage_chunk(const TokenRegs<DK> &R, ChunkLds &L, PrepScratch &S, int lane) {
+    constexpr int CPR = TokenRegs<DK>::CPR;
+#pragma unroll
+    for (int it = 0; it < TokenRegs<DK>::NL; ++it) {
+        const int e = lane + 64 * it;
+        const int row = e / CPR, col = (e % CPR) * 8;
+        const int t = row & 15, which = row >> 4;
+        uint16_t *dst = which < 2 ? &L.kq[which * 16 + t][col] : &L.v[t][col];
+        *(u32x4 *)dst = R.val[it];
+    }
+    if (lane < 32) (lane >= 16 ? S.beta : S.alpha)[lane & 15] = R.ab;
+    if (lane == 0) L.n_valid = R.nv;
+}
+
+// Producer, part 3: the staged chunk's token-only matrices.
+template <int DK>
+__device__ __attribute__((always_inline)) inline void prep_chunk(ChunkLds &L, PrepScratch &S, int lane) {
+    constexpr int NKS = DK / 32;
+    const int g = lane >> 4, n = lane & 15;
     wave_sync();
 
     // Gram products on MFMA: A row m of the K (Q) block is token 4 (m % 4) + m / 4
@@ -232,15 +252,50 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) acc[rt] *= sk;
     }
-    if (producer) prep_chunk<DK>(a, L.ch[0], L.ps, tile_row, 0, lane);
-    __syncthreads();
+    // Output flush of chunk c, shared by every wave: rows of DK floats, 16
+    // bytes per lane (between the two barriers that close a chunk)
+    auto flush = [&](int c) {
+        if (!a.out) return;
+        constexpr int PER_ROW = DK / 4;
+        const int e = wave * 64 + lane;
+        const int t = e / PER_ROW, c4 = (e % PER_ROW) * 4;
+        if (t < CT && t < L.ch[c & 1].n_valid) {
+            const f32x4 x = *(const f32x4 *)&L.o[t][c4];
+            __builtin_nontemporal_store(
+                x, (f32x4 *)(a.out + (((size_t)CT * c + t) * tok_stride + tile_row) * DK + c4));
+        }
+    };
 
+    if (producer) {
+        // the producer keeps the next chunk's tokens in flight in its own
+        // registers: chunk c+2 loads while chunk c+1 is prepared and chunk c
+        // applied (its loop has the same barriers as the consumers')
+        TokenRegs<DK> R;
+        load_chunk<DK>(a, R, tile_row, 0, lane);
+        stage_chunk<DK>(R, L.ch[0], L.ps, lane);
+        if (n_chunks > 1) load_chunk<DK>(a, R, tile_row, 1, lane);
+        prep_chunk<DK>(L.ch[0], L.ps, lane);
+        __syncthreads();
+        for (int c = 0; c < n_chunks; ++c) {
+            if (c + 1 < n_chunks) {
+                // chunk c+1 into LDS; its registers then take chunk c+2's loads
+                ChunkLds &N = L.ch[(c + 1) & 1];
+                stage_chunk<DK>(R, N, L.ps, lane);
+                if (c + 2 < n_chunks) load_chunk<DK>(a, R, tile_row, c + 2, lane);
+                prep_chunk<DK>(N, L.ps, lane);
+            }
+            __syncthreads();  // chunk c+1 staged, chunk c's outputs complete
+            flush(c);
+            __syncthreads();  // the output staging is free again
+        }
+        return;
+    }
+
+    __syncthreads();
     const int tok_n = 4 * (n & 3) + (n >> 2);
     for (int c = 0; c < n_chunks; ++c) {
         ChunkLds &C = L.ch[c & 1];
-        if (producer) {
-            if (c + 1 < n_chunks) prep_chunk<DK>(a, L.ch[(c + 1) & 1], L.ps, tile_row, c + 1, lane);
-        } else {
+        {
             // P = [K; Q] M0 over three bf16 parts of M0
             f32x4 PK = {0.f, 0.f, 0.f, 0.f}, PQ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -306,22 +361,12 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
             }
         }
         __syncthreads();  // chunk c+1 staged, chunk c's outputs complete
-        if (a.out) {
-            // every wave helps flush: rows of DK floats, 16 bytes per lane
-            constexpr int PER_ROW = DK / 4;
-            const int e = wave * 64 + lane;
-            const int t = e / PER_ROW, c4 = (e % PER_ROW) * 4;
-            if (t < C.n_valid) {
-                const f32x4 x = *(const f32x4 *)&L.o[t][c4];
-                __builtin_nontemporal_store(
-                    x, (f32x4 *)(a.out + (((size_t)CT * c + t) * tok_stride + tile_row) * DK + c4));
-            }
-        }
+        flush(c);
         __syncthreads();  // the output staging is free again
     }
 
     // ---- encode each column block once: absmax, scale, codes ----
-    if (!producer) {
+    {
         float am = 0.f;
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt)
