@@ -153,15 +153,18 @@ __device__ __attribute__((always_inline)) inline void prep_chunk(ChunkLds &L, Pr
         float al[CT];
 #pragma unroll
         for (int r = 0; r < CT; ++r) al[r] = S.alpha[r];
+        // lane -> row t, columns s0..s0+3: Gamma_{t,s0+3} as one masked
+        // product, then the running product down to s0
         const int t = lane >> 2, s0 = 4 * (lane & 3);
+        float gts = 1.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int r = 1; r < CT; ++r) gts *= (r > s0 + 3 && r <= t) ? al[r] : 1.f;
+#pragma unroll
+        for (int e = 3; e >= 0; --e) {
             const int s = s0 + e;
-            float gts = 1.f;
-#pragma unroll
-            for (int r = 1; r < CT; ++r) gts *= (r > s && r <= t) ? al[r] : 1.f;
             S.A[t][s] = s < t ? gts * S.kk[t][s] : 0.f;
             S.Lq[t][s] = s <= t ? gts * S.qk[t][s] : 0.f;
+            if (e > 0 && s <= t) gts *= S.alpha[s];  // Gamma_{t,s-1} = Gamma_{t,s} alpha_s
         }
         if (lane < CT) {
             float gm = 1.f, gc = 1.f;
@@ -196,16 +199,13 @@ __device__ __attribute__((always_inline)) inline void prep_chunk(ChunkLds &L, Pr
     }
     wave_sync();
 
-    // Lq T: lane -> row t = lane / 4, columns s = 4 (lane % 4) + e
+    // Lq T on float32 MFMA: step st takes column / row 4 st + g
     {
-        const int t = lane >> 2, s0 = 4 * (lane & 3);
+        f32x4 D = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float r2 = 0.f;
+        for (int st = 0; st < 4; ++st) D = mfma_f32_k4(S.Lq[n][4 * st + g], L.Tt[n][4 * st + g], D);
 #pragma unroll
-            for (int u = 0; u < CT; ++u) r2 = fmaf(S.Lq[t][u], L.Tt[s0 + e][u], r2);
-            L.LqT[t][s0 + e] = r2;
-        }
+        for (int r = 0; r < 4; ++r) L.LqT[4 * g + r][n] = D[r];
     }
 }
 
