@@ -144,6 +144,18 @@ def cpu_baseline(w, seed, warm_tok, periods_tok, head_bits, n_seq):
             "seconds": dt}
 
 
+def window_bytes(w: inputs.Workload, head_bits, S: int) -> int:
+    """Bytes of one FP8-window step with a full window: the stored history read
+    and written (a write leaves the window every step), the S pairs of E4M3
+    vectors and their scales read, one pair written, the token read and the
+    float32 outputs written."""
+    e_in = 2 if w.dtype == inputs.DT_BF16 else 4
+    state = sum(w.dk * w.dv * int(b) // 8 + 4 * w.dv for b in head_bits)
+    win = w.H * (S * (w.dk + w.dv + 12) + (w.dk + w.dv + 12))
+    io = w.H * ((w.dk * 2 + w.dv) * e_in + 8 + 4 * w.dv)
+    return w.B * (2 * state + win + io)
+
+
 def prefill_bytes(w: inputs.Workload, n_tok: int, head_bits) -> int:
     """Bytes of one prefill call at minimum: the prompt's q/k/v/alpha/beta read
     once, its float32 outputs written once, every code and scale read and
@@ -226,10 +238,12 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=inputs.HEADLINE.name, choices=sorted(inputs.WORKLOADS))
-    ap.add_argument("--mode", default="period", choices=("period", "step", "prefill"),
+    ap.add_argument("--mode", default="period", choices=("period", "step", "prefill", "window"),
                     help="period: one call per period of k tokens; step: one call per token "
                          "(PACE_STEP_BUFFER handle), every sequence active; prefill: one "
-                         "pace_prefill_encode call per prompt (the workload's prompt length)")
+                         "pace_prefill_encode call per prompt (the workload's prompt length); "
+                         "window: one call per token with the FP8 write window")
+    ap.add_argument("--fp8-window", type=int, default=8, help="window mode: writes kept in FP8")
     ap.add_argument("--prompt-distinct", type=int, default=256,
                     help="prefill mode: distinct prompt tokens generated on the host; the "
                          "device prompt repeats them to the full length")
@@ -280,11 +294,14 @@ def main() -> int:
 
     M0 = torch.zeros((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
     runtime.prefill(w, runtime.DeviceTokens(warm_tok), M0)
-    step_mode = args.mode == "step"
+    step_mode = args.mode in ("step", "window")
+    window_mode = args.mode == "window"
     adaptive = step_mode and args.adapt_tau > 0
-    flags = (pace.PACE_STEP_BUFFER if step_mode else 0) | (pace.PACE_ADAPTIVE if adaptive else 0)
+    flags = (pace.PACE_STEP_BUFFER if step_mode and not window_mode else 0) | \
+        (pace.PACE_ADAPTIVE if adaptive else 0) | (pace.PACE_FP8_WINDOW if window_mode else 0)
     st = runtime.State(w, head_bits, pace.PACE_INIT_F32, M0, flags=flags,
-                       adapt_tau=args.adapt_tau if adaptive else 0.0)
+                       adapt_tau=args.adapt_tau if adaptive else 0.0,
+                       fp8_window=args.fp8_window if window_mode else 0)
     del M0
     ring = [runtime.DeviceTokens(tk) for tk in ring_tok]
     if step_mode:   # one token per call: the ring's periods cut into tokens
@@ -336,8 +353,12 @@ def main() -> int:
             closes += int((fill == 0).sum().item())
         k_eff = K * w.B * w.H / max(1, closes)
         log(f"adaptive period: mean period {k_eff:.2f} tokens over {K} steps")
-    nbytes = algorithmic_bytes_step(w, head_bits, k_eff) if step_mode else \
-        algorithmic_bytes(w, C, head_bits)
+    if window_mode:
+        nbytes = window_bytes(w, head_bits, args.fp8_window)
+    elif step_mode:
+        nbytes = algorithmic_bytes_step(w, head_bits, k_eff)
+    else:
+        nbytes = algorithmic_bytes(w, C, head_bits)
     achieved = nbytes / (launch_ms * 1e-3) / 1e9
     sha = kernel_sha()
     tokens_per_call = 1 if step_mode else C
@@ -360,6 +381,7 @@ def main() -> int:
                    "inputs": w.dtype, "outlier_channels": w.n_outliers,
                    "mode": args.mode, "decode_steps": K * tokens_per_call,
                    "adapt_tau": args.adapt_tau if adaptive else None,
+                   "fp8_window": args.fp8_window if window_mode else None,
                    "mean_period": k_eff,
                    "input_ring_calls": ring_n,
                    "start_state": f"{warm[2]} {'prompt' if w.prompt else 'warm-up'} tokens from zero"},

@@ -86,7 +86,14 @@ extern "C" {
 #define PACE_READ_RAW 2     /* dst: device bytes [pace_raw_bytes()]; scales_dst must be NULL */
 #define PACE_READ_STEP 3    /* PACE_STEP_BUFFER handles: dst: device int32 [B, H] buffered tokens
                                per state; scales_dst: device float32 [B, H, 2] = (A, R) of
-                               PACE_ADAPTIVE (zeros without it), or NULL */
+                               PACE_ADAPTIVE (zeros without it), or NULL.  PACE_FP8_WINDOW
+                               handles: dst: writes in the window; scales_dst: (lam, head) with
+                               lam the history's decay since its last encode and head the slot
+                               of the oldest write (as a float) */
+#define PACE_READ_WINDOW 4  /* PACE_FP8_WINDOW handles: dst: device uint8 [B, H, S, d_k + d_v], the
+                               E4M3 codes of k_t then u_t per slot (slots in ring order, see
+                               PACE_READ_STEP); scales_dst: device float32 [B, H, S, 3] = (k scale,
+                               u scale, decay since the write), or NULL */
 
 /* config flags */
 /* PACE_STATS_ERR: every encode (the PACE_INIT_F32 encode at alloc and the
@@ -119,6 +126,18 @@ extern "C" {
  * when its buffer is full (cfg.period is then the maximum period) or when
  * A > adapt_tau * R already holds before the step.  Costs B * H * 8 bytes. */
 #define PACE_ADAPTIVE 0x4u
+/* PACE_FP8_WINDOW: the handle decodes one token per call (pace_decode_step)
+ * with a pure-write window instead of a period ('低比特量化新突破：GGA+PW让线性
+ * 注意力长文本生成更准更短', section 'PW：让近期写入走“纯净通道”').  Each write of
+ * the delta rule, M_t = alpha_t M_{t-1} + k_t u_t^T with
+ * u_t = beta_t (v_t - alpha_t M_{t-1}^T k_t), is kept as a pair of OCP E4M3
+ * vectors (one float32 scale each, absmax / 448, nearest-even codes); the
+ * last cfg.fp8_window writes stay out of the column-quantized history and
+ * decay with it; a write leaving the window is added to the history, which is
+ * re-encoded.  Outputs are read from the state after the step's exact write.
+ * Excludes PACE_STEP_BUFFER and PACE_ADAPTIVE; cfg.period is ignored.
+ * Window bytes: B * H * (S * (d_k + d_v + 12) + 12). */
+#define PACE_FP8_WINDOW 0x8u
 
 typedef struct pace_state pace_state; /* opaque; owns the device pools */
 
@@ -132,6 +151,7 @@ typedef struct pace_config {
     const uint8_t *head_bits; /* host [H]: bit width of each head, 4 or 8; copied at alloc */
     uint32_t flags;           /* 0 or an OR of PACE_STATS_ERR, PACE_STEP_BUFFER, PACE_ADAPTIVE */
     float adapt_tau;          /* PACE_ADAPTIVE: threshold tau, finite and > 0; otherwise ignored */
+    int32_t fp8_window;       /* PACE_FP8_WINDOW: writes kept in the window, 1..64; otherwise ignored */
 } pace_config;
 
 typedef struct pace_stats {
@@ -147,8 +167,8 @@ typedef struct pace_stats {
     uint64_t tokens;           /* tokens applied since alloc: n_tok per pace_decode_period,
                                   1 per pace_decode_step (whatever its active mask) */
     uint64_t zero_columns;     /* stored columns whose scale is 0 */
-    uint64_t bytes_step_buffer; /* device bytes of the per-step token buffer and fill counts
-                                  (0 without PACE_STEP_BUFFER) */
+    uint64_t bytes_step_buffer; /* device bytes of the per-step token buffer and fill counts,
+                                  or of the FP8 window (0 for period handles) */
     /* with PACE_STATS_ERR (err_tracked = 1), per head h < heads, over every
      * sequence b and entry (i, j) of the state M of the last encode:
      * err_sq[h] = sum (M_ij - c_ij s_j)^2 and ref_sq[h] = sum M_ij^2, so that
@@ -213,8 +233,9 @@ int pace_decode_period(pace_state *st, int32_t n_tok, const void *q, const void 
                        void *stream);
 
 /*
- * One decode step of a PACE_STEP_BUFFER handle: one token for every active
- * sequence.  For each (sequence, head) state with f tokens buffered, the
+ * One decode step of a PACE_STEP_BUFFER or PACE_FP8_WINDOW handle: one token
+ * for every active sequence (for the window see PACE_FP8_WINDOW; the rest of
+ * this comment describes the buffer).  For each (sequence, head) state with f tokens buffered, the
  * output is read from the stored state decoded with the f buffered tokens and
  * then this token applied in order, in float32 (the high-precision state the
  * period holds after this token).  If f + 1 = period the state is re-encoded
@@ -229,7 +250,7 @@ int pace_decode_period(pace_state *st, int32_t n_tok, const void *q, const void 
  *           for all sequences.  Sequences can so sit at different phases.
  *   out:    device float32 [B, H, d_v], 16-byte aligned.
  * Errors: EINVAL (null or misaligned pointer, a handle without
- *         PACE_STEP_BUFFER), EDEVICE.
+ *         PACE_STEP_BUFFER or PACE_FP8_WINDOW), EDEVICE.
  */
 int pace_decode_step(pace_state *st, const void *q, const void *k, const void *v,
                      const float *alpha, const float *beta, const uint8_t *active,
@@ -238,10 +259,12 @@ int pace_decode_step(pace_state *st, const void *q, const void *k, const void *v
 /*
  * End every partial period of a PACE_STEP_BUFFER handle: each state with a
  * non-empty buffer has its buffered tokens applied and is re-encoded (as a
- * shorter final period); its buffer is emptied.  Call before
+ * shorter final period); its buffer is emptied.  For a PACE_FP8_WINDOW handle:
+ * every write still in the window is added to the history (oldest first),
+ * which is re-encoded once; the window is emptied.  Call before
  * pace_read_state or a raw checkpoint when the buffered tokens must be part
  * of the stored state.  No outputs.
- * Errors: EINVAL (a handle without PACE_STEP_BUFFER), EDEVICE.
+ * Errors: EINVAL (a handle without PACE_STEP_BUFFER or PACE_FP8_WINDOW), EDEVICE.
  */
 int pace_flush_steps(pace_state *st, void *stream);
 

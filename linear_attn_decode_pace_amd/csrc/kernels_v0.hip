@@ -129,7 +129,7 @@ __device__ inline void apply_tokens(float M[DK], float *sk, float *sq, int n_tok
 }
 
 template <int DK>
-__global__ void decode_v0_kernel(PoolView p, int n_tok, const void *q, const void *k,
+__global__ void __launch_bounds__(256) decode_v0_kernel(PoolView p, int n_tok, const void *q, const void *k,
                                  const void *v, const float *alpha, const float *beta,
                                  float *out, int bf16) {
     __shared__ float sk[DK], sq[DK];
@@ -145,7 +145,7 @@ __global__ void decode_v0_kernel(PoolView p, int n_tok, const void *q, const voi
 }
 
 template <int DK>
-__global__ void encode_f32_kernel(PoolView p, const float *src) {
+__global__ void __launch_bounds__(256) encode_f32_kernel(PoolView p, const float *src) {
     const int tile = blockIdx.x, b = tile / p.H, h = tile % p.H, j = threadIdx.x;
     int bits;
     uint8_t *codes = tile_codes(p, b, h, &bits);
@@ -158,7 +158,7 @@ __global__ void encode_f32_kernel(PoolView p, const float *src) {
 }
 
 template <int DK>
-__global__ void prefill_v0_kernel(int B, int H, int dv, int n_tok, int bf16, const void *q,
+__global__ void __launch_bounds__(256) prefill_v0_kernel(int B, int H, int dv, int n_tok, int bf16, const void *q,
                                   const void *k, const void *v, const float *alpha,
                                   const float *beta, float *state, float *out) {
     __shared__ float sk[DK], sq[DK];
@@ -174,7 +174,7 @@ __global__ void prefill_v0_kernel(int B, int H, int dv, int n_tok, int bf16, con
 
 // what: 0 = codes to int8 [B,H,dk,dv] + scales, 1 = dequantized float32
 template <int DK>
-__global__ void read_kernel(PoolView p, int what, void *dst, float *sdst) {
+__global__ void __launch_bounds__(256) read_kernel(PoolView p, int what, void *dst, float *sdst) {
     const int tile = blockIdx.x, b = tile / p.H, h = tile % p.H, j = threadIdx.x;
     int bits;
     const uint8_t *codes = tile_codes(p, b, h, &bits);
@@ -269,7 +269,7 @@ __device__ inline float block_sum(float x, float *red) {
 }
 
 template <int DK>
-__global__ void step_v0_kernel(PoolView p, StepView sv, const void *q, const void *k,
+__global__ void __launch_bounds__(256) step_v0_kernel(PoolView p, StepView sv, const void *q, const void *k,
                                const void *v, const float *alpha, const float *beta, float *out,
                                int bf16) {
     __shared__ float sk[DK], sq[DK], red[4];
@@ -321,7 +321,7 @@ __global__ void step_v0_kernel(PoolView p, StepView sv, const void *q, const voi
 }
 
 template <int DK>
-__global__ void flush_v0_kernel(PoolView p, StepView sv, int bf16) {
+__global__ void __launch_bounds__(256) flush_v0_kernel(PoolView p, StepView sv, int bf16) {
     __shared__ float sk[DK], sq[DK], red[4];
     const int tile = blockIdx.x, b = tile / p.H, h = tile % p.H, j = threadIdx.x;
     const int f = sv.fill[tile];
@@ -348,7 +348,7 @@ __global__ void flush_v0_kernel(PoolView p, StepView sv, int bf16) {
 
 // adapt[2 t] = 0, adapt[2 t + 1] = ||decode(stored state t)||_F
 template <int DK>
-__global__ void adapt_init_kernel(PoolView p, float *adapt) {
+__global__ void __launch_bounds__(256) adapt_init_kernel(PoolView p, float *adapt) {
     __shared__ float red[4];
     const int tile = blockIdx.x, b = tile / p.H, h = tile % p.H, j = threadIdx.x;
     int bits;

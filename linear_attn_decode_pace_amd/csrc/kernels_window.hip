@@ -1,0 +1,284 @@
+// FP8 write window over the low-bit state (PACE_FP8_WINDOW handles), one
+// thread per state column: the pure-write sliding window of
+// '低比特量化新突破：GGA+PW让线性注意力长文本生成更准更短', section 'PW：让近期写入走“纯净通道”'.
+// The last S writes (k_t, u_t) of the delta rule, M_t = alpha_t M_{t-1} +
+// k_t u_t^T with u_t = beta_t (v_t - alpha_t M_{t-1}^T k_t), are kept as OCP
+// E4M3 vectors with one float32 scale each and a decay factor; the history is
+// column-quantized as every other state here and decays through one factor
+// lam.  When a write leaves the window it is merged into the history, which
+// is then re-encoded.
+#include "pace_window.h"
+
+namespace pace {
+namespace {
+
+constexpr float E4M3_MAX = 448.f;
+
+__device__ inline float ld_in_w(const void *p, size_t idx, int bf16) {
+    if (bf16) return __uint_as_float((uint32_t)((const uint16_t *)p)[idx] << 16);
+    return ((const float *)p)[idx];
+}
+
+// nearest E4M3 code of x (|x| <= 448), ties to even: 3 mantissa bits from
+// float32's 23; below 2^-6 the quantum is 2^-9
+__device__ inline uint8_t e4m3_encode(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const float a = fabsf(x);
+    if (a < 0.015625f) {  // subnormal range: multiples of 2^-9
+        const float m = rintf(a * 512.f);  // exact scaling, nearest even
+        return (uint8_t)(sign | (uint32_t)m);
+    }
+    const uint32_t au = __float_as_uint(a);
+    int e = (int)(au >> 23) - 127;
+    uint32_t man = au & 0x7fffffu;
+    uint32_t r = man >> 20, rem = man & 0xfffffu;
+    if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
+    if (r == 8u) {
+        r = 0;
+        ++e;
+    }
+    return (uint8_t)(sign | ((uint32_t)(e + 7) << 3) | r);
+}
+
+__device__ inline float e4m3_decode(uint8_t c) {
+    const uint32_t E = (c >> 3) & 15u, M = c & 7u;
+    float v;
+    if (E == 0)
+        v = (float)M * 0.001953125f;  // M * 2^-9
+    else
+        v = __uint_as_float(((E + 120u) << 23) | (M << 20));  // (1 + M/8) 2^(E-7)
+    return (c & 0x80u) ? -v : v;
+}
+
+template <int DK>
+__device__ inline void load_col(const PoolView &p, const uint8_t *codes, int bits, int j, float s,
+                                float M[DK]) {
+#pragma unroll
+    for (int i = 0; i < DK; ++i) {
+        int c;
+        if (bits == 4) {
+            int sh;
+            const size_t o = loc4(DK, i, j, &sh);
+            c = ((int)((uint32_t)codes[o] << (28 - sh))) >> 28;
+        } else {
+            c = (int)(int8_t)codes[loc8(DK, i, j)];
+        }
+        M[i] = (float)c * s;
+    }
+}
+
+// column quantizer (absmax / qmax, nearest even), as the other encoders here
+template <int DK>
+__device__ inline float store_col(uint8_t *codes, int bits, int j, const float M[DK], float *err) {
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < DK; ++i) amax = fmaxf(amax, fabsf(M[i]));
+    const int qm = bits == 4 ? 7 : 127;
+    const float s = amax / (float)qm;
+    float e2 = 0.f, m2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < DK; ++i) {
+        int c = 0;
+        if (s > 0.f) c = (int)fminf(fmaxf(rintf(M[i] / s), -(float)qm), (float)qm);
+        if (err) {
+            const float d = M[i] - (float)c * s;
+            e2 += d * d;
+            m2 += M[i] * M[i];
+        }
+        if (bits == 4) {
+            int sh;
+            const size_t o = loc4(DK, i, j, &sh);
+            codes[o] = (uint8_t)((codes[o] & ~(0xf << sh)) | ((c & 15) << sh));
+        } else {
+            codes[loc8(DK, i, j)] = (uint8_t)(int8_t)c;
+        }
+    }
+    if (err) {
+        err[0] = e2;
+        err[1] = m2;
+    }
+    return s;
+}
+
+__device__ inline float block_max(float x, float *red) {
+    for (int m = 32; m > 0; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    float t = 0.f;
+    for (int w = 0; w < (int)(blockDim.x + 63) / 64; ++w) t = fmaxf(t, red[w]);
+    return t;
+}
+
+// one step for the state `tile`: thread j owns column j (blockDim = d_v)
+template <int DK>
+__global__ void __launch_bounds__(256) window_step_kernel(PoolView p, WindowView wv, const void *q, const void *k,
+                                   const void *v, const float *alpha, const float *beta,
+                                   float *out, int bf16) {
+    __shared__ float sk[DK], sq[DK], kw[DK], red[4];
+    const int tile = blockIdx.x, b = tile / p.H, h = tile % p.H, j = threadIdx.x;
+    if (wv.active && !wv.active[b]) return;
+    const int S = wv.S, cnt = wv.count[tile], head = wv.head[tile];
+    const float lam = wv.lam[tile];
+    const size_t row = (size_t)DK + p.dv;
+    uint8_t *wc = wv.codes + (size_t)tile * S * row;
+    float *wf = wv.f + (size_t)tile * S * 3;  // per slot: k scale, u scale, decay
+    int bits;
+    uint8_t *codes = tile_codes(p, b, h, &bits);
+    float *sc = p.scales + (size_t)tile * p.dv;
+
+    // M_{t-1}, column j: lam * history + the decayed FP8 writes of the window
+    float M[DK];
+    load_col<DK>(p, codes, bits, j, sc[j], M);
+#pragma unroll
+    for (int i = 0; i < DK; ++i) M[i] *= lam;
+    for (int e = 0; e < cnt; ++e) {
+        const int slot = (head + e) % S;
+        const uint8_t *c = wc + slot * row;
+        __syncthreads();
+        for (int i = j; i < DK; i += blockDim.x) kw[i] = e4m3_decode(c[i]) * wf[3 * slot];
+        __syncthreads();
+        const float w = e4m3_decode(c[DK + j]) * wf[3 * slot + 1] * wf[3 * slot + 2];
+#pragma unroll
+        for (int i = 0; i < DK; ++i) M[i] = fmaf(kw[i], w, M[i]);
+    }
+    // this token
+    for (int i = j; i < DK; i += blockDim.x) {
+        sk[i] = ld_in_w(k, (size_t)tile * DK + i, bf16);
+        sq[i] = ld_in_w(q, (size_t)tile * DK + i, bf16);
+    }
+    __syncthreads();
+    const float a = alpha[tile], bt = beta[tile];
+    float d = 0.f;
+#pragma unroll
+    for (int i = 0; i < DK; ++i) d = fmaf(sk[i], M[i], d);
+    const float u = bt * (ld_in_w(v, (size_t)tile * p.dv + j, bf16) - a * d);
+    float o = 0.f;
+#pragma unroll
+    for (int i = 0; i < DK; ++i) o = fmaf(sq[i], fmaf(a, M[i], sk[i] * u), o);
+    out[(size_t)tile * p.dv + j] = o;
+
+    // decay the history and every window entry; a full window merges its
+    // oldest write (already decayed) into the history, which is re-encoded
+    const float lam_new = lam * a;
+    const int slot_new = (head + cnt) % S;  // == head when the window is full
+    if (cnt == S) {
+        const uint8_t *c = wc + head * row;
+        const float delta_o = wf[3 * head + 2] * a;
+        __syncthreads();
+        for (int i = j; i < DK; i += blockDim.x) kw[i] = e4m3_decode(c[i]) * wf[3 * head];
+        __syncthreads();
+        const float w = e4m3_decode(c[DK + j]) * wf[3 * head + 1] * delta_o;
+        // M is no longer needed: reuse its registers for the history column
+        load_col<DK>(p, codes, bits, j, sc[j], M);
+#pragma unroll
+        for (int i = 0; i < DK; ++i) M[i] = fmaf(kw[i], w, lam_new * M[i]);
+        sc[j] = store_col<DK>(codes, bits, j, M,
+                              p.colerr ? p.colerr + ((size_t)tile * p.dv + j) * 2 : nullptr);
+    }
+    // the new write (k_t, u_t) in E4M3, one scale per vector
+    float ka = 0.f;
+    for (int i = j; i < DK; i += blockDim.x) ka = fmaxf(ka, fabsf(sk[i]));
+    const float s_k = block_max(ka, red) / E4M3_MAX;
+    const float s_u = block_max(fabsf(u), red) / E4M3_MAX;
+    uint8_t *cn = wc + slot_new * row;
+    for (int i = j; i < DK; i += blockDim.x)
+        cn[i] = s_k > 0.f ? e4m3_encode(fminf(fmaxf(sk[i] / s_k, -E4M3_MAX), E4M3_MAX)) : 0;
+    cn[DK + j] = s_u > 0.f ? e4m3_encode(fminf(fmaxf(u / s_u, -E4M3_MAX), E4M3_MAX)) : 0;
+    __syncthreads();  // every thread has read the window's decay factors
+    if (j == 0) {
+        for (int e = 0; e < cnt; ++e) {
+            const int slot = (head + e) % S;
+            if (!(cnt == S && slot == head)) wf[3 * slot + 2] *= a;
+        }
+        wf[3 * slot_new] = s_k;
+        wf[3 * slot_new + 1] = s_u;
+        wf[3 * slot_new + 2] = 1.f;
+        if (cnt == S) {
+            wv.head[tile] = (head + 1) % S;
+            wv.lam[tile] = 1.f;
+        } else {
+            wv.count[tile] = cnt + 1;
+            wv.lam[tile] = lam_new;
+        }
+    }
+}
+
+// merge every window entry into the history (oldest first) and encode once
+template <int DK>
+__global__ void __launch_bounds__(256) window_flush_kernel(PoolView p, WindowView wv) {
+    __shared__ float kw[DK];
+    const int tile = blockIdx.x, b = tile / p.H, h = tile % p.H, j = threadIdx.x;
+    const int S = wv.S, cnt = wv.count[tile], head = wv.head[tile];
+    if (cnt == 0) return;
+    const float lam = wv.lam[tile];
+    const size_t row = (size_t)DK + p.dv;
+    const uint8_t *wc = wv.codes + (size_t)tile * S * row;
+    const float *wf = wv.f + (size_t)tile * S * 3;
+    int bits;
+    uint8_t *codes = tile_codes(p, b, h, &bits);
+    float *sc = p.scales + (size_t)tile * p.dv;
+    float H[DK];
+    load_col<DK>(p, codes, bits, j, sc[j], H);
+#pragma unroll
+    for (int i = 0; i < DK; ++i) H[i] *= lam;
+    for (int e = 0; e < cnt; ++e) {
+        const int slot = (head + e) % S;
+        const uint8_t *c = wc + slot * row;
+        __syncthreads();
+        for (int i = j; i < DK; i += blockDim.x) kw[i] = e4m3_decode(c[i]) * wf[3 * slot];
+        __syncthreads();
+        const float w = e4m3_decode(c[DK + j]) * wf[3 * slot + 1] * wf[3 * slot + 2];
+#pragma unroll
+        for (int i = 0; i < DK; ++i) H[i] = fmaf(kw[i], w, H[i]);
+    }
+    sc[j] = store_col<DK>(codes, bits, j, H,
+                          p.colerr ? p.colerr + ((size_t)tile * p.dv + j) * 2 : nullptr);
+    __syncthreads();
+    if (j == 0) {
+        wv.count[tile] = 0;
+        wv.head[tile] = 0;
+        wv.lam[tile] = 1.f;
+    }
+}
+
+__global__ void window_meta_kernel(WindowView wv, float *out, size_t states) {
+    const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < states) {
+        out[2 * t] = wv.lam[t];
+        out[2 * t + 1] = (float)wv.head[t];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_window_meta(const WindowView &wv, float *out, size_t states, hipStream_t s) {
+    hipLaunchKernelGGL(window_meta_kernel, dim3((unsigned)((states + 255) / 256)), dim3(256), 0, s,
+                       wv, out, states);
+    return hipGetLastError();
+}
+
+hipError_t launch_window_step(const PoolView &p, const WindowView &wv, const void *q,
+                              const void *k, const void *v, const float *alpha,
+                              const float *beta, float *out, int in_bf16, hipStream_t s) {
+    dim3 grid(p.B * p.H), block(p.dv);
+    if (p.dk == 128)
+        hipLaunchKernelGGL(window_step_kernel<128>, grid, block, 0, s, p, wv, q, k, v, alpha,
+                           beta, out, in_bf16);
+    else
+        hipLaunchKernelGGL(window_step_kernel<64>, grid, block, 0, s, p, wv, q, k, v, alpha,
+                           beta, out, in_bf16);
+    return hipGetLastError();
+}
+
+hipError_t launch_window_flush(const PoolView &p, const WindowView &wv, hipStream_t s) {
+    dim3 grid(p.B * p.H), block(p.dv);
+    if (p.dk == 128)
+        hipLaunchKernelGGL(window_flush_kernel<128>, grid, block, 0, s, p, wv);
+    else
+        hipLaunchKernelGGL(window_flush_kernel<64>, grid, block, 0, s, p, wv);
+    return hipGetLastError();
+}
+
+}  // namespace pace

@@ -15,6 +15,7 @@
 #include "pace_mfma.h"
 #include "pace_prefill.h"
 #include "pace_step.h"
+#include "pace_window.h"
 
 #define PACE_API extern "C" __attribute__((visibility("default")))
 
@@ -35,6 +36,10 @@ struct pace_state {
     float *step_ab = nullptr;      // PACE_STEP_BUFFER: [B * H][period - 1][2]
     int32_t *step_fill = nullptr;  // PACE_STEP_BUFFER: [B * H]
     float *adapt = nullptr;        // PACE_ADAPTIVE: [B * H][2] = (A, R)
+    uint8_t *win_codes = nullptr;  // PACE_FP8_WINDOW: [B * H][S][d_k + d_v]
+    float *win_f = nullptr;        // PACE_FP8_WINDOW: [B * H][S][3]
+    int32_t *win_meta = nullptr;   // PACE_FP8_WINDOW: count [B * H], then head [B * H]
+    float *win_lam = nullptr;      // PACE_FP8_WINDOW: [B * H]
     size_t bytes4 = 0, bytes8 = 0, bytes_scales = 0, bytes_step = 0;
     uint64_t periods = 0, tokens = 0;
 
@@ -66,6 +71,19 @@ struct pace_state {
         return v;
     }
     bool stepped() const { return (cfg.flags & PACE_STEP_BUFFER) != 0; }
+    bool windowed() const { return (cfg.flags & PACE_FP8_WINDOW) != 0; }
+    pace::WindowView window_view(const uint8_t *active) const {
+        pace::WindowView w;
+        const size_t states = (size_t)cfg.batch * cfg.heads;
+        w.codes = win_codes;
+        w.f = win_f;
+        w.count = win_meta;
+        w.head = win_meta + states;
+        w.lam = win_lam;
+        w.active = active;
+        w.S = cfg.fp8_window;
+        return w;
+    }
 };
 
 namespace {
@@ -139,8 +157,14 @@ PACE_API int pace_state_alloc(const pace_config *cfg, int init_kind, const void 
     if (rc) return rc;
     if (cfg->period < 1 || cfg->period > 64) return fail(PACE_EUNSUPPORTED, "period must be 1..64");
     if ((rc = check_dtype(cfg->in_dtype))) return rc;
-    if (cfg->flags & ~(PACE_STATS_ERR | PACE_STEP_BUFFER | PACE_ADAPTIVE))
+    if (cfg->flags & ~(PACE_STATS_ERR | PACE_STEP_BUFFER | PACE_ADAPTIVE | PACE_FP8_WINDOW))
         return fail(PACE_EINVAL, "unknown flags 0x%x", cfg->flags);
+    if (cfg->flags & PACE_FP8_WINDOW) {
+        if (cfg->flags & (PACE_STEP_BUFFER | PACE_ADAPTIVE))
+            return fail(PACE_EINVAL, "PACE_FP8_WINDOW excludes PACE_STEP_BUFFER and PACE_ADAPTIVE");
+        if (cfg->fp8_window < 1 || cfg->fp8_window > 64)
+            return fail(PACE_EINVAL, "fp8_window must be 1..64");
+    }
     if (cfg->flags & PACE_ADAPTIVE) {
         if (!(cfg->flags & PACE_STEP_BUFFER)) return fail(PACE_EINVAL, "PACE_ADAPTIVE needs PACE_STEP_BUFFER");
         if (!(cfg->adapt_tau > 0.f) || !(cfg->adapt_tau < 3.0e38f))
@@ -197,6 +221,10 @@ PACE_API int pace_state_alloc(const pace_config *cfg, int init_kind, const void 
         if (st->step_ab) (void)hipFree(st->step_ab);
         if (st->step_fill) (void)hipFree(st->step_fill);
         if (st->adapt) (void)hipFree(st->adapt);
+        if (st->win_codes) (void)hipFree(st->win_codes);
+        if (st->win_f) (void)hipFree(st->win_f);
+        if (st->win_meta) (void)hipFree(st->win_meta);
+        if (st->win_lam) (void)hipFree(st->win_lam);
         delete st;
         (void)code;
         return hip_fail(err, what);
@@ -263,6 +291,25 @@ PACE_API int pace_state_alloc(const pace_config *cfg, int init_kind, const void 
         if ((e = hipMemcpyAsync(st->scales, src, st->bytes_scales, hipMemcpyDeviceToDevice, s)) != hipSuccess)
             return cleanup(0, "raw copy scales", e);
     }
+    if (cfg->flags & PACE_FP8_WINDOW) {
+        const size_t states = (size_t)cfg->batch * cfg->heads, S = (size_t)cfg->fp8_window;
+        const size_t b_codes = states * S * (cfg->d_k + cfg->d_v), b_f = states * S * 12;
+        st->bytes_step = b_codes + b_f + states * 12;
+        if ((e = hipMalloc((void **)&st->win_codes, b_codes)) != hipSuccess)
+            return cleanup(0, "hipMalloc(fp8 window)", e);
+        if ((e = hipMalloc((void **)&st->win_f, b_f)) != hipSuccess)
+            return cleanup(0, "hipMalloc(fp8 window scales)", e);
+        if ((e = hipMalloc((void **)&st->win_meta, states * 8)) != hipSuccess)
+            return cleanup(0, "hipMalloc(fp8 window counts)", e);
+        if ((e = hipMalloc((void **)&st->win_lam, states * 4)) != hipSuccess)
+            return cleanup(0, "hipMalloc(fp8 window decay)", e);
+        if ((e = hipMemsetAsync(st->win_meta, 0, states * 8, s)) != hipSuccess)
+            return cleanup(0, "zero fp8 window counts", e);
+        std::vector<float> ones(states, 1.f);
+        if ((e = hipMemcpyAsync(st->win_lam, ones.data(), states * 4, hipMemcpyHostToDevice, s)) != hipSuccess ||
+            (e = hipStreamSynchronize(s)) != hipSuccess)
+            return cleanup(0, "init fp8 window decay", e);
+    }
     if (st->adapt && (e = pace::launch_adapt_init(st->view(), st->adapt, s)) != hipSuccess)
         return cleanup(0, "adaptive period init", e);
     // the host copy of the head map must outlive the async copy: wait for it
@@ -285,6 +332,10 @@ PACE_API int pace_state_free(pace_state *st) {
     if (st->step_ab) (void)hipFree(st->step_ab);
     if (st->step_fill) (void)hipFree(st->step_fill);
     if (st->adapt) (void)hipFree(st->adapt);
+    if (st->win_codes) (void)hipFree(st->win_codes);
+    if (st->win_f) (void)hipFree(st->win_f);
+    if (st->win_meta) (void)hipFree(st->win_meta);
+    if (st->win_lam) (void)hipFree(st->win_lam);
     delete st;
     if (e != hipSuccess) return hip_fail(e, "pace_state_free");
     return ok();
@@ -306,8 +357,8 @@ PACE_API int pace_decode_period(pace_state *st, int32_t n_tok, const void *q, co
                                 const void *v, const float *alpha, const float *beta,
                                 float *out, void *stream) {
     if (!st) return fail(PACE_EINVAL, "null state handle");
-    if (st->stepped())
-        return fail(PACE_EINVAL, "a PACE_STEP_BUFFER handle decodes with pace_decode_step");
+    if (st->stepped() || st->windowed())
+        return fail(PACE_EINVAL, "a per-step handle decodes with pace_decode_step");
     if (n_tok < 1 || n_tok > st->cfg.period)
         return fail(PACE_EINVAL, "n_tok = %d outside 1..period (%d)", n_tok, st->cfg.period);
     int rc = check_tokens(n_tok, st->cfg.in_dtype, q, k, v, alpha, beta);
@@ -333,8 +384,8 @@ PACE_API int pace_prefill_encode(pace_state *st, int32_t n_tok, const void *q, c
                                  const void *v, const float *alpha, const float *beta,
                                  float *out, void *stream) {
     if (!st) return fail(PACE_EINVAL, "null state handle");
-    if (st->stepped())
-        return fail(PACE_EINVAL, "a PACE_STEP_BUFFER handle decodes with pace_decode_step");
+    if (st->stepped() || st->windowed())
+        return fail(PACE_EINVAL, "a per-step handle decodes with pace_decode_step");
     if (n_tok < 1) return fail(PACE_EINVAL, "n_tok must be >= 1");
     int rc = check_tokens(n_tok, st->cfg.in_dtype, q, k, v, alpha, beta);
     if (rc) return rc;
@@ -357,12 +408,20 @@ PACE_API int pace_decode_step(pace_state *st, const void *q, const void *k, cons
                               const float *alpha, const float *beta, const uint8_t *active,
                               float *out, void *stream) {
     if (!st) return fail(PACE_EINVAL, "null state handle");
-    if (!st->stepped()) return fail(PACE_EINVAL, "the handle was not allocated with PACE_STEP_BUFFER");
+    if (!st->stepped() && !st->windowed())
+        return fail(PACE_EINVAL, "the handle was not allocated with PACE_STEP_BUFFER or PACE_FP8_WINDOW");
     int rc = check_tokens(1, st->cfg.in_dtype, q, k, v, alpha, beta);
     if (rc) return rc;
     if (!out || !aligned(out, 16)) return fail(PACE_EINVAL, "out must be a 16-byte aligned device pointer");
     hipStream_t s = (hipStream_t)stream;
     const int bf16 = st->cfg.in_dtype == PACE_DTYPE_BF16;
+    if (st->windowed()) {
+        hipError_t e = pace::launch_window_step(st->view(), st->window_view(active), q, k, v, alpha,
+                                                beta, out, bf16, s);
+        if (e != hipSuccess) return hip_fail(e, "window step launch");
+        st->tokens += 1;
+        return ok();
+    }
     const pace::StepView sv = st->step_view(active);
     hipError_t e;
     if (pace::mfma_step_supported(st->cfg.d_k, st->cfg.d_v, st->cfg.period, bf16,
@@ -378,6 +437,11 @@ PACE_API int pace_decode_step(pace_state *st, const void *q, const void *k, cons
 
 PACE_API int pace_flush_steps(pace_state *st, void *stream) {
     if (!st) return fail(PACE_EINVAL, "null state handle");
+    if (st->windowed()) {
+        hipError_t e = pace::launch_window_flush(st->view(), st->window_view(nullptr), (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "window flush launch");
+        return ok();
+    }
     if (!st->stepped()) return fail(PACE_EINVAL, "the handle was not allocated with PACE_STEP_BUFFER");
     hipError_t e = pace::launch_flush_v0(st->view(), st->step_view(nullptr),
                                          st->cfg.in_dtype == PACE_DTYPE_BF16, (hipStream_t)stream);
@@ -407,8 +471,20 @@ PACE_API int pace_read_state(const pace_state *st, int what, void *dst, float *s
         d += st->bytes8;
         if (e == hipSuccess)
             e = hipMemcpyAsync(d, st->scales, st->bytes_scales, hipMemcpyDeviceToDevice, s);
+    } else if (what == PACE_READ_STEP && st->windowed()) {
+        const size_t states = (size_t)st->cfg.batch * st->cfg.heads;
+        e = hipMemcpyAsync(dst, st->win_meta, states * 4, hipMemcpyDeviceToDevice, s);
+        if (e == hipSuccess && scales_dst)
+            e = pace::launch_window_meta(st->window_view(nullptr), scales_dst, states, s);
+    } else if (what == PACE_READ_WINDOW) {
+        if (!st->windowed()) return fail(PACE_EINVAL, "PACE_READ_WINDOW needs a PACE_FP8_WINDOW handle");
+        const size_t states = (size_t)st->cfg.batch * st->cfg.heads, S = (size_t)st->cfg.fp8_window;
+        e = hipMemcpyAsync(dst, st->win_codes, states * S * (st->cfg.d_k + st->cfg.d_v),
+                           hipMemcpyDeviceToDevice, s);
+        if (e == hipSuccess && scales_dst)
+            e = hipMemcpyAsync(scales_dst, st->win_f, states * S * 12, hipMemcpyDeviceToDevice, s);
     } else if (what == PACE_READ_STEP) {
-        if (!st->stepped()) return fail(PACE_EINVAL, "PACE_READ_STEP needs a PACE_STEP_BUFFER handle");
+        if (!st->stepped()) return fail(PACE_EINVAL, "PACE_READ_STEP needs a per-step handle");
         const size_t states = (size_t)st->cfg.batch * st->cfg.heads;
         e = hipMemcpyAsync(dst, st->step_fill, states * 4, hipMemcpyDeviceToDevice, s);
         if (e == hipSuccess && scales_dst)

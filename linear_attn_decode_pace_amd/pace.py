@@ -34,10 +34,12 @@ PACE_READ_CODES = 0
 PACE_READ_DEQUANT = 1
 PACE_READ_RAW = 2
 PACE_READ_STEP = 3
+PACE_READ_WINDOW = 4
 
 PACE_STATS_ERR = 0x1
 PACE_STEP_BUFFER = 0x2
 PACE_ADAPTIVE = 0x4
+PACE_FP8_WINDOW = 0x8
 PACE_STATS_MAX_HEADS = 256
 
 EXPORTED = ("pace_abi_version", "pace_last_error", "pace_state_alloc", "pace_state_free",
@@ -58,7 +60,7 @@ class pace_config(ctypes.Structure):
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("period", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
                 ("head_bits", ctypes.POINTER(ctypes.c_uint8)), ("flags", ctypes.c_uint32),
-                ("adapt_tau", ctypes.c_float)]
+                ("adapt_tau", ctypes.c_float), ("fp8_window", ctypes.c_int32)]
 
 
 class pace_stats(ctypes.Structure):
@@ -147,11 +149,13 @@ def _stream(stream) -> Optional[int]:
 
 def pace_state_alloc(batch: int, heads: int, d_k: int, d_v: int, period: int, in_dtype: int,
                      head_bits: Sequence[int], init_kind: int = PACE_INIT_ZERO, init=None,
-                     flags: int = 0, stream=None, adapt_tau: float = 0.0) -> int:
+                     flags: int = 0, stream=None, adapt_tau: float = 0.0,
+                     fp8_window: int = 0) -> int:
     """Allocate and initialise the pools; returns the opaque handle (an int)."""
     hb = (ctypes.c_uint8 * max(1, len(head_bits)))(*[int(b) for b in head_bits])
     cfg = pace_config(batch, heads, d_k, d_v, period, in_dtype,
-                      ctypes.cast(hb, ctypes.POINTER(ctypes.c_uint8)), flags, adapt_tau)
+                      ctypes.cast(hb, ctypes.POINTER(ctypes.c_uint8)), flags, adapt_tau,
+                      fp8_window)
     out = ctypes.c_void_p()
     _check(LIB.pace_state_alloc(ctypes.byref(cfg), init_kind, _ptr(init), _stream(stream),
                                 ctypes.byref(out)))
@@ -168,7 +172,7 @@ def pace_state_config(st: int) -> dict:
     return {"batch": c.batch, "heads": c.heads, "d_k": c.d_k, "d_v": c.d_v,
             "period": c.period, "in_dtype": c.in_dtype,
             "head_bits": [c.head_bits[i] for i in range(c.heads)], "flags": c.flags,
-            "adapt_tau": c.adapt_tau}
+            "adapt_tau": c.adapt_tau, "fp8_window": c.fp8_window}
 
 
 def pace_raw_bytes(st: int) -> int:

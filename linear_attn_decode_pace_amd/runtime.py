@@ -55,13 +55,14 @@ class State:
     def __init__(self, w: inputs.Workload, head_bits: Sequence[int],
                  init_kind: int = pace.PACE_INIT_ZERO, init: Optional[torch.Tensor] = None,
                  period: Optional[int] = None, stream=None, flags: int = 0,
-                 adapt_tau: float = 0.0):
+                 adapt_tau: float = 0.0, fp8_window: int = 0):
         self.w = w
         self.head_bits = np.asarray(head_bits, dtype=np.uint8)
         self.period = w.period if period is None else period
+        self.fp8_window = fp8_window
         self.handle = pace.pace_state_alloc(w.B, w.H, w.dk, w.dv, self.period, dtype_code(w),
                                             list(self.head_bits), init_kind, init, flags, stream,
-                                            adapt_tau)
+                                            adapt_tau, fp8_window)
 
     def free(self):
         if self.handle:
@@ -102,6 +103,15 @@ class State:
         ar = torch.empty((w.B, w.H, 2), dtype=torch.float32, device="cuda")
         pace.pace_read_state(self.handle, pace.PACE_READ_STEP, fill, ar, stream)
         return fill, ar
+
+    def read_window(self, stream=None):
+        """FP8 window of a PACE_FP8_WINDOW handle: codes [B, H, S, d_k + d_v]
+        (uint8) and per slot (k scale, u scale, decay) [B, H, S, 3]."""
+        w, S = self.w, self.fp8_window
+        codes = torch.empty((w.B, w.H, S, w.dk + w.dv), dtype=torch.uint8, device="cuda")
+        f = torch.empty((w.B, w.H, S, 3), dtype=torch.float32, device="cuda")
+        pace.pace_read_state(self.handle, pace.PACE_READ_WINDOW, codes, f, stream)
+        return codes, f
 
     def read_codes(self, stream=None):
         w = self.w

@@ -7,7 +7,9 @@ Tolerances (relative L2 unless stated):
 * scales: 1e-5 relative, zero equals zero;
 * codes: equal, except +-1 flips where the oracle's quotient M / s lies within
   1e-3 of a half-integer (a rounding tie that float32 and float64 may resolve
-  differently), on at most 0.1% of the entries;
+  differently), on at most 0.1% of the entries (for a merge of the FP8 write
+  window, on at most the entries the oracle holds within 1e-5 of a tie: a
+  column dominated by an E4M3 write has its quotients on exact half-integers);
 * dequantized state: 2e-3 per tile and aggregated over all checked tiles,
   with the entries of allowed flips masked.  A single allowed 4-bit flip moves
   one entry by a whole code step (1/7 of its column's largest entry), which by
@@ -72,9 +74,12 @@ class Report:
                       max(self.max_scale, o.max_scale))
 
 
-def check_encoded(codes, scales, ref_codes, ref_scales, M_ref, what="") -> Report:
+def check_encoded(codes, scales, ref_codes, ref_scales, M_ref, what="",
+                  lattice_ties=False) -> Report:
     """GPU codes/scales against the oracle's encode of M_ref (the high-precision
-    state the oracle had just before encoding)."""
+    state the oracle had just before encoding).  lattice_ties: states whose
+    quotients sit on exact rounding ties by construction (FP8 writes merged
+    into the history) may flip every such tie, not only 0.1% of entries."""
     codes = np.asarray(codes).astype(np.int16)
     ref_codes = np.asarray(ref_codes).astype(np.int16)
     scales = np.asarray(scales, dtype=np.float64)
@@ -96,7 +101,10 @@ def check_encoded(codes, scales, ref_codes, ref_scales, M_ref, what="") -> Repor
         x = quant.quotients(M_ref, ref_scales)
         td = quant.tie_distance(x)[flips]
         assert td.max() < TIE_TOL, f"{what}: code flip away from a rounding tie (distance {td.max():.3g})"
-    assert rep.flips <= MAX_FLIP_FRAC * rep.entries, f"{what}: {rep.flips} flips of {rep.entries}"
+    budget = MAX_FLIP_FRAC * rep.entries
+    if lattice_ties and rep.flips:
+        budget = max(budget, int((quant.tie_distance(quant.quotients(M_ref, ref_scales)) < 1e-5).sum()))
+    assert rep.flips <= budget, f"{what}: {rep.flips} flips of {rep.entries}"
     # dequantized state
     D = codes.astype(np.float64) * scales[..., None, :]
     Dr = ref_codes.astype(np.float64) * ref_scales[..., None, :]

@@ -41,7 +41,7 @@ def _alloc_status(init_kind=pace.PACE_INIT_ZERO, init=None, flags=0, **kw):
     hb = (ctypes.c_uint8 * max(1, len(c["head_bits"])))(*c["head_bits"])
     cfg = pace.pace_config(c["batch"], c["heads"], c["d_k"], c["d_v"], c["period"], c["in_dtype"],
                            ctypes.cast(hb, ctypes.POINTER(ctypes.c_uint8)), flags,
-                           c.get("adapt_tau", 0.0))
+                           c.get("adapt_tau", 0.0), c.get("fp8_window", 0))
     out = ctypes.c_void_p()
     return pace.LIB.pace_state_alloc(ctypes.byref(cfg), init_kind, init, None, ctypes.byref(out))
 
@@ -63,7 +63,10 @@ def test_alloc_rejects_bad_config(kw, status):
 
 
 def test_alloc_rejects_bad_flags():
-    assert _alloc_status(flags=8) == pace.PACE_EINVAL
+    assert _alloc_status(flags=16) == pace.PACE_EINVAL
+    for bad in (0, 65):
+        assert _alloc_status(flags=pace.PACE_FP8_WINDOW, fp8_window=bad) == pace.PACE_EINVAL
+    assert _alloc_status(flags=pace.PACE_FP8_WINDOW | pace.PACE_STEP_BUFFER, fp8_window=8) == pace.PACE_EINVAL
     assert _alloc_status(flags=pace.PACE_ADAPTIVE, adapt_tau=0.5) == pace.PACE_EINVAL   # needs steps
     both = pace.PACE_ADAPTIVE | pace.PACE_STEP_BUFFER
     for tau in (0.0, -1.0, float("inf"), float("nan")):

@@ -1,0 +1,132 @@
+"""FP8 write window (PACE_FP8_WINDOW) on the GPU against oracle/window.py.
+
+A column dominated by a merged FP8 write has its quotients at 7 (or 127)
+times an E4M3 value over the largest, i.e. on exact half-integers, so a
+merge's encode may flip every such tie (each flip still within the tie
+tolerance); see parity.check_encoded(lattice_ties).
+
+Transition validity, step by step: before every step the oracle is rebuilt
+from what the GPU stores (the history's codes and scales, its decay, and the
+window's E4M3 codes, scales and decays in ring order), then both take the
+step.  Outputs must agree to float32 accuracy; the new write's E4M3 codes must
+be equal except where the oracle's float32 quotient sits on a rounding
+midpoint; a merge's history encode is checked like every other encode.
+"""
+import numpy as np
+import pytest
+
+from linear_attn_decode_pace_amd import inputs
+from oracle import window
+from tests import parity
+from tests.gpu_cases import say, tok_tiles
+
+pytestmark = pytest.mark.gpu
+
+MID_TOL = 1e-4  # relative distance of a quotient to an E4M3 rounding midpoint
+
+
+def _midpoint_distance(q: np.ndarray) -> np.ndarray:
+    """Distance of each float32 quotient to the nearest E4M3 midpoint, in quanta."""
+    a = np.abs(q.astype(np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    quantum = np.where(a < 2.0 ** -6, 2.0 ** -9, 2.0 ** (e - 3))
+    x = a / quantum
+    return np.abs(np.abs(x - np.floor(x)) - 0.5)
+
+
+def _gpu_state(st, w, S):
+    n = w.B * w.H
+    c, s = st.read_codes()
+    wc, wf = st.read_window()
+    cnt, meta = st.read_step()
+    return (c.reshape(n, w.dk, w.dv).cpu().numpy(), s.reshape(n, w.dv).cpu().numpy(),
+            wc.reshape(n, S, w.dk + w.dv).cpu().numpy(), wf.reshape(n, S, 3).cpu().numpy(),
+            cnt.reshape(n).cpu().numpy(), meta.reshape(n, 2).cpu().numpy())
+
+
+def _oracle_from(gpu, bits, S, dk):
+    c, s, wc, wf, cnt, meta = gpu
+    ref = window.Window(c, s, bits, S)
+    for i in range(c.shape[0]):
+        ref.lam[i] = float(meta[i, 0])
+        head = int(meta[i, 1])
+        for e in range(int(cnt[i])):
+            slot = (head + e) % S
+            ref.win[i].append([wc[i, slot, :dk].copy(), np.float32(wf[i, slot, 0]),
+                               wc[i, slot, dk:].copy(), np.float32(wf[i, slot, 1]),
+                               float(wf[i, slot, 2])])
+    return ref
+
+
+@pytest.mark.parametrize("name,kw,S", [
+    ("win-s4", dict(B=2, H=3, n_int8=1, n_outliers=8, steps=14), 4),
+    ("win-s1", dict(B=2, H=2, n_int8=1, steps=6), 1),
+    ("win-d64", dict(B=3, H=2, dk=64, dv=64, n_int8=1, steps=10), 3),
+    ("win-f32", dict(B=2, H=2, n_int8=1, dtype=inputs.DT_F32, steps=8), 2),
+])
+def test_window_steps_against_oracle(name, kw, S):
+    from linear_attn_decode_pace_amd import pace, runtime
+    w = inputs.ragged(name, 250, **kw)
+    seed = 0
+    say(f"[case] fp8 window {name} S={S}")
+    n = w.B * w.H
+    idx = np.arange(n)
+    bits = np.tile(inputs.head_bits(w, seed), w.B).astype(np.int64)
+    st = runtime.State(w, inputs.head_bits(w, seed), pace.PACE_INIT_F32,
+                       runtime.warmup_state(w, seed), flags=pace.PACE_FP8_WINDOW, fp8_window=S)
+    flips = entries = merges = 0
+    for t in range(w.steps):
+        before = _gpu_state(st, w, S)
+        ref = _oracle_from(before, bits, S, w.dk)
+        cnt0, head0 = before[4], before[5][:, 1].astype(int)
+        tok = inputs.tokens(w, seed, inputs.SEG_DECODE, t, t + 1)
+        out = runtime.out_buffer(w, 1)
+        st.step(runtime.DeviceTokens(tok), out)
+        q, k, v, a, b = [x[0] for x in tok_tiles(tok, idx, w.H)]
+        o_ref = ref.step(q, k, v, a, b)
+        parity.check_outputs(out.reshape(1, n, w.dv).cpu().numpy(), o_ref[None], f"{name} step {t}")
+        c, s, wc, wf, cnt, meta = _gpu_state(st, w, S)
+        for i in range(n):
+            slot = (head0[i] + cnt0[i]) % S
+            kc, ks, uc, us, _ = ref.win[i][-1]
+            assert np.array_equal(wc[i, slot, :w.dk], kc) and wf[i, slot, 0] == ks, f"{name} step {t} key"
+            assert abs(wf[i, slot, 1] - us) <= 1e-6 * us, f"{name} step {t} u scale"
+            diff = wc[i, slot, w.dk:] != uc
+            if diff.any():
+                # the oracle's quotients of the differing codes must sit on a midpoint
+                M = _oracle_from(before, bits, S, w.dk).state(i)
+                u = b[i] * (v[i] - a[i] * (k[i] @ M))
+                qv = np.clip(np.asarray(u, np.float32) / np.float32(us), -448, 448)
+                assert np.all(_midpoint_distance(qv[diff]) < MID_TOL), f"{name} step {t} u codes"
+                flips += int(diff.sum())
+            entries += w.dv
+        np.testing.assert_array_equal(cnt, [len(x) for x in ref.win])
+        np.testing.assert_allclose(meta[:, 0], ref.lam, rtol=1e-6)
+        merged = cnt0 == S
+        if merged.any():
+            merges += int(merged.sum())
+            pre = np.stack([ref.last_pre[i] for i in np.nonzero(merged)[0]])
+            parity.check_encoded(c[merged], s[merged], ref.codes[merged], ref.scales[merged], pre,
+                                 f"{name} step {t} merge", lattice_ties=True)
+        # decays of the window, oldest first, against the oracle's
+        for i in range(n):
+            head = int(meta[i, 1])
+            got = [wf[i, (head + e) % S, 2] for e in range(int(cnt[i]))]
+            np.testing.assert_allclose(got, [e_[4] for e_ in ref.win[i]], rtol=1e-6)
+    assert merges > 0 or S >= w.steps
+    assert flips <= 1e-3 * entries
+    say(f"[case] {name}: {merges} merges, {flips} FP8 tie flips of {entries} codes")
+    # flush: the whole window into the history
+    before = _gpu_state(st, w, S)
+    ref = _oracle_from(before, bits, S, w.dk)
+    st.flush_steps()
+    ref.flush()
+    c, s, wc, wf, cnt, meta = _gpu_state(st, w, S)
+    assert not cnt.any() and np.all(meta[:, 0] == 1.0)
+    full = before[4] > 0
+    pre = np.stack([ref.last_pre[i] for i in np.nonzero(full)[0]])
+    parity.check_encoded(c[full], s[full], ref.codes[full], ref.scales[full], pre, f"{name} flush",
+                         lattice_ties=True)
+    s_ = st.stats()
+    assert s_["bytes_step_buffer"] == n * (S * (w.dk + w.dv + 12) + 12)
+    st.free()
