@@ -7,17 +7,13 @@
 // column-quantized as every other state here and decays through one factor
 // lam.  When a write leaves the window it is merged into the history, which
 // is then re-encoded.
+#include "column_codec.h"
 #include "pace_window.h"
 
 namespace pace {
 namespace {
 
 constexpr float E4M3_MAX = 448.f;
-
-__device__ inline float ld_in_w(const void *p, size_t idx, int bf16) {
-    if (bf16) return __uint_as_float((uint32_t)((const uint16_t *)p)[idx] << 16);
-    return ((const float *)p)[idx];
-}
 
 // nearest E4M3 code of x (|x| <= 448), ties to even: 3 mantissa bits from
 // float32's 23; below 2^-6 the quantum is 2^-9
@@ -51,66 +47,6 @@ __device__ inline float e4m3_decode(uint8_t c) {
     return (c & 0x80u) ? -v : v;
 }
 
-template <int DK>
-__device__ inline void load_col(const PoolView &p, const uint8_t *codes, int bits, int j, float s,
-                                float M[DK]) {
-#pragma unroll
-    for (int i = 0; i < DK; ++i) {
-        int c;
-        if (bits == 4) {
-            int sh;
-            const size_t o = loc4(DK, i, j, &sh);
-            c = ((int)((uint32_t)codes[o] << (28 - sh))) >> 28;
-        } else {
-            c = (int)(int8_t)codes[loc8(DK, i, j)];
-        }
-        M[i] = (float)c * s;
-    }
-}
-
-// column quantizer (absmax / qmax, nearest even), as the other encoders here
-template <int DK>
-__device__ inline float store_col(uint8_t *codes, int bits, int j, const float M[DK], float *err) {
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < DK; ++i) amax = fmaxf(amax, fabsf(M[i]));
-    const int qm = bits == 4 ? 7 : 127;
-    const float s = amax / (float)qm;
-    float e2 = 0.f, m2 = 0.f;
-#pragma unroll
-    for (int i = 0; i < DK; ++i) {
-        int c = 0;
-        if (s > 0.f) c = (int)fminf(fmaxf(rintf(M[i] / s), -(float)qm), (float)qm);
-        if (err) {
-            const float d = M[i] - (float)c * s;
-            e2 += d * d;
-            m2 += M[i] * M[i];
-        }
-        if (bits == 4) {
-            int sh;
-            const size_t o = loc4(DK, i, j, &sh);
-            codes[o] = (uint8_t)((codes[o] & ~(0xf << sh)) | ((c & 15) << sh));
-        } else {
-            codes[loc8(DK, i, j)] = (uint8_t)(int8_t)c;
-        }
-    }
-    if (err) {
-        err[0] = e2;
-        err[1] = m2;
-    }
-    return s;
-}
-
-__device__ inline float block_max(float x, float *red) {
-    for (int m = 32; m > 0; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-    __syncthreads();
-    float t = 0.f;
-    for (int w = 0; w < (int)(blockDim.x + 63) / 64; ++w) t = fmaxf(t, red[w]);
-    return t;
-}
-
 // one step for the state `tile`: thread j owns column j (blockDim = d_v)
 template <int DK>
 __global__ void __launch_bounds__(256) window_step_kernel(PoolView p, WindowView wv, const void *q, const void *k,
@@ -130,7 +66,7 @@ __global__ void __launch_bounds__(256) window_step_kernel(PoolView p, WindowView
 
     // M_{t-1}, column j: lam * history + the decayed FP8 writes of the window
     float M[DK];
-    load_col<DK>(p, codes, bits, j, sc[j], M);
+    load_column<DK>(codes, bits, j, sc[j], M);
 #pragma unroll
     for (int i = 0; i < DK; ++i) M[i] *= lam;
     for (int e = 0; e < cnt; ++e) {
@@ -145,15 +81,15 @@ __global__ void __launch_bounds__(256) window_step_kernel(PoolView p, WindowView
     }
     // this token
     for (int i = j; i < DK; i += blockDim.x) {
-        sk[i] = ld_in_w(k, (size_t)tile * DK + i, bf16);
-        sq[i] = ld_in_w(q, (size_t)tile * DK + i, bf16);
+        sk[i] = ld_in(k, (size_t)tile * DK + i, bf16);
+        sq[i] = ld_in(q, (size_t)tile * DK + i, bf16);
     }
     __syncthreads();
     const float a = alpha[tile], bt = beta[tile];
     float d = 0.f;
 #pragma unroll
     for (int i = 0; i < DK; ++i) d = fmaf(sk[i], M[i], d);
-    const float u = bt * (ld_in_w(v, (size_t)tile * p.dv + j, bf16) - a * d);
+    const float u = bt * (ld_in(v, (size_t)tile * p.dv + j, bf16) - a * d);
     float o = 0.f;
 #pragma unroll
     for (int i = 0; i < DK; ++i) o = fmaf(sq[i], fmaf(a, M[i], sk[i] * u), o);
@@ -171,10 +107,10 @@ __global__ void __launch_bounds__(256) window_step_kernel(PoolView p, WindowView
         __syncthreads();
         const float w = e4m3_decode(c[DK + j]) * wf[3 * head + 1] * delta_o;
         // M is no longer needed: reuse its registers for the history column
-        load_col<DK>(p, codes, bits, j, sc[j], M);
+        load_column<DK>(codes, bits, j, sc[j], M);
 #pragma unroll
         for (int i = 0; i < DK; ++i) M[i] = fmaf(kw[i], w, lam_new * M[i]);
-        sc[j] = store_col<DK>(codes, bits, j, M,
+        sc[j] = store_column<DK>(codes, bits, j, M,
                               p.colerr ? p.colerr + ((size_t)tile * p.dv + j) * 2 : nullptr);
     }
     // the new write (k_t, u_t) in E4M3, one scale per vector
@@ -220,7 +156,7 @@ __global__ void __launch_bounds__(256) window_flush_kernel(PoolView p, WindowVie
     uint8_t *codes = tile_codes(p, b, h, &bits);
     float *sc = p.scales + (size_t)tile * p.dv;
     float H[DK];
-    load_col<DK>(p, codes, bits, j, sc[j], H);
+    load_column<DK>(codes, bits, j, sc[j], H);
 #pragma unroll
     for (int i = 0; i < DK; ++i) H[i] *= lam;
     for (int e = 0; e < cnt; ++e) {
@@ -233,7 +169,7 @@ __global__ void __launch_bounds__(256) window_flush_kernel(PoolView p, WindowVie
 #pragma unroll
         for (int i = 0; i < DK; ++i) H[i] = fmaf(kw[i], w, H[i]);
     }
-    sc[j] = store_col<DK>(codes, bits, j, H,
+    sc[j] = store_column<DK>(codes, bits, j, H,
                           p.colerr ? p.colerr + ((size_t)tile * p.dv + j) * 2 : nullptr);
     __syncthreads();
     if (j == 0) {
