@@ -1,0 +1,125 @@
+// Token-only matrices of a 16-token chunk, shared by the 16-token decode
+// kernel (decode_mfma16.hip) and the prefill (prefill_mfma.hip).  One
+// wavefront computes them from the chunk's k_t, q_t (bf16 rows in LDS, row
+// stride ROW elements) and alpha_t, beta_t:
+//   kk[t][s] = k_t . k_s,  qk[t][s] = q_t . k_s                (Gram on MFMA)
+//   Gamma_ts = prod_{s<r<=t} alpha_r, gam[t] = Gamma_t,-1, gamC[t] = Gamma_15,t
+//   A = strictly lower (Gamma * kk),  Lq = lower incl. diagonal (Gamma * qk)
+//   Tt = ((I + diag(beta) A)^-1 diag(beta))^T                  (UT transform)
+//   LqT = Lq T                                                  (float32 MFMA)
+// Gates are products of alpha (no log / exp).  All arrays live in LDS; each
+// step ends with the wavefront's LDS writes visible to it (wave_sync).
+#pragma once
+
+#include "mfma_common.h"
+
+namespace pace {
+namespace {
+
+constexpr int CK = 16;  // tokens per chunk
+
+// Gram products: the A row m of the K (Q) block is token 4 (m % 4) + m / 4,
+// so output row 4 g + r is token 4 r + g
+template <int DK, int ROW>
+__device__ inline void chunk16_gram(const uint16_t (*kq)[ROW], float (*kk)[CK], float (*qk)[CK],
+                                    int lane) {
+    constexpr int NKS = DK / 32;
+    const int g = lane >> 4, n = lane & 15;
+    const int tok_n = 4 * (n & 3) + (n >> 2);
+    f32x4 GK = {0.f, 0.f, 0.f, 0.f}, GQ = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        const int c0 = 32 * ks + 4 * g, c1 = c0 + 16;
+        const u32x2 k0 = *(const u32x2 *)&kq[tok_n][c0], k1 = *(const u32x2 *)&kq[tok_n][c1];
+        const u32x2 q0 = *(const u32x2 *)&kq[CK + tok_n][c0], q1 = *(const u32x2 *)&kq[CK + tok_n][c1];
+        const u32x2 s0 = *(const u32x2 *)&kq[n][c0], s1 = *(const u32x2 *)&kq[n][c1];
+        const bf16x8 BG = __builtin_bit_cast(bf16x8, u32x4{s0[0], s0[1], s1[0], s1[1]});
+        GK = mfma_bf16_k32(__builtin_bit_cast(bf16x8, u32x4{k0[0], k0[1], k1[0], k1[1]}), BG, GK);
+        GQ = mfma_bf16_k32(__builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]}), BG, GQ);
+    }
+    wave_sync();  // the A operands are read before kk / qk may alias them
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        kk[4 * r + g][n] = GK[r];
+        qk[4 * r + g][n] = GQ[r];
+    }
+    wave_sync();
+}
+
+// gates, A and Lq: lane -> row t = lane / 4, columns s0 .. s0 + 3 with
+// s0 = 4 (lane % 4): Gamma_{t,s0+3} as one masked product, then the running
+// product down to s0
+__device__ inline void chunk16_gates(const float *alpha, const float (*kk)[CK],
+                                     const float (*qk)[CK], float (*A)[CK], float (*Lq)[CK],
+                                     float *gam, float *gamC, int lane) {
+    float al[CK];
+#pragma unroll
+    for (int r = 0; r < CK; ++r) al[r] = alpha[r];
+    const int t = lane >> 2, s0 = 4 * (lane & 3);
+    float gts = 1.f;
+#pragma unroll
+    for (int r = 1; r < CK; ++r) gts *= (r > s0 + 3 && r <= t) ? al[r] : 1.f;
+    float a_row[4], l_row[4];
+#pragma unroll
+    for (int e = 3; e >= 0; --e) {
+        const int s = s0 + e;
+        a_row[e] = s < t ? gts * kk[t][s] : 0.f;
+        l_row[e] = s <= t ? gts * qk[t][s] : 0.f;
+        if (e > 0 && s <= t) gts *= alpha[s];  // Gamma_{t,s-1} = Gamma_{t,s} alpha_s
+    }
+    wave_sync();  // kk / qk are read before A / Lq may alias them
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        A[t][s0 + e] = a_row[e];
+        Lq[t][s0 + e] = l_row[e];
+    }
+    if (lane < CK) {
+        float gm = 1.f, gc = 1.f;
+#pragma unroll
+        for (int r = 0; r < CK; ++r) {
+            gm *= r <= lane ? al[r] : 1.f;
+            gc *= r > lane ? al[r] : 1.f;
+        }
+        gam[lane] = gm;
+        gamC[lane] = gc;
+    }
+    wave_sync();
+}
+
+// UT transform: column s of Z = (I + diag(beta) A)^-1 by forward
+// substitution (one column per lane), T = Z diag(beta), stored transposed
+__device__ inline void chunk16_ut(const float (*A)[CK], const float *beta, float (*Tt)[CK],
+                                  int lane) {
+    const int s = lane & 15;
+    float be[CK], z[CK];
+#pragma unroll
+    for (int r = 0; r < CK; ++r) be[r] = beta[r];
+#pragma unroll
+    for (int t = 0; t < CK; ++t) {
+        float sum = 0.f;
+#pragma unroll
+        for (int u = 0; u < t; ++u) sum = fmaf(A[t][u], z[u], sum);
+        z[t] = (t == s ? 1.f : 0.f) - be[t] * sum;
+    }
+    if (lane < CK) {
+#pragma unroll
+        for (int t = 0; t < CK; ++t) Tt[s][t] = z[t] * be[s];
+    }
+    wave_sync();
+}
+
+// Lq T on float32 MFMA: step st takes column / row 4 st + g
+__device__ inline void chunk16_lqt(const float (*Lq)[CK], const float (*Tt)[CK], float (*LqT)[CK],
+                                   int lane) {
+    const int g = lane >> 4, n = lane & 15;
+    f32x4 D = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) D = mfma_f32_k4(Lq[n][4 * st + g], Tt[n][4 * st + g], D);
+    wave_sync();  // Lq is read before LqT may alias it
+#pragma unroll
+    for (int r = 0; r < 4; ++r) LqT[4 * g + r][n] = D[r];
+    wave_sync();
+}
+
+}  // namespace
+}  // namespace pace

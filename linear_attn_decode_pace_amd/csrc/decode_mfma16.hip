@@ -15,7 +15,7 @@
 // i.e. tokens 4 g + r, which are the reduction indices this lane feeds to the
 // K^T W update (16x16x16 bf16 MFMA, W split into hi + mid + lo): no
 // cross-lane exchange is needed at C = 16.
-#include "mfma_common.h"
+#include "chunk16.h"
 
 namespace pace {
 namespace {
@@ -31,10 +31,9 @@ struct alignas(16) Tile16Lds {
     float alpha[C16], beta[C16];
     union {
         struct {
-            float kk[C16][C16], qk[C16][C16];  // k_t.k_s, q_t.k_s
-            float A[C16][C16];                 // strictly lower Gamma * K K^T
-            float Lq[C16][C16];                // lower incl. diagonal Gamma * Q K^T
-        } m;                                   // chunk matrices (dead after the operands are built)
+            float kkA[C16][C16];   // k_t.k_s, then A (strictly lower Gamma * K K^T) in place
+            float qkLq[C16][C16];  // q_t.k_s, then Lq, then Lq T in place
+        } m;                       // chunk matrices (dead after the operands are built)
         float o[C16][OROW16];                  // outputs of two column blocks
     } u;
     float Tt[C16][C16];  // Tt[s][t] = T[t][s]
@@ -123,76 +122,11 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
         u32x4 w = {r0[0], r0[1], r1[0], r1[1]};
         return __builtin_bit_cast(bf16x8, w);
     };
-    {
-        // G_K[m][n] = k_{t(m)} . k_n, G_Q[m][n] = q_{t(m)} . k_n
-        f32x4 GK = {0.f, 0.f, 0.f, 0.f}, GQ = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const int c0 = 32 * ks + 4 * g, c1 = c0 + 16;
-            u32x2 s0 = *(const u32x2 *)&L.kq[n][c0];
-            u32x2 s1 = *(const u32x2 *)&L.kq[n][c1];
-            const bf16x8 BG = __builtin_bit_cast(bf16x8, u32x4{s0[0], s0[1], s1[0], s1[1]});
-            GK = mfma_bf16_k32(ap_slice(0, ks), BG, GK);
-            GQ = mfma_bf16_k32(ap_slice(1, ks), BG, GQ);
-        }
-        wave_sync();
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            L.u.m.kk[4 * r + g][n] = GK[r];
-            L.u.m.qk[4 * r + g][n] = GQ[r];
-        }
-    }
-    wave_sync();
-
-    // ---- gates (products of alpha), A and Lq: lane -> row t = lane / 4,
-    //      columns s = 4 (lane % 4) + e ----
-    {
-        float al[C16];
-#pragma unroll
-        for (int r = 0; r < C16; ++r) al[r] = L.alpha[r];
-        const int t = lane >> 2, s0 = 4 * (lane & 3);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int s = s0 + e;
-            float gts = 1.f;
-#pragma unroll
-            for (int r = 1; r < C16; ++r) gts *= (r > s && r <= t) ? al[r] : 1.f;
-            L.u.m.A[t][s] = s < t ? gts * L.u.m.kk[t][s] : 0.f;
-            L.u.m.Lq[t][s] = s <= t ? gts * L.u.m.qk[t][s] : 0.f;
-        }
-        if (lane < C16) {
-            float gm = 1.f, gc = 1.f;
-#pragma unroll
-            for (int r = 0; r < C16; ++r) {
-                gm *= r <= lane ? al[r] : 1.f;
-                gc *= r > lane ? al[r] : 1.f;
-            }
-            L.gam[lane] = gm;
-            L.gamC[lane] = gc;
-        }
-    }
-    wave_sync();
-
-    // ---- UT transform: column s of Z = (I + diag(beta) A)^-1 by forward
-    //      substitution; T = Z diag(beta) ----
-    {
-        const int s = lane & 15;
-        float be[C16], z[C16];
-#pragma unroll
-        for (int r = 0; r < C16; ++r) be[r] = L.beta[r];
-#pragma unroll
-        for (int t = 0; t < C16; ++t) {
-            float sum = 0.f;
-#pragma unroll
-            for (int u = 0; u < t; ++u) sum = fmaf(L.u.m.A[t][u], z[u], sum);
-            z[t] = (t == s ? 1.f : 0.f) - be[t] * sum;
-        }
-        if (lane < C16) {
-#pragma unroll
-            for (int t = 0; t < C16; ++t) L.Tt[s][t] = z[t] * be[s];
-        }
-    }
-    wave_sync();
+    // ---- the chunk's token-only matrices (chunk16.h) ----
+    chunk16_gram<DK, LROW16>(L.kq, L.u.m.kkA, L.u.m.qkLq, lane);
+    chunk16_gates(L.alpha, L.u.m.kkA, L.u.m.qkLq, L.u.m.kkA, L.u.m.qkLq, L.gam, L.gamC, lane);
+    chunk16_ut(L.u.m.kkA, L.beta, L.Tt, lane);
+    chunk16_lqt(L.u.m.qkLq, L.Tt, L.u.m.qkLq, lane);
 
     // ---- chunk-mixing operands (float32 16x16x4 MFMA; step st takes token
     //      4 st + g from lane group g):
@@ -205,10 +139,7 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
         for (int st = 0; st < 4; ++st) {
             const int s = 4 * st + g;
             CW[st] = gct * L.Tt[s][n];
-            float r2 = 0.f;
-#pragma unroll
-            for (int u = 0; u < C16; ++u) r2 = fmaf(L.u.m.Lq[n][u], L.Tt[s][u], r2);
-            CO[st] = r2;
+            CO[st] = L.u.m.qkLq[n][s];  // (Lq T)[n][s]
         }
     }
     float gam_r[4];

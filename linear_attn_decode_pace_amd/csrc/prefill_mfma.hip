@@ -19,13 +19,13 @@
 //   Y = diag(g) Q M0; W = diag(G_C) T X and O = Lq T X + Y on float32 MFMA;
 //   M <- g_C M + K^T W (bf16 MFMA, W in three parts).
 // Outputs of a chunk go through LDS and leave as whole 512-byte rows.
-#include "mfma_common.h"
+#include "chunk16.h"
 #include "pace_prefill.h"
 
 namespace pace {
 namespace {
 
-constexpr int CT = 16;      // tokens per chunk
+constexpr int CT = CK;      // tokens per chunk
 constexpr int PROW = 136;   // bf16 elements per LDS token row (128 + 8 padding)
 constexpr int OPAD = 132;   // floats per LDS output row
 
@@ -41,8 +41,8 @@ struct alignas(16) ChunkLds {
 
 struct alignas(16) PrepScratch {
     float alpha[CT], beta[CT];
-    float kk[CT][CT], qk[CT][CT];
-    float A[CT][CT], Lq[CT][CT];
+    float kkA[CT][CT];   // k_t . k_s, then A in place
+    float qkLq[CT][CT];  // q_t . k_s, then Lq in place
 };
 
 template <int DK>
@@ -122,91 +122,11 @@ __device__ __attribute__((always_inline)) inline void stage_chunk(const TokenReg
 // Producer, part 3: the staged chunk's token-only matrices.
 template <int DK>
 __device__ __attribute__((always_inline)) inline void prep_chunk(ChunkLds &L, PrepScratch &S, int lane) {
-    constexpr int NKS = DK / 32;
-    const int g = lane >> 4, n = lane & 15;
     wave_sync();
-
-    // Gram products on MFMA: A row m of the K (Q) block is token 4 (m % 4) + m / 4
-    {
-        const int tok_n = 4 * (n & 3) + (n >> 2);
-        f32x4 GK = {0.f, 0.f, 0.f, 0.f}, GQ = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const int c0 = 32 * ks + 4 * g, c1 = c0 + 16;
-            const u32x2 k0 = *(const u32x2 *)&L.kq[tok_n][c0], k1 = *(const u32x2 *)&L.kq[tok_n][c1];
-            const u32x2 q0 = *(const u32x2 *)&L.kq[16 + tok_n][c0], q1 = *(const u32x2 *)&L.kq[16 + tok_n][c1];
-            const u32x2 s0 = *(const u32x2 *)&L.kq[n][c0], s1 = *(const u32x2 *)&L.kq[n][c1];
-            const bf16x8 BG = __builtin_bit_cast(bf16x8, u32x4{s0[0], s0[1], s1[0], s1[1]});
-            GK = mfma_bf16_k32(__builtin_bit_cast(bf16x8, u32x4{k0[0], k0[1], k1[0], k1[1]}), BG, GK);
-            GQ = mfma_bf16_k32(__builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]}), BG, GQ);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            S.kk[4 * r + g][n] = GK[r];
-            S.qk[4 * r + g][n] = GQ[r];
-        }
-    }
-    wave_sync();
-
-    // gates as products of alpha; A (strictly lower) and Lq (lower incl. diagonal)
-    {
-        float al[CT];
-#pragma unroll
-        for (int r = 0; r < CT; ++r) al[r] = S.alpha[r];
-        // lane -> row t, columns s0..s0+3: Gamma_{t,s0+3} as one masked
-        // product, then the running product down to s0
-        const int t = lane >> 2, s0 = 4 * (lane & 3);
-        float gts = 1.f;
-#pragma unroll
-        for (int r = 1; r < CT; ++r) gts *= (r > s0 + 3 && r <= t) ? al[r] : 1.f;
-#pragma unroll
-        for (int e = 3; e >= 0; --e) {
-            const int s = s0 + e;
-            S.A[t][s] = s < t ? gts * S.kk[t][s] : 0.f;
-            S.Lq[t][s] = s <= t ? gts * S.qk[t][s] : 0.f;
-            if (e > 0 && s <= t) gts *= S.alpha[s];  // Gamma_{t,s-1} = Gamma_{t,s} alpha_s
-        }
-        if (lane < CT) {
-            float gm = 1.f, gc = 1.f;
-#pragma unroll
-            for (int r = 0; r < CT; ++r) {
-                gm *= r <= lane ? al[r] : 1.f;
-                gc *= r > lane ? al[r] : 1.f;
-            }
-            L.gam[lane] = gm;
-            L.gamC[lane] = gc;
-        }
-    }
-    wave_sync();
-
-    // UT transform: column s of (I + diag(beta) A)^-1 by forward substitution
-    {
-        const int s = lane & 15;
-        float be[CT], z[CT];
-#pragma unroll
-        for (int r = 0; r < CT; ++r) be[r] = S.beta[r];
-#pragma unroll
-        for (int t = 0; t < CT; ++t) {
-            float sum = 0.f;
-#pragma unroll
-            for (int u = 0; u < t; ++u) sum = fmaf(S.A[t][u], z[u], sum);
-            z[t] = (t == s ? 1.f : 0.f) - be[t] * sum;
-        }
-        if (lane < CT) {
-#pragma unroll
-            for (int t = 0; t < CT; ++t) L.Tt[s][t] = z[t] * be[s];
-        }
-    }
-    wave_sync();
-
-    // Lq T on float32 MFMA: step st takes column / row 4 st + g
-    {
-        f32x4 D = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < 4; ++st) D = mfma_f32_k4(S.Lq[n][4 * st + g], L.Tt[n][4 * st + g], D);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) L.LqT[4 * g + r][n] = D[r];
-    }
+    chunk16_gram<DK, PROW>(L.kq, S.kkA, S.qkLq, lane);
+    chunk16_gates(S.alpha, S.kkA, S.qkLq, S.kkA, S.qkLq, L.gam, L.gamC, lane);
+    chunk16_ut(S.kkA, S.beta, L.Tt, lane);
+    chunk16_lqt(S.qkLq, L.Tt, L.LqT, lane);
 }
 
 // bf16 parts (hi, mid, lo) of the four floats x[0..3], as two packed dwords each
