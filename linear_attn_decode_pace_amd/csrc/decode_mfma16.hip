@@ -25,20 +25,24 @@ constexpr int LROW16 = 136;  // bf16 elements per LDS token row (128 + 8 padding
 constexpr int OCOL16 = 32;   // output columns staged before a flush
 constexpr int OROW16 = 36;   // floats per LDS output staging row
 
+// One region serves three phases in turn: the staged v rows (read into
+// registers right after staging), the chunk matrices (dead once the MFMA
+// operands are built), then the output staging of the column loop.  13 KB per
+// tile: three waves per SIMD.
 struct alignas(16) Tile16Lds {
     uint16_t kq[2 * C16][LROW16];  // rows 0..15: k_t, rows 16..31: q_t (bf16 bits)
-    uint16_t v[C16][LROW16];
-    float alpha[C16], beta[C16];
     union {
+        uint16_t v[C16][LROW16];
         struct {
             float kkA[C16][C16];   // k_t.k_s, then A (strictly lower Gamma * K K^T) in place
             float qkLq[C16][C16];  // q_t.k_s, then Lq, then Lq T in place
-        } m;                       // chunk matrices (dead after the operands are built)
-        float o[C16][OROW16];                  // outputs of two column blocks
+            float Tt[C16][C16];    // Tt[s][t] = T[t][s]
+        } m;
+        float o[C16][OROW16];      // outputs of two column blocks
     } u;
-    float Tt[C16][C16];  // Tt[s][t] = T[t][s]
-    float gam[C16];      // gamma_t
-    float gamC[C16];     // Gamma_{C-1, t}
+    float alpha[C16], beta[C16];
+    float gam[C16];   // gamma_t
+    float gamC[C16];  // Gamma_{C-1, t}
 };
 
 constexpr int TPB16 = 2;  // tiles (waves) per workgroup
@@ -98,7 +102,7 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
             const int c = lane + 64 * it;
             const int row = c / CPR, col = (c % CPR) * 8;
             const int t = row & 15, which = row >> 4;
-            uint16_t *dst = which < 2 ? &L.kq[which * 16 + t][col] : &L.v[t][col];
+            uint16_t *dst = which < 2 ? &L.kq[which * 16 + t][col] : &L.u.v[t][col];
             *(u32x4 *)dst = val[it];
         }
         if (lane < 32) {
@@ -122,11 +126,23 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
         u32x4 w = {r0[0], r0[1], r1[0], r1[1]};
         return __builtin_bit_cast(bf16x8, w);
     };
+    // v_{4 r + g}[16 cb + n] of every column block, two tokens per register
+    // (the v rows' LDS then takes the chunk matrices)
+    constexpr int NCBV = DK / 16;
+    uint32_t vreg[NCBV][2];
+#pragma unroll
+    for (int cb = 0; cb < NCBV; ++cb)
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp)
+            vreg[cb][hp] = (uint32_t)L.u.v[4 * (2 * hp) + g][16 * cb + n] |
+                           ((uint32_t)L.u.v[4 * (2 * hp + 1) + g][16 * cb + n] << 16);
+    wave_sync();
+
     // ---- the chunk's token-only matrices (chunk16.h) ----
     chunk16_gram<DK, LROW16>(L.kq, L.u.m.kkA, L.u.m.qkLq, lane);
     chunk16_gates(L.alpha, L.u.m.kkA, L.u.m.qkLq, L.u.m.kkA, L.u.m.qkLq, L.gam, L.gamC, lane);
-    chunk16_ut(L.u.m.kkA, L.beta, L.Tt, lane);
-    chunk16_lqt(L.u.m.qkLq, L.Tt, L.u.m.qkLq, lane);
+    chunk16_ut(L.u.m.kkA, L.beta, L.u.m.Tt, lane);
+    chunk16_lqt(L.u.m.qkLq, L.u.m.Tt, L.u.m.qkLq, lane);
 
     // ---- chunk-mixing operands (float32 16x16x4 MFMA; step st takes token
     //      4 st + g from lane group g):
@@ -138,7 +154,7 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             const int s = 4 * st + g;
-            CW[st] = gct * L.Tt[s][n];
+            CW[st] = gct * L.u.m.Tt[s][n];
             CO[st] = L.u.m.qkLq[n][s];  // (Lq T)[n][s]
         }
     }
@@ -200,7 +216,8 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float sg = gam_r[r] * sk;
-            X[r] = fmaf(-sg, PK[r], bf2f(L.v[4 * r + g][j]));
+            const uint32_t vv = vreg[cb][r >> 1];
+            X[r] = fmaf(-sg, PK[r], bf2f((uint16_t)((r & 1) ? (vv >> 16) : (vv & 0xffffu))));
             Y[r] = sg * PQ[r];
         }
         f32x4 W = {0.f, 0.f, 0.f, 0.f}, O = {0.f, 0.f, 0.f, 0.f};
@@ -280,7 +297,7 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
 }
 
 template <int DK, bool ERR>
-__global__ void __launch_bounds__(64 * TPB16) decode_mfma16_kernel(MfmaArgs a) {
+__global__ void __launch_bounds__(64 * TPB16) __attribute__((amdgpu_waves_per_eu(3))) decode_mfma16_kernel(MfmaArgs a) {
     __shared__ Tile16Lds tl[TPB16];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
