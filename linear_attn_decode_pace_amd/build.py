@@ -13,7 +13,7 @@ OUT = os.path.join(HERE, "libpace.so")
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["pace_abi.cpp", "kernels_v0.hip", "decode_mfma.hip", "decode_mfma16.hip",
-           "prefill_mfma.hip", "kernels_window.hip"]
+           "prefill_mfma.hip", "kernels_window.hip", "window_mfma.hip"]
 ARCH = "gfx950"
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

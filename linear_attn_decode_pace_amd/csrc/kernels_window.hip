@@ -8,44 +8,11 @@
 // lam.  When a write leaves the window it is merged into the history, which
 // is then re-encoded.
 #include "column_codec.h"
+#include "e4m3.h"
 #include "pace_window.h"
 
 namespace pace {
 namespace {
-
-constexpr float E4M3_MAX = 448.f;
-
-// nearest E4M3 code of x (|x| <= 448), ties to even: 3 mantissa bits from
-// float32's 23; below 2^-6 the quantum is 2^-9
-__device__ inline uint8_t e4m3_encode(float x) {
-    const uint32_t u = __float_as_uint(x);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const float a = fabsf(x);
-    if (a < 0.015625f) {  // subnormal range: multiples of 2^-9
-        const float m = rintf(a * 512.f);  // exact scaling, nearest even
-        return (uint8_t)(sign | (uint32_t)m);
-    }
-    const uint32_t au = __float_as_uint(a);
-    int e = (int)(au >> 23) - 127;
-    uint32_t man = au & 0x7fffffu;
-    uint32_t r = man >> 20, rem = man & 0xfffffu;
-    if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
-    if (r == 8u) {
-        r = 0;
-        ++e;
-    }
-    return (uint8_t)(sign | ((uint32_t)(e + 7) << 3) | r);
-}
-
-__device__ inline float e4m3_decode(uint8_t c) {
-    const uint32_t E = (c >> 3) & 15u, M = c & 7u;
-    float v;
-    if (E == 0)
-        v = (float)M * 0.001953125f;  // M * 2^-9
-    else
-        v = __uint_as_float(((E + 120u) << 23) | (M << 20));  // (1 + M/8) 2^(E-7)
-    return (c & 0x80u) ? -v : v;
-}
 
 // one step for the state `tile`: thread j owns column j (blockDim = d_v)
 template <int DK>

@@ -416,8 +416,13 @@ PACE_API int pace_decode_step(pace_state *st, const void *q, const void *k, cons
     hipStream_t s = (hipStream_t)stream;
     const int bf16 = st->cfg.in_dtype == PACE_DTYPE_BF16;
     if (st->windowed()) {
-        hipError_t e = pace::launch_window_step(st->view(), st->window_view(active), q, k, v, alpha,
-                                                beta, out, bf16, s);
+        hipError_t e;
+        if (pace::window_mfma_supported(st->cfg.d_k, st->cfg.d_v, bf16, st->cfg.fp8_window))
+            e = pace::launch_window_step_mfma(st->view(), st->window_view(active), q, k, v, alpha,
+                                              beta, out, s);
+        else
+            e = pace::launch_window_step(st->view(), st->window_view(active), q, k, v, alpha,
+                                         beta, out, bf16, s);
         if (e != hipSuccess) return hip_fail(e, "window step launch");
         st->tokens += 1;
         return ok();

@@ -18,6 +18,12 @@ struct WindowView {
 hipError_t launch_window_step(const PoolView &p, const WindowView &wv, const void *q,
                               const void *k, const void *v, const float *alpha,
                               const float *beta, float *out, int in_bf16, hipStream_t s);
+// The fused window step (window_mfma.hip): bf16 inputs, d_k = d_v = 64 or
+// 128; other shapes take launch_window_step (one thread per column).
+bool window_mfma_supported(int dk, int dv, int in_bf16, int S);
+hipError_t launch_window_step_mfma(const PoolView &p, const WindowView &wv, const void *q,
+                                   const void *k, const void *v, const float *alpha,
+                                   const float *beta, float *out, hipStream_t s);
 hipError_t launch_window_flush(const PoolView &p, const WindowView &wv, hipStream_t s);
 // out[2 t] = lam[t], out[2 t + 1] = head[t] (as float), t < states
 hipError_t launch_window_meta(const WindowView &wv, float *out, size_t states, hipStream_t s);

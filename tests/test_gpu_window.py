@@ -11,6 +11,9 @@ window's E4M3 codes, scales and decays in ring order), then both take the
 step.  Outputs must agree to float32 accuracy; the new write's E4M3 codes must
 be equal except where the oracle's float32 quotient sits on a rounding
 midpoint; a merge's history encode is checked like every other encode.
+bf16 inputs at d_k = d_v = 64 or 128 run the fused wavefront-per-state kernel,
+float32 inputs the per-column one.  Masked steps must leave the outputs and
+every stored byte of inactive sequences untouched.
 """
 import numpy as np
 import pytest
@@ -58,13 +61,30 @@ def _oracle_from(gpu, bits, S, dk):
     return ref
 
 
-@pytest.mark.parametrize("name,kw,S", [
+CASES = [
     ("win-s4", dict(B=2, H=3, n_int8=1, n_outliers=8, steps=14), 4),
     ("win-s1", dict(B=2, H=2, n_int8=1, steps=6), 1),
     ("win-d64", dict(B=3, H=2, dk=64, dv=64, n_int8=1, steps=10), 3),
     ("win-f32", dict(B=2, H=2, n_int8=1, dtype=inputs.DT_F32, steps=8), 2),
-])
+    # more than 8 entries: the key dot products take two groups of lanes
+    ("win-s12", dict(B=2, H=3, n_int8=1, steps=16), 12),
+    # 256 states in 64 workgroups: two whole groups of the XCD order
+    ("win-xcd", dict(B=16, H=16, dk=64, dv=64, n_int8=4, steps=5), 3),
+]
+
+
+@pytest.mark.parametrize("name,kw,S", CASES)
 def test_window_steps_against_oracle(name, kw, S):
+    _run(name, kw, S, masked=False)
+
+
+@pytest.mark.parametrize("name,kw,S", [CASES[0], CASES[2], CASES[3]])
+def test_window_masked_steps(name, kw, S):
+    _run(name + "-mask", kw, S, masked=True)
+
+
+def _run(name, kw, S, masked):
+    import torch
     from linear_attn_decode_pace_amd import pace, runtime
     w = inputs.ragged(name, 250, **kw)
     seed = 0
@@ -74,19 +94,31 @@ def test_window_steps_against_oracle(name, kw, S):
     bits = np.tile(inputs.head_bits(w, seed), w.B).astype(np.int64)
     st = runtime.State(w, inputs.head_bits(w, seed), pace.PACE_INIT_F32,
                        runtime.warmup_state(w, seed), flags=pace.PACE_FP8_WINDOW, fp8_window=S)
+    rng = np.random.default_rng(11)
     flips = entries = merges = 0
     for t in range(w.steps):
+        act = np.ones(w.B, bool)
+        if masked and t >= 1:
+            act = rng.uniform(size=w.B) < 0.6
+        act_t = np.repeat(act, w.H)
         before = _gpu_state(st, w, S)
         ref = _oracle_from(before, bits, S, w.dk)
         cnt0, head0 = before[4], before[5][:, 1].astype(int)
         tok = inputs.tokens(w, seed, inputs.SEG_DECODE, t, t + 1)
-        out = runtime.out_buffer(w, 1)
-        st.step(runtime.DeviceTokens(tok), out)
+        out = runtime.out_buffer(w, 1).fill_(np.nan)
+        st.step(runtime.DeviceTokens(tok), out,
+                torch.as_tensor(act.astype(np.uint8), device="cuda") if masked else None)
         q, k, v, a, b = [x[0] for x in tok_tiles(tok, idx, w.H)]
         o_ref = ref.step(q, k, v, a, b)
-        parity.check_outputs(out.reshape(1, n, w.dv).cpu().numpy(), o_ref[None], f"{name} step {t}")
-        c, s, wc, wf, cnt, meta = _gpu_state(st, w, S)
-        for i in range(n):
+        o = out.reshape(n, w.dv).cpu().numpy()
+        assert np.all(np.isnan(o[~act_t])), f"{name} step {t}: inactive rows were written"
+        if act_t.any():
+            parity.check_outputs(o[act_t][None], o_ref[act_t][None], f"{name} step {t}")
+        after = _gpu_state(st, w, S)
+        for x0, x1 in zip(before, after):
+            np.testing.assert_array_equal(x1[~act_t], x0[~act_t], f"{name} step {t}: inactive state changed")
+        c, s, wc, wf, cnt, meta = after
+        for i in np.nonzero(act_t)[0]:
             slot = (head0[i] + cnt0[i]) % S
             kc, ks, uc, us, _ = ref.win[i][-1]
             assert np.array_equal(wc[i, slot, :w.dk], kc) and wf[i, slot, 0] == ks, f"{name} step {t} key"
@@ -100,16 +132,16 @@ def test_window_steps_against_oracle(name, kw, S):
                 assert np.all(_midpoint_distance(qv[diff]) < MID_TOL), f"{name} step {t} u codes"
                 flips += int(diff.sum())
             entries += w.dv
-        np.testing.assert_array_equal(cnt, [len(x) for x in ref.win])
-        np.testing.assert_allclose(meta[:, 0], ref.lam, rtol=1e-6)
-        merged = cnt0 == S
+        np.testing.assert_array_equal(cnt[act_t], [len(ref.win[i]) for i in np.nonzero(act_t)[0]])
+        np.testing.assert_allclose(meta[act_t, 0], ref.lam[act_t], rtol=1e-6)
+        merged = (cnt0 == S) & act_t
         if merged.any():
             merges += int(merged.sum())
             pre = np.stack([ref.last_pre[i] for i in np.nonzero(merged)[0]])
             parity.check_encoded(c[merged], s[merged], ref.codes[merged], ref.scales[merged], pre,
                                  f"{name} step {t} merge", lattice_ties=True)
         # decays of the window, oldest first, against the oracle's
-        for i in range(n):
+        for i in np.nonzero(act_t)[0]:
             head = int(meta[i, 1])
             got = [wf[i, (head + e) % S, 2] for e in range(int(cnt[i]))]
             np.testing.assert_allclose(got, [e_[4] for e_ in ref.win[i]], rtol=1e-6)
