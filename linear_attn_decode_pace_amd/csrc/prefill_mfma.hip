@@ -12,18 +12,31 @@
 //   * one producer wave stages chunk c+1's 16 tokens in LDS and computes the
 //     chunk's token-only matrices (Gram products, gates, UT solve, Lq T)
 //     while the consumers apply chunk c: double-buffered LDS, one workgroup
-//     barrier per chunk.
+//     barrier per chunk that orders LDS only (global loads and stores stay
+//     in flight across it).
 // Per chunk and column block (WY / UT form, as the decode kernels):
-//   P = [K; Q] M0 with M0 split exactly enough into three bf16 parts
-//   (hi + mid + lo) so the products keep float32 accuracy; X = V - diag(g) K M0,
-//   Y = diag(g) Q M0; W = diag(G_C) T X and O = Lq T X + Y on float32 MFMA;
-//   M <- g_C M + K^T W (bf16 MFMA, W in three parts).
-// Outputs of a chunk go through LDS and leave as whole 512-byte rows.
+//   P_K = K M0 with M0 split exactly into three bf16 parts (hi + mid + lo), so
+//   the state update keeps float32 accuracy; P_Q = Q M0 over hi + mid (it
+//   only reaches the outputs, and two parts leave ~1e-5 relative error);
+//   X = V - diag(g) P_K; W = diag(G_C) T X and Lq T X on float32 MFMA;
+//   O = Lq T X + diag(g) P_Q; M <- g_C M + K^T W (bf16 MFMA, W in three parts:
+//   hi and mid in one 32-deep product, lo in a 16-deep one).
+// Outputs of a chunk go through double-buffered LDS and leave as whole
+// 512-byte rows.
 #include "chunk16.h"
 #include "pace_prefill.h"
 
 namespace pace {
 namespace {
+
+
+// Workgroup barrier for LDS hand-offs only: global loads and stores stay in
+// flight across it (a plain __syncthreads waits for every outstanding one)
+__device__ inline void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 constexpr int CT = CK;      // tokens per chunk
 constexpr int PROW = 136;   // bf16 elements per LDS token row (128 + 8 padding)
@@ -36,7 +49,6 @@ struct alignas(16) ChunkLds {
     float LqT[CT][CT];  // (Lq T)[t][s]
     float gam[CT];      // gamma_t inside the chunk
     float gamC[CT];     // Gamma_{C-1, t}
-    int n_valid;        // real tokens of the chunk (the rest are identity padding)
 };
 
 struct alignas(16) PrepScratch {
@@ -49,7 +61,7 @@ template <int DK>
 struct PrefillLds {
     ChunkLds ch[2];
     PrepScratch ps;
-    alignas(16) float o[CT][OPAD];
+    alignas(16) float o[2][CT][OPAD];
 };
 
 struct PrefillArgs {
@@ -67,7 +79,6 @@ struct TokenRegs {
     static constexpr int NL = 3 * CT * CPR / 64;  // loads per lane
     u32x4 val[NL];
     float ab;
-    int nv;
 };
 
 // Producer, part 1: issue the loads of chunk c's tokens (k, q, v rows, then
@@ -100,7 +111,6 @@ __device__ __attribute__((always_inline)) inline void load_chunk(const PrefillAr
         R.ab = is_beta ? 0.f : 1.f;
         if (t < nv) R.ab = (is_beta ? a.beta : a.alpha)[((size_t)t0 + t) * tok_stride + tile_row];
     }
-    R.nv = nv;
 }
 
 // Producer, part 2: write the loaded chunk into LDS.
@@ -116,7 +126,6 @@ __device__ __attribute__((always_inline)) inline void stage_chunk(const TokenReg
         *(u32x4 *)dst = R.val[it];
     }
     if (lane < 32) (lane >= 16 ? S.beta : S.alpha)[lane & 15] = R.ab;
-    if (lane == 0) L.n_valid = R.nv;
 }
 
 // Producer, part 3: the staged chunk's token-only matrices.
@@ -129,16 +138,31 @@ __device__ __attribute__((always_inline)) inline void prep_chunk(ChunkLds &L, Pr
     chunk16_lqt(S.qkLq, L.Tt, L.LqT, lane);
 }
 
-// bf16 parts (hi, mid, lo) of the four floats x[0..3], as two packed dwords each
+// x - (low / high bf16 of pk) in one instruction: a bf16 dot product with
+// (-1, -0) / (0, -1) accumulated onto x (exact: the difference is a float32).
+// The low-half factor is (-1, -0), not (-1, 0): the compiler encodes the
+// packed (-1, 0) as the inline constant -1.0, which the dot product applies
+// to the high half.
+__device__ inline float sub_lo(uint32_t pk, float x) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
+                                           __builtin_bit_cast(bf16x2, 0x8000bf80u), x, false);
+}
+__device__ inline float sub_hi(uint32_t pk, float x) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
+                                           __builtin_bit_cast(bf16x2, 0xbf800000u), x, false);
+}
+
+// bf16 parts (hi, mid, lo) of the four floats x[0..3], as two packed dwords
+// each: x = hi + mid + lo exactly (8 + 8 + 8 significant bits)
 __device__ inline void split3(const f32x4 &x, uint32_t hi[2], uint32_t md[2], uint32_t lo[2]) {
     hi[0] = pk_bf16(x[0], x[1]);
     hi[1] = pk_bf16(x[2], x[3]);
-    const float r0 = x[0] - lo_f32(hi[0]), r1 = x[1] - hi_f32(hi[0]);
-    const float r2 = x[2] - lo_f32(hi[1]), r3 = x[3] - hi_f32(hi[1]);
+    const float r0 = sub_lo(hi[0], x[0]), r1 = sub_hi(hi[0], x[1]);
+    const float r2 = sub_lo(hi[1], x[2]), r3 = sub_hi(hi[1], x[3]);
     md[0] = pk_bf16(r0, r1);
     md[1] = pk_bf16(r2, r3);
-    lo[0] = pk_bf16(r0 - lo_f32(md[0]), r1 - hi_f32(md[0]));
-    lo[1] = pk_bf16(r2 - lo_f32(md[1]), r3 - hi_f32(md[1]));
+    lo[0] = pk_bf16(sub_lo(md[0], r0), sub_hi(md[0], r1));
+    lo[1] = pk_bf16(sub_lo(md[1], r2), sub_hi(md[1], r3));
 }
 
 template <int DK, int BITS, bool ERR>
@@ -172,15 +196,17 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) acc[rt] *= sk;
     }
-    // Output flush of chunk c, shared by every wave: rows of DK floats, 16
-    // bytes per lane (between the two barriers that close a chunk)
+    // Output flush of chunk c, shared by every wave after the barrier that
+    // closes it: rows of DK floats, 16 bytes per lane.  Staging buffer c & 1
+    // is written again only in chunk c + 2, after the next barrier, by which
+    // every wave has finished this flush.
     auto flush = [&](int c) {
         if (!a.out) return;
         constexpr int PER_ROW = DK / 4;
         const int e = wave * 64 + lane;
         const int t = e / PER_ROW, c4 = (e % PER_ROW) * 4;
-        if (t < CT && t < L.ch[c & 1].n_valid) {
-            const f32x4 x = *(const f32x4 *)&L.o[t][c4];
+        if (t < CT && t < a.n_tok - CT * c) {  // chunk c's real tokens
+            const f32x4 x = *(const f32x4 *)&L.o[c & 1][t][c4];
             __builtin_nontemporal_store(
                 x, (f32x4 *)(a.out + (((size_t)CT * c + t) * tok_stride + tile_row) * DK + c4));
         }
@@ -195,7 +221,7 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
         stage_chunk<DK>(R, L.ch[0], L.ps, lane);
         if (n_chunks > 1) load_chunk<DK>(a, R, tile_row, 1, lane);
         prep_chunk<DK>(L.ch[0], L.ps, lane);
-        __syncthreads();
+        lds_barrier();
         for (int c = 0; c < n_chunks; ++c) {
             if (c + 1 < n_chunks) {
                 // chunk c+1 into LDS; its registers then take chunk c+2's loads
@@ -204,25 +230,28 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
                 if (c + 2 < n_chunks) load_chunk<DK>(a, R, tile_row, c + 2, lane);
                 prep_chunk<DK>(N, L.ps, lane);
             }
-            __syncthreads();  // chunk c+1 staged, chunk c's outputs complete
+            lds_barrier();  // chunk c+1 staged, chunk c's outputs complete
             flush(c);
-            __syncthreads();  // the output staging is free again
         }
         return;
     }
 
-    __syncthreads();
+    lds_barrier();
+    // A operand rows: the K block's row m is token 4 (m % 4) + m / 4, so P_K's
+    // row 4 g + r is token 4 r + g (the B layout of the float32 chunk MFMAs);
+    // the Q block's row m is token m, so P_Q's rows line up with O's
     const int tok_n = 4 * (n & 3) + (n >> 2);
     for (int c = 0; c < n_chunks; ++c) {
         ChunkLds &C = L.ch[c & 1];
         {
-            // P = [K; Q] M0 over three bf16 parts of M0
+            // P_K = K M0 over three bf16 parts of M0 (the state update needs
+            // float32 accuracy), P_Q = Q M0 over two (outputs only)
             f32x4 PK = {0.f, 0.f, 0.f, 0.f}, PQ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const int c0 = 32 * ks + 4 * g, c1 = c0 + 16;
                 const u32x2 k0 = *(const u32x2 *)&C.kq[tok_n][c0], k1 = *(const u32x2 *)&C.kq[tok_n][c1];
-                const u32x2 q0 = *(const u32x2 *)&C.kq[16 + tok_n][c0], q1 = *(const u32x2 *)&C.kq[16 + tok_n][c1];
+                const u32x2 q0 = *(const u32x2 *)&C.kq[16 + n][c0], q1 = *(const u32x2 *)&C.kq[16 + n][c1];
                 const bf16x8 AK = __builtin_bit_cast(bf16x8, u32x4{k0[0], k0[1], k1[0], k1[1]});
                 const bf16x8 AQ = __builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]});
                 uint32_t h0[2], m0[2], l0[2], h1[2], m1[2], l1[2];
@@ -236,17 +265,12 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
                 PK = mfma_bf16_k32(AK, BM, PK);
                 PQ = mfma_bf16_k32(AQ, BM, PQ);
                 PK = mfma_bf16_k32(AK, BL, PK);
-                PQ = mfma_bf16_k32(AQ, BL, PQ);
             }
-            // X, Y for tokens 4 r + g (the P rows this lane holds)
-            float X[4], Y[4];
+            // X for tokens 4 r + g (the P_K rows this lane holds)
+            float X[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float gm = C.gam[4 * r + g];
-                X[r] = fmaf(-gm, PK[r], bf2f(C.v[4 * r + g][j]));
-                Y[r] = gm * PQ[r];
-            }
-            // W (rows = tokens) and O on float32 MFMA; step st takes token 4 st + g
+            for (int r = 0; r < 4; ++r) X[r] = fmaf(-C.gam[4 * r + g], PK[r], bf2f(C.v[4 * r + g][j]));
+            // W (rows = tokens) and Lq T X on float32 MFMA; step st takes token 4 st + g
             f32x4 W = {0.f, 0.f, 0.f, 0.f}, O = {0.f, 0.f, 0.f, 0.f};
             const float gct = C.gamC[n];
 #pragma unroll
@@ -255,19 +279,18 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
                 W = mfma_f32_k4(gct * C.Tt[s][n], X[st], W);
                 O = mfma_f32_k4(C.LqT[n][s], X[st], O);
             }
+            // O += diag(gamma) Q M0: rows 4 g + r of O and P_Q are the same tokens
 #pragma unroll
-            for (int st = 0; st < 4; ++st) O = mfma_f32_k4(n == 4 * st + g ? 1.f : 0.f, Y[st], O);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) L.o[4 * g + r][j] = O[r];
+            for (int r = 0; r < 4; ++r) L.o[c & 1][4 * g + r][j] = fmaf(C.gam[4 * g + r], PQ[r], O[r]);
 
-            // M <- gamma_C M + K^T W, W in three bf16 parts (tokens 4 g + e)
+            // M <- gamma_C M + K^T W, W in three bf16 parts: hi and mid of
+            // tokens 4 g + e in one 32-deep product, lo in a 16-deep one
             const float gC = C.gam[CT - 1];
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) acc[rt] *= gC;
             uint32_t wh[2], wm[2], wl[2];
             split3(W, wh, wm, wl);
-            const s16x4 BH = __builtin_bit_cast(s16x4, u32x2{wh[0], wh[1]});
-            const s16x4 BM = __builtin_bit_cast(s16x4, u32x2{wm[0], wm[1]});
+            const bf16x8 BHM = __builtin_bit_cast(bf16x8, u32x4{wh[0], wh[1], wm[0], wm[1]});
             const s16x4 BL = __builtin_bit_cast(s16x4, u32x2{wl[0], wl[1]});
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) {
@@ -275,14 +298,13 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
                 s16x4 au;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) au[e] = (short)C.kq[4 * g + e][i];
-                acc[rt] = mfma_bf16_k16(au, BH, acc[rt]);
-                acc[rt] = mfma_bf16_k16(au, BM, acc[rt]);
+                const u32x2 a2 = __builtin_bit_cast(u32x2, au);
+                acc[rt] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, u32x4{a2[0], a2[1], a2[0], a2[1]}), BHM, acc[rt]);
                 acc[rt] = mfma_bf16_k16(au, BL, acc[rt]);
             }
         }
-        __syncthreads();  // chunk c+1 staged, chunk c's outputs complete
+        lds_barrier();  // chunk c+1 staged, chunk c's outputs complete
         flush(c);
-        __syncthreads();  // the output staging is free again
     }
 
     // ---- encode each column block once: absmax, scale, codes ----

@@ -162,3 +162,39 @@ def _run(name, kw, S, masked):
     s_ = st.stats()
     assert s_["bytes_step_buffer"] == n * (S * (w.dk + w.dv + 12) + 12)
     st.free()
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("win-err", dict(B=3, H=5, n_int8=2, n_outliers=8)),                # fused kernel
+    ("win-err-f32", dict(B=2, H=3, n_int8=1, dtype=inputs.DT_F32)),    # per-column kernel
+])
+def test_window_error_statistics(name, kw):
+    # PACE_STATS_ERR on a window handle: a merge's encode reports, per head,
+    # sum (H - c s)^2 and sum H^2 of the history it quantized
+    from oracle import quant
+    from linear_attn_decode_pace_amd import pace, runtime
+    S = 3
+    w = inputs.ragged(name, 251, **kw)
+    seed = 2
+    say(f"[case] window error statistics {name}")
+    n = w.B * w.H
+    bits = np.tile(inputs.head_bits(w, seed), w.B).astype(np.int64)
+    st = runtime.State(w, inputs.head_bits(w, seed), pace.PACE_INIT_F32,
+                       runtime.warmup_state(w, seed),
+                       flags=pace.PACE_FP8_WINDOW | pace.PACE_STATS_ERR, fp8_window=S)
+    for t in range(S):
+        tok = inputs.tokens(w, seed, inputs.SEG_DECODE, t, t + 1)
+        st.step(runtime.DeviceTokens(tok), runtime.out_buffer(w, 1))
+    before = _gpu_state(st, w, S)
+    assert np.all(before[4] == S)
+    ref = _oracle_from(before, bits, S, w.dk)
+    tok = inputs.tokens(w, seed, inputs.SEG_DECODE, S, S + 1)
+    st.step(runtime.DeviceTokens(tok), runtime.out_buffer(w, 1))
+    ref.step(*[x[0] for x in tok_tiles(tok, np.arange(n), w.H)])
+    pre = np.stack(ref.last_pre)
+    e, r = quant.roundtrip_error(pre, bits)
+    s = st.stats()
+    assert s["err_tracked"] == 1
+    np.testing.assert_allclose(s["err_sq"], e.reshape(w.B, w.H).sum(axis=0), rtol=1e-3)
+    np.testing.assert_allclose(s["ref_sq"], r.reshape(w.B, w.H).sum(axis=0), rtol=1e-4)
+    st.free()
