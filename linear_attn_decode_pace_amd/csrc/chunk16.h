@@ -17,12 +17,18 @@ namespace pace {
 namespace {
 
 constexpr int CK = 16;  // tokens per chunk
+// Row stride (floats) that callers may give the 16 x 16 matrices: rows stay
+// 16-byte aligned and a column's 16 entries fall in 16 different LDS banks
+// (a stride of 16 puts rows t and t + 4 in the same bank).
+constexpr int CKS = 20;
 
-// Gram products: the A row m of the K (Q) block is token 4 (m % 4) + m / 4,
+// Gram products kk[t][s] = k_t . k'_s and qk[t][s] = q_t . k'_s, where k_t,
+// q_t come from kq_t (rows 0..15 keys, rows 16..31 queries) and k'_s from
+// kq_s (rows 0..15): the A row m of the K (Q) block is token 4 (m % 4) + m / 4,
 // so output row 4 g + r is token 4 r + g
-template <int DK, int ROW>
-__device__ inline void chunk16_gram(const uint16_t (*kq)[ROW], float (*kk)[CK], float (*qk)[CK],
-                                    int lane) {
+template <int DK, int ROW, int STR>
+__device__ inline void chunk16_gram2(const uint16_t (*kq_t)[ROW], const uint16_t (*kq_s)[ROW],
+                                     float (*kk)[STR], float (*qk)[STR], int lane) {
     constexpr int NKS = DK / 32;
     const int g = lane >> 4, n = lane & 15;
     const int tok_n = 4 * (n & 3) + (n >> 2);
@@ -30,9 +36,9 @@ __device__ inline void chunk16_gram(const uint16_t (*kq)[ROW], float (*kk)[CK], 
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
         const int c0 = 32 * ks + 4 * g, c1 = c0 + 16;
-        const u32x2 k0 = *(const u32x2 *)&kq[tok_n][c0], k1 = *(const u32x2 *)&kq[tok_n][c1];
-        const u32x2 q0 = *(const u32x2 *)&kq[CK + tok_n][c0], q1 = *(const u32x2 *)&kq[CK + tok_n][c1];
-        const u32x2 s0 = *(const u32x2 *)&kq[n][c0], s1 = *(const u32x2 *)&kq[n][c1];
+        const u32x2 k0 = *(const u32x2 *)&kq_t[tok_n][c0], k1 = *(const u32x2 *)&kq_t[tok_n][c1];
+        const u32x2 q0 = *(const u32x2 *)&kq_t[CK + tok_n][c0], q1 = *(const u32x2 *)&kq_t[CK + tok_n][c1];
+        const u32x2 s0 = *(const u32x2 *)&kq_s[n][c0], s1 = *(const u32x2 *)&kq_s[n][c1];
         const bf16x8 BG = __builtin_bit_cast(bf16x8, u32x4{s0[0], s0[1], s1[0], s1[1]});
         GK = mfma_bf16_k32(__builtin_bit_cast(bf16x8, u32x4{k0[0], k0[1], k1[0], k1[1]}), BG, GK);
         GQ = mfma_bf16_k32(__builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]}), BG, GQ);
@@ -46,11 +52,19 @@ __device__ inline void chunk16_gram(const uint16_t (*kq)[ROW], float (*kk)[CK], 
     wave_sync();
 }
 
+// Gram products of one chunk: kk[t][s] = k_t . k_s, qk[t][s] = q_t . k_s
+template <int DK, int ROW, int STR>
+__device__ inline void chunk16_gram(const uint16_t (*kq)[ROW], float (*kk)[STR], float (*qk)[STR],
+                                    int lane) {
+    chunk16_gram2<DK, ROW, STR>(kq, kq, kk, qk, lane);
+}
+
 // gates, A and Lq: lane -> row t = lane / 4, columns s0 .. s0 + 3 with
 // s0 = 4 (lane % 4): Gamma_{t,s0+3} as one masked product, then the running
 // product down to s0
-__device__ inline void chunk16_gates(const float *alpha, const float (*kk)[CK],
-                                     const float (*qk)[CK], float (*A)[CK], float (*Lq)[CK],
+template <int STR>
+__device__ inline void chunk16_gates(const float *alpha, const float (*kk)[STR],
+                                     const float (*qk)[STR], float (*A)[STR], float (*Lq)[STR],
                                      float *gam, float *gamC, int lane) {
     float al[CK];
 #pragma unroll
@@ -88,7 +102,8 @@ __device__ inline void chunk16_gates(const float *alpha, const float (*kk)[CK],
 
 // UT transform: column s of Z = (I + diag(beta) A)^-1 by forward
 // substitution (one column per lane), T = Z diag(beta), stored transposed
-__device__ inline void chunk16_ut(const float (*A)[CK], const float *beta, float (*Tt)[CK],
+template <int STR>
+__device__ inline void chunk16_ut(const float (*A)[STR], const float *beta, float (*Tt)[STR],
                                   int lane) {
     const int s = lane & 15;
     float be[CK], z[CK];
@@ -109,7 +124,8 @@ __device__ inline void chunk16_ut(const float (*A)[CK], const float *beta, float
 }
 
 // Lq T on float32 MFMA: step st takes column / row 4 st + g
-__device__ inline void chunk16_lqt(const float (*Lq)[CK], const float (*Tt)[CK], float (*LqT)[CK],
+template <int STR>
+__device__ inline void chunk16_lqt(const float (*Lq)[STR], const float (*Tt)[STR], float (*LqT)[STR],
                                    int lane) {
     const int g = lane >> 4, n = lane & 15;
     f32x4 D = {0.f, 0.f, 0.f, 0.f};

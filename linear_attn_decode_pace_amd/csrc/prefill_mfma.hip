@@ -9,18 +9,20 @@
 //   * NCB consumer waves (one per 16-column block) hold the tile's float32
 //     state in MFMA accumulator layout (the same lane -> (row, column) map as
 //     the pool layout) from the first token to the final encode;
-//   * one producer wave stages chunk c+1's 16 tokens in LDS and computes the
-//     chunk's token-only matrices (Gram products, gates, UT solve, Lq T)
-//     while the consumers apply chunk c: double-buffered LDS, one workgroup
-//     barrier per chunk that orders LDS only (global loads and stores stay
-//     in flight across it).
+//   * two producer waves, on different SIMDs, take alternate chunks: each
+//     stages a chunk's keys and queries in LDS and computes its Gram products
+//     and gates two chunks ahead of the consumers, then its UT solve and
+//     Lq T one chunk ahead (three chunk buffers in LDS); the consumers read
+//     their own v values straight from the inputs, one chunk ahead;
+//   * one workgroup barrier per chunk, ordering LDS only (global loads and
+//     stores stay in flight across it).
 // Per chunk and column block (WY / UT form, as the decode kernels):
 //   P_K = K M0 with M0 split exactly into three bf16 parts (hi + mid + lo), so
 //   the state update keeps float32 accuracy; P_Q = Q M0 over hi + mid (it
 //   only reaches the outputs, and two parts leave ~1e-5 relative error);
 //   X = V - diag(g) P_K; W = diag(G_C) T X and Lq T X on float32 MFMA;
 //   O = Lq T X + diag(g) P_Q; M <- g_C M + K^T W (bf16 MFMA, W in three parts:
-//   hi and mid in one 32-deep product, lo in a 16-deep one).
+//   hi and mid in one 32-deep product, lo in a second one).
 // Outputs of a chunk go through double-buffered LDS and leave as whole
 // 512-byte rows.
 #include "chunk16.h"
@@ -28,7 +30,6 @@
 
 namespace pace {
 namespace {
-
 
 // Workgroup barrier for LDS hand-offs only: global loads and stores stay in
 // flight across it (a plain __syncthreads waits for every outstanding one)
@@ -44,7 +45,6 @@ constexpr int OPAD = 132;   // floats per LDS output row
 
 struct alignas(16) ChunkLds {
     uint16_t kq[2 * CT][PROW];  // rows 0..15: k_t, rows 16..31: q_t (bf16 bits)
-    uint16_t v[CT][PROW];
     float Tt[CT][CT];   // Tt[s][t] = T[t][s]
     float LqT[CT][CT];  // (Lq T)[t][s]
     float gam[CT];      // gamma_t inside the chunk
@@ -57,10 +57,13 @@ struct alignas(16) PrepScratch {
     float qkLq[CT][CT];  // q_t . k_s, then Lq in place
 };
 
+constexpr int NBUF = 3;  // chunk buffers: applied, being prepared, being staged
+constexpr int NPROD = 2; // producer waves
+
 template <int DK>
 struct PrefillLds {
-    ChunkLds ch[2];
-    PrepScratch ps;
+    ChunkLds ch[NBUF];
+    PrepScratch ps[NPROD];
     alignas(16) float o[2][CT][OPAD];
 };
 
@@ -76,7 +79,7 @@ struct PrefillArgs {
 template <int DK>
 struct TokenRegs {
     static constexpr int CPR = DK / 8;            // 16-byte chunks per token row
-    static constexpr int NL = 3 * CT * CPR / 64;  // loads per lane
+    static constexpr int NL = 2 * CT * CPR / 64;  // loads per lane (k and q rows)
     u32x4 val[NL];
     float ab;
 };
@@ -95,10 +98,10 @@ __device__ __attribute__((always_inline)) inline void load_chunk(const PrefillAr
         const int e = lane + 64 * it;
         const int row = e / CPR, col = (e % CPR) * 8;
         const int t = row & 15;
-        // the 48 rows are k, q, v in blocks of 16: the block is fixed per load
+        // the 32 rows are k, q in blocks of 16: the block is fixed per load
         constexpr int RPL = 64 / CPR;  // rows per load
         const int which = (it * RPL) / CT;
-        const uint16_t *src = (which == 0 ? a.k : which == 1 ? a.q : a.v) + base;
+        const uint16_t *src = (which == 0 ? a.k : a.q) + base;
         R.val[it] = u32x4{0u, 0u, 0u, 0u};
         if (t < nv)
             R.val[it] = __builtin_nontemporal_load(
@@ -122,18 +125,21 @@ __device__ __attribute__((always_inline)) inline void stage_chunk(const TokenReg
         const int e = lane + 64 * it;
         const int row = e / CPR, col = (e % CPR) * 8;
         const int t = row & 15, which = row >> 4;
-        uint16_t *dst = which < 2 ? &L.kq[which * 16 + t][col] : &L.v[t][col];
+        uint16_t *dst = &L.kq[which * 16 + t][col];
         *(u32x4 *)dst = R.val[it];
     }
     if (lane < 32) (lane >= 16 ? S.beta : S.alpha)[lane & 15] = R.ab;
 }
 
-// Producer, part 3: the staged chunk's token-only matrices.
+// Producer, part 3: the staged chunk's token-only matrices, in two phases
+// of about equal length (Gram products and gates; UT solve and Lq T).
 template <int DK>
-__device__ __attribute__((always_inline)) inline void prep_chunk(ChunkLds &L, PrepScratch &S, int lane) {
+__device__ __attribute__((always_inline)) inline void prep_a(ChunkLds &L, PrepScratch &S, int lane) {
     wave_sync();
     chunk16_gram<DK, PROW>(L.kq, S.kkA, S.qkLq, lane);
     chunk16_gates(S.alpha, S.kkA, S.qkLq, S.kkA, S.qkLq, L.gam, L.gamC, lane);
+}
+__device__ __attribute__((always_inline)) inline void prep_b(ChunkLds &L, PrepScratch &S, int lane) {
     chunk16_ut(S.kkA, S.beta, L.Tt, lane);
     chunk16_lqt(S.qkLq, L.Tt, L.LqT, lane);
 }
@@ -177,7 +183,7 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
     const size_t tile_row = (size_t)b * a.p.H + h;
     const uint32_t tok_stride = (uint32_t)a.p.B * (uint32_t)a.p.H;
     const int n_chunks = (a.n_tok + CT - 1) / CT;
-    const bool producer = wave == NCB;
+    const bool producer = wave >= NCB;
     const int cb = wave, j = 16 * cb + n;
 
     uint8_t *codes = BITS == 4
@@ -213,24 +219,35 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
     };
 
     if (producer) {
-        // the producer keeps the next chunk's tokens in flight in its own
-        // registers: chunk c+2 loads while chunk c+1 is prepared and chunk c
-        // applied (its loop has the same barriers as the consumers')
+        // Two producers take alternate chunks.  Chunk c is staged and its
+        // Gram products and gates computed (phase A) while the consumers
+        // apply chunk c - 2, its UT solve and Lq T (phase B) while they apply
+        // chunk c - 1; its tokens were loaded into the producer's registers
+        // two intervals earlier.  Each producer alternates A and B, so both
+        // carry half of the work every interval, on different SIMDs.
+        const int p = wave - NCB;
+        PrepScratch &ps = L.ps[p];
         TokenRegs<DK> R;
-        load_chunk<DK>(a, R, tile_row, 0, lane);
-        stage_chunk<DK>(R, L.ch[0], L.ps, lane);
-        if (n_chunks > 1) load_chunk<DK>(a, R, tile_row, 1, lane);
-        prep_chunk<DK>(L.ch[0], L.ps, lane);
+        auto phase_a = [&](int c) {
+            ChunkLds &N = L.ch[c % NBUF];
+            stage_chunk<DK>(R, N, ps, lane);
+            if (c + NPROD < n_chunks) load_chunk<DK>(a, R, tile_row, c + NPROD, lane);
+            prep_a<DK>(N, ps, lane);
+        };
+        if (p < n_chunks) {
+            load_chunk<DK>(a, R, tile_row, p, lane);
+            phase_a(p);
+            if (p == 0) prep_b(L.ch[0], ps, lane);
+        }
         lds_barrier();
         for (int c = 0; c < n_chunks; ++c) {
-            if (c + 1 < n_chunks) {
-                // chunk c+1 into LDS; its registers then take chunk c+2's loads
-                ChunkLds &N = L.ch[(c + 1) & 1];
-                stage_chunk<DK>(R, N, L.ps, lane);
-                if (c + 2 < n_chunks) load_chunk<DK>(a, R, tile_row, c + 2, lane);
-                prep_chunk<DK>(N, L.ps, lane);
+            // this interval: phase B of chunk c + 1 or phase A of chunk c + 2
+            if ((c + 1) % NPROD == p) {
+                if (c + 1 < n_chunks) prep_b(L.ch[(c + 1) % NBUF], ps, lane);
+            } else if (c + 2 < n_chunks) {
+                phase_a(c + 2);
             }
-            lds_barrier();  // chunk c+1 staged, chunk c's outputs complete
+            lds_barrier();  // chunk c+1 prepared, chunk c's outputs complete
             flush(c);
         }
         return;
@@ -241,8 +258,20 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
     // row 4 g + r is token 4 r + g (the B layout of the float32 chunk MFMAs);
     // the Q block's row m is token m, so P_Q's rows line up with O's
     const int tok_n = 4 * (n & 3) + (n >> 2);
+    // this lane's v values (tokens 4 r + g of a chunk, column j), read from
+    // the inputs one chunk ahead
+    auto load_v = [&](int c, uint32_t (&vv)[4]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = CT * c + 4 * r + g;
+            vv[r] = t < a.n_tok ? (uint32_t)a.v[((size_t)t * tok_stride + tile_row) * DK + j] : 0u;
+        }
+    };
+    uint32_t vcur[4], vnext[4];
+    load_v(0, vcur);
     for (int c = 0; c < n_chunks; ++c) {
-        ChunkLds &C = L.ch[c & 1];
+        if (c + 1 < n_chunks) load_v(c + 1, vnext);
+        ChunkLds &C = L.ch[c % NBUF];
         {
             // P_K = K M0 over three bf16 parts of M0 (the state update needs
             // float32 accuracy), P_Q = Q M0 over two (outputs only)
@@ -269,7 +298,7 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
             // X for tokens 4 r + g (the P_K rows this lane holds)
             float X[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) X[r] = fmaf(-C.gam[4 * r + g], PK[r], bf2f(C.v[4 * r + g][j]));
+            for (int r = 0; r < 4; ++r) X[r] = fmaf(-C.gam[4 * r + g], PK[r], bf2f((uint16_t)vcur[r]));
             // W (rows = tokens) and Lq T X on float32 MFMA; step st takes token 4 st + g
             f32x4 W = {0.f, 0.f, 0.f, 0.f}, O = {0.f, 0.f, 0.f, 0.f};
             const float gct = C.gamC[n];
@@ -284,14 +313,18 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
             for (int r = 0; r < 4; ++r) L.o[c & 1][4 * g + r][j] = fmaf(C.gam[4 * g + r], PQ[r], O[r]);
 
             // M <- gamma_C M + K^T W, W in three bf16 parts: hi and mid of
-            // tokens 4 g + e in one 32-deep product, lo in a 16-deep one
+            // tokens 4 g + e in one 32-deep product, lo (and zeros) in a
+            // second one of the same shape.  Both products accumulate into
+            // the same registers back to back; a 16-deep product there
+            // instead lost the 32-deep one's result on some row tiles (the
+            // compiler inserts no wait between the two shapes).
             const float gC = C.gam[CT - 1];
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) acc[rt] *= gC;
             uint32_t wh[2], wm[2], wl[2];
             split3(W, wh, wm, wl);
             const bf16x8 BHM = __builtin_bit_cast(bf16x8, u32x4{wh[0], wh[1], wm[0], wm[1]});
-            const s16x4 BL = __builtin_bit_cast(s16x4, u32x2{wl[0], wl[1]});
+            const bf16x8 BL0 = __builtin_bit_cast(bf16x8, u32x4{wl[0], wl[1], 0u, 0u});
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) {
                 const int i = 16 * rt + n;
@@ -299,12 +332,15 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
 #pragma unroll
                 for (int e = 0; e < 4; ++e) au[e] = (short)C.kq[4 * g + e][i];
                 const u32x2 a2 = __builtin_bit_cast(u32x2, au);
-                acc[rt] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, u32x4{a2[0], a2[1], a2[0], a2[1]}), BHM, acc[rt]);
-                acc[rt] = mfma_bf16_k16(au, BL, acc[rt]);
+                const bf16x8 A2 = __builtin_bit_cast(bf16x8, u32x4{a2[0], a2[1], a2[0], a2[1]});
+                acc[rt] = mfma_bf16_k32(A2, BHM, acc[rt]);
+                acc[rt] = mfma_bf16_k32(A2, BL0, acc[rt]);
             }
         }
         lds_barrier();  // chunk c+1 staged, chunk c's outputs complete
         flush(c);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vcur[r] = vnext[r];
     }
 
     // ---- encode each column block once: absmax, scale, codes ----
@@ -343,7 +379,7 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
 }
 
 template <int DK, bool ERR>
-__global__ void __launch_bounds__(64 * (DK / 16 + 1)) prefill_mfma_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(64 * (DK / 16 + NPROD)) prefill_mfma_kernel(PrefillArgs a) {
     __shared__ PrefillLds<DK> L;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -381,14 +417,14 @@ hipError_t launch_prefill_mfma(const PoolView &p, int n_tok, const void *q, cons
     const bool err = p.colerr != nullptr;
     if (p.dk == 128) {
         if (err)
-            hipLaunchKernelGGL((prefill_mfma_kernel<128, true>), dim3(a.tiles), dim3(64 * 9), 0, s, a);
+            hipLaunchKernelGGL((prefill_mfma_kernel<128, true>), dim3(a.tiles), dim3(64 * (8 + NPROD)), 0, s, a);
         else
-            hipLaunchKernelGGL((prefill_mfma_kernel<128, false>), dim3(a.tiles), dim3(64 * 9), 0, s, a);
+            hipLaunchKernelGGL((prefill_mfma_kernel<128, false>), dim3(a.tiles), dim3(64 * (8 + NPROD)), 0, s, a);
     } else {
         if (err)
-            hipLaunchKernelGGL((prefill_mfma_kernel<64, true>), dim3(a.tiles), dim3(64 * 5), 0, s, a);
+            hipLaunchKernelGGL((prefill_mfma_kernel<64, true>), dim3(a.tiles), dim3(64 * (4 + NPROD)), 0, s, a);
         else
-            hipLaunchKernelGGL((prefill_mfma_kernel<64, false>), dim3(a.tiles), dim3(64 * 5), 0, s, a);
+            hipLaunchKernelGGL((prefill_mfma_kernel<64, false>), dim3(a.tiles), dim3(64 * (4 + NPROD)), 0, s, a);
     }
     return hipGetLastError();
 }
