@@ -37,9 +37,12 @@ def default_calls(w: inputs.Workload, n_periods: Optional[int] = None) -> List[T
 def run_case(w: inputs.Workload, seed: int, calls: Sequence[Tuple[int, int]],
              sample: Optional[np.ndarray] = None, head_bits=None,
              free_running: bool = True, label: str = "", workers: int = 1,
-             M0_gpu=None, M0_ref=None, warm_rel: float = WARM_REL) -> dict:
+             M0_gpu=None, M0_ref=None, warm_rel: float = WARM_REL,
+             tok_hook=None) -> dict:
     """Warm up, encode and decode on the GPU through the C ABI; check every
-    step against the oracle on the tiles in ``sample`` (all tiles if None)."""
+    step against the oracle on the tiles in ``sample`` (all tiles if None).
+    tok_hook(call index, tokens) may replace each call's tokens (both sides
+    then see the replaced ones)."""
     import torch
 
     from linear_attn_decode_pace_amd import pace, runtime
@@ -95,6 +98,8 @@ def run_case(w: inputs.Workload, seed: int, calls: Sequence[Tuple[int, int]],
     free_max_out = 0.0
     for ci, ((t0, t1), tok) in enumerate(zip(calls, inputs.iter_tokens(w, seed, inputs.SEG_DECODE,
                                                                        calls, workers))):
+        if tok_hook is not None:
+            tok = tok_hook(ci, tok)
         dt = runtime.DeviceTokens(tok)
         out = runtime.out_buffer(w, tok.T)
         st.decode(dt, out)

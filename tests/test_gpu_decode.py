@@ -1,4 +1,6 @@
 """Period decode on the GPU against the float64 oracle (through the C ABI)."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -56,3 +58,24 @@ def test_long_periods_ragged():
 def test_d64_long_periods():
     w = inputs.ragged("d64-long", 106, B=4, H=4, dk=64, dv=64, n_int8=1, period=16, steps=48)
     run_case(w, 7, [(0, 16), (16, 26), (26, 42), (42, 48)])
+
+
+def _vanishing_alpha(value):
+    # every token of the even sequences decays by `value`: over a period the
+    # product gamma_C falls below float32's normal range (or to zero), so the
+    # fused kernels take their below-normal-decay branch for those tiles
+    def hook(ci, tok):
+        a = tok.alpha.copy()
+        a[:, 0::2] = np.float32(value)
+        return dataclasses.replace(tok, alpha=a)
+    return hook
+
+
+@pytest.mark.parametrize("period,value", [(8, 1e-5), (16, 1e-5), (8, 2e-5)])
+def test_vanishing_decay(period, value):
+    # period 8 at 1e-5: gamma_C = 1e-40 (a float32 subnormal); period 16:
+    # 1e-80 (zero in float32); 2e-5 at period 8: gamma_C = 2.6e-38 is still
+    # normal, but gamma_C s falls below float32's normal range
+    w = inputs.ragged(f"vanish-k{period}", 107, B=4, H=3, n_int8=1, period=period, steps=2 * period)
+    run_case(w, 8, default_calls(w), tok_hook=_vanishing_alpha(value),
+             label=f"vanish-k{period}-{value:g}")

@@ -83,7 +83,15 @@ def test_window_masked_steps(name, kw, S):
     _run(name + "-mask", kw, S, masked=True)
 
 
-def _run(name, kw, S, masked):
+@pytest.mark.parametrize("name,kw,S", [CASES[0], CASES[2]])
+def test_window_tiny_columns(name, kw, S):
+    # the even state columns start at 1e-37 of their values (scales near the
+    # bottom of float32's normal range): a merge's lam alpha s then falls
+    # below it, while the merged write keeps the new column normal
+    _run(name + "-tiny", kw, S, masked=False, tiny_cols=True)
+
+
+def _run(name, kw, S, masked, tiny_cols=False):
     import torch
     from linear_attn_decode_pace_amd import pace, runtime
     w = inputs.ragged(name, 250, **kw)
@@ -92,8 +100,11 @@ def _run(name, kw, S, masked):
     n = w.B * w.H
     idx = np.arange(n)
     bits = np.tile(inputs.head_bits(w, seed), w.B).astype(np.int64)
-    st = runtime.State(w, inputs.head_bits(w, seed), pace.PACE_INIT_F32,
-                       runtime.warmup_state(w, seed), flags=pace.PACE_FP8_WINDOW, fp8_window=S)
+    M0 = runtime.warmup_state(w, seed)
+    if tiny_cols:
+        M0[..., 0::2] *= 1e-37
+    st = runtime.State(w, inputs.head_bits(w, seed), pace.PACE_INIT_F32, M0,
+                       flags=pace.PACE_FP8_WINDOW, fp8_window=S)
     rng = np.random.default_rng(11)
     flips = entries = merges = 0
     for t in range(w.steps):
