@@ -34,9 +34,10 @@ struct alignas(16) Tile16Lds {
     union {
         uint16_t v[C16][LROW16];
         struct {
-            float kkA[C16][C16];   // k_t.k_s, then A (strictly lower Gamma * K K^T) in place
-            float qkLq[C16][C16];  // q_t.k_s, then Lq, then Lq T in place
-            float Tt[C16][C16];    // Tt[s][t] = T[t][s]
+            // rows padded to CKS floats: a column's 16 entries in 16 banks
+            float kkA[C16][CKS];   // k_t.k_s, then A (strictly lower Gamma * K K^T) in place
+            float qkLq[C16][CKS];  // q_t.k_s, then Lq, then Lq T in place
+            float Tt[C16][CKS];    // Tt[s][t] = T[t][s]
         } m;
         float o[C16][OROW16];      // outputs of two column blocks
     } u;
