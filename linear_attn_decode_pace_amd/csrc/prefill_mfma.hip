@@ -13,7 +13,9 @@
 //     stages a chunk's keys and queries in LDS and computes its Gram products
 //     and gates two chunks ahead of the consumers, then its UT solve and
 //     Lq T one chunk ahead (three chunk buffers in LDS); the consumers read
-//     their own v values straight from the inputs, one chunk ahead;
+//     their own v values straight from the inputs, one chunk ahead, and
+//     build the next chunk's key table by state row for K^T W (16 rows
+//     each);
 //   * one workgroup barrier per chunk, ordering LDS only (global loads and
 //     stores stay in flight across it).
 // Per chunk and column block (WY / UT form, as the decode kernels):
@@ -49,6 +51,10 @@ struct alignas(16) ChunkLds {
     float LqT[CT][CT];  // (Lq T)[t][s]
     float gam[CT];      // gamma_t inside the chunk
     float gamC[CT];     // Gamma_{C-1, t}
+    // keys by state row for K^T W, built by the consumers: row i holds, per
+    // group gg of tokens 4 gg .. 4 gg + 3, their k[i] twice (16 bytes), the
+    // groups in the order gg ^ ((i % 16) / 4) (conflict-free row reads)
+    uint16_t kt[128][32];
 };
 
 struct alignas(16) PrepScratch {
@@ -240,6 +246,7 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
             if (p == 0) prep_b(L.ch[0], ps, lane);
         }
         lds_barrier();
+        lds_barrier();  // the consumers' key table of chunk 0
         for (int c = 0; c < n_chunks; ++c) {
             // this interval: phase B of chunk c + 1 or phase A of chunk c + 2
             if ((c + 1) % NPROD == p) {
@@ -253,6 +260,15 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
         return;
     }
 
+    lds_barrier();
+    // this wave's 16 rows of a chunk's key table: lane -> (row, token group)
+    auto build_kt = [&](ChunkLds &N) {
+        const int i = 16 * wave + (lane >> 2), gg = lane & 3;
+        const uint32_t a01 = (uint32_t)N.kq[4 * gg][i] | ((uint32_t)N.kq[4 * gg + 1][i] << 16);
+        const uint32_t a23 = (uint32_t)N.kq[4 * gg + 2][i] | ((uint32_t)N.kq[4 * gg + 3][i] << 16);
+        *(u32x4 *)&N.kt[i][8 * (gg ^ ((i & 15) >> 2))] = u32x4{a01, a23, a01, a23};
+    };
+    build_kt(L.ch[0]);
     lds_barrier();
     // A operand rows: the K block's row m is token 4 (m % 4) + m / 4, so P_K's
     // row 4 g + r is token 4 r + g (the B layout of the float32 chunk MFMAs);
@@ -272,6 +288,7 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
     for (int c = 0; c < n_chunks; ++c) {
         if (c + 1 < n_chunks) load_v(c + 1, vnext);
         ChunkLds &C = L.ch[c % NBUF];
+        if (c + 1 < n_chunks) build_kt(L.ch[(c + 1) % NBUF]);  // staged before the last barrier
         {
             // P_K = K M0 over three bf16 parts of M0 (the state update needs
             // float32 accuracy), P_Q = Q M0 over two (outputs only)
@@ -327,12 +344,8 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
             const bf16x8 BL0 = __builtin_bit_cast(bf16x8, u32x4{wl[0], wl[1], 0u, 0u});
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) {
-                const int i = 16 * rt + n;
-                s16x4 au;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) au[e] = (short)C.kq[4 * g + e][i];
-                const u32x2 a2 = __builtin_bit_cast(u32x2, au);
-                const bf16x8 A2 = __builtin_bit_cast(bf16x8, u32x4{a2[0], a2[1], a2[0], a2[1]});
+                // k of tokens 4 g .. 4 g + 3 at row 16 rt + n, twice
+                const bf16x8 A2 = __builtin_bit_cast(bf16x8, *(const u32x4 *)&C.kt[16 * rt + n][8 * (g ^ (n >> 2))]);
                 acc[rt] = mfma_bf16_k32(A2, BHM, acc[rt]);
                 acc[rt] = mfma_bf16_k32(A2, BL0, acc[rt]);
             }
