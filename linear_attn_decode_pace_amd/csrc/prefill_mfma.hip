@@ -5,28 +5,36 @@
 // that to decode: 'PACE: four-bit recurrent state by rounding less often',
 // TL;DR point (1)).
 //
-// One workgroup per state tile, resident for the whole prompt:
+// Chunks of 32 tokens in the WY / UT form, split into two 16-token halves H1,
+// H2 (one MFMA tile of rows each).  One workgroup per state tile, resident
+// for the whole prompt:
 //   * NCB consumer waves (one per 16-column block) hold the tile's float32
-//     state in MFMA accumulator layout (the same lane -> (row, column) map as
-//     the pool layout) from the first token to the final encode;
-//   * two producer waves, on different SIMDs, take alternate chunks: each
-//     stages a chunk's keys and queries in LDS and computes its Gram products
-//     and gates two chunks ahead of the consumers, then its UT solve and
-//     Lq T one chunk ahead (three chunk buffers in LDS); the consumers read
-//     their own v values straight from the inputs, one chunk ahead, and
-//     build the next chunk's key table by state row for K^T W (16 rows
-//     each);
+//     state in registers from the first token to the final encode;
+//   * two producer waves, on different SIMDs, take alternate chunks.  A
+//     producer copies a chunk's keys, queries and gates from HBM straight
+//     into LDS (no registers) one interval before it needs them, computes
+//     the chunk's Gram blocks and gates (phase A) two chunks ahead of the
+//     consumers, then its UT solve and Lq T (phase B) one chunk ahead (four
+//     chunk buffers in LDS).  The token matrices are block lower triangular:
+//     the diagonal blocks of T come from forward substitution, the
+//     off-diagonal one from T21 = -T22 A21 T11;
+//   * the consumers read their own v values straight from the inputs, one
+//     chunk ahead, build the next chunk's key table by state row, and write
+//     the outputs;
 //   * one workgroup barrier per chunk, ordering LDS only (global loads and
 //     stores stay in flight across it).
-// Per chunk and column block (WY / UT form, as the decode kernels):
+// Per chunk and column block:
 //   P_K = K M0 with M0 split exactly into three bf16 parts (hi + mid + lo), so
 //   the state update keeps float32 accuracy; P_Q = Q M0 over hi + mid (it
 //   only reaches the outputs, and two parts leave ~1e-5 relative error);
-//   X = V - diag(g) P_K; W = diag(G_C) T X and Lq T X on float32 MFMA;
-//   O = Lq T X + diag(g) P_Q; M <- g_C M + K^T W (bf16 MFMA, W in three parts:
-//   hi and mid in one 32-deep product, lo in a second one).
-// Outputs of a chunk go through double-buffered LDS and leave as whole
-// 512-byte rows.
+//   X = V - diag(g) P_K; W = diag(G') T X and Lq T X on float32 MFMA;
+//   O = Lq T X + diag(g) P_Q; M <- g_C M + K^T W (bf16 MFMA, W in three
+//   parts, each a 32-deep product over the chunk's tokens).
+// While a chunk is applied, lane group g of a consumer holds state rows
+// 32 ks + 8 g .. 32 ks + 8 g + 7 of each 32-row slice ks, so its MFMA k-slots
+// are eight adjacent key columns (one 16-byte LDS read); the stored pool
+// layout is restored for the final encode.  Outputs of a chunk go through
+// double-buffered LDS and leave as whole rows.
 #include "chunk16.h"
 #include "pace_prefill.h"
 
@@ -41,34 +49,75 @@ __device__ inline void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-constexpr int CT = CK;      // tokens per chunk
-constexpr int PROW = 136;   // bf16 elements per LDS token row (128 + 8 padding)
-constexpr int OPAD = 132;   // floats per LDS output row
+// The producers' side of the same barrier.  A memory fence would also wait
+// for the producer's buffer-to-LDS loads still in flight (they write LDS),
+// which are meant to land an interval later; this waits for its LDS
+// instructions only and keeps the compiler from moving memory accesses
+// across it.
+__device__ inline void producer_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
+// Hide a value's origin from the optimiser: lane-dependent masks, constants
+// and offsets are then recomputed where they are used instead of being
+// hoisted out of the chunk loop, where they would hold registers for the
+// whole prompt.
+__device__ inline void launder(int &x) { asm volatile("" : "+v"(x)); }
+
+constexpr int CT = 32;      // tokens per chunk
+constexpr int HT = 16;      // tokens per half chunk
+constexpr int OPAD = 132;   // floats per LDS output row
+constexpr int KS = 18;      // row stride of the Gram / gate blocks (column reads stay
+                            // free of bank conflicts)
+
+// 16-byte piece p of key / query row `row` sits in LDS slot p ^ kq_swz(row):
+// the 16 rows one MFMA operand read touches then fall in 16 different bank
+// groups
+template <int DK>
+__device__ inline int kq_swz(int row) {
+    return DK == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int DK>
+__device__ inline u32x4 kq_piece(const uint16_t (*kq)[DK], int row, int p) {
+    return *(const u32x4 *)&kq[row][8 * (p ^ kq_swz<DK>(row))];
+}
+
+// State row held by MFMA row m of row tile rt in the chunk layout
+__device__ inline int chunk_row(int rt, int m) {
+    return 32 * (rt >> 1) + 8 * (m >> 2) + 4 * (rt & 1) + (m & 3);
+}
+
+// Blocks of a chunk's lower-triangular token matrices: 0 = (H1, H1),
+// 1 = (H2, H1), 2 = (H2, H2).
+template <int DK>
 struct alignas(16) ChunkLds {
-    uint16_t kq[2 * CT][PROW];  // rows 0..15: k_t, rows 16..31: q_t (bf16 bits)
-    float Tt[CT][CT];   // Tt[s][t] = T[t][s]
-    float LqT[CT][CT];  // (Lq T)[t][s]
-    float gam[CT];      // gamma_t inside the chunk
-    float gamC[CT];     // Gamma_{C-1, t}
-    // keys by state row for K^T W, built by the consumers: row i holds, per
-    // group gg of tokens 4 gg .. 4 gg + 3, their k[i] twice (16 bytes), the
-    // groups in the order gg ^ ((i % 16) / 4) (conflict-free row reads)
-    uint16_t kt[128][32];
+    uint16_t kq[2 * CT][DK];  // rows 0..31: k_t, rows 32..63: q_t (bf16, pieces swizzled)
+    float TGt[3][HT][HT];     // TGt[b][s][t] = G'_t T_b[t][s]   (diag(G') T, transposed)
+    float LqTt[3][HT][HT];    // LqTt[b][s][t] = (Lq T)_b[t][s]
+    float gam[CT];            // gamma_t = alpha_0 ... alpha_t
+    float ab[2 * CT];         // alpha_t, then beta_t (padding tokens: 1, 0)
 };
 
 struct alignas(16) PrepScratch {
-    float alpha[CT], beta[CT];
-    float kkA[CT][CT];   // k_t . k_s, then A in place
-    float qkLq[CT][CT];  // q_t . k_s, then Lq in place
+    float gh[2][HT];    // per half: alpha products from the half's start to t
+    float gch[2][HT];   // per half: alpha products over (t, half end]
+    float gcp[CT];      // G'_t = alpha products over (t, chunk end]
+    float kk[3][HT][KS];  // k_t . k_s per block, then A in place
+    float qk[3][HT][KS];  // q_t . k_s per block, then Lq in place
+    float T[3][HT][HT];   // T blocks, natural layout (block 1 holds A21 T11 first)
 };
 
-constexpr int NBUF = 3;  // chunk buffers: applied, being prepared, being staged
+constexpr int NBUF = 4;  // chunk buffers: applied, prepared (B), prepared (A), loading
 constexpr int NPROD = 2; // producer waves
 
 template <int DK>
 struct PrefillLds {
-    ChunkLds ch[NBUF];
+    ChunkLds<DK> ch[NBUF];
+    // keys by state row for K^T W, built by the consumers one chunk ahead
+    // (double buffered): row i holds, per group gg, k[i] of tokens
+    // 4 gg .. 4 gg + 3 and 16 + 4 gg .. 16 + 4 gg + 3 (16 bytes), the groups
+    // in the order gg ^ ((i / 8) % 4) (conflict-free reads)
+    alignas(16) uint16_t kt[2][DK][32];
     PrepScratch ps[NPROD];
     alignas(16) float o[2][CT][OPAD];
 };
@@ -82,72 +131,171 @@ struct PrefillArgs {
     int tiles;
 };
 
+// Producer: copy chunk c's k and q rows and its alpha / beta from HBM into
+// LDS (buffer-to-LDS loads: lane l of each instruction fills 16 bytes at
+// 16 l).  Tokens past the prompt repeat its last token; phase A resets their
+// gates.
 template <int DK>
-struct TokenRegs {
-    static constexpr int CPR = DK / 8;            // 16-byte chunks per token row
-    static constexpr int NL = 2 * CT * CPR / 64;  // loads per lane (k and q rows)
-    u32x4 val[NL];
-    float ab;
-};
-
-// Producer, part 1: issue the loads of chunk c's tokens (k, q, v rows, then
-// alpha / beta) into registers; padding tokens are zero (alpha 1, beta 0).
-template <int DK>
-__device__ __attribute__((always_inline)) inline void load_chunk(const PrefillArgs &a, TokenRegs<DK> &R, size_t tile_row, int c,
-                                  int lane) {
-    constexpr int CPR = TokenRegs<DK>::CPR;
+__device__ __attribute__((always_inline)) inline void issue_chunk(const PrefillArgs &a, ChunkLds<DK> &N,
+                                                                  size_t tile_row, int c, int lane) {
+    launder(lane);
+    constexpr int SPR = DK / 8;    // 16-byte slots per row
+    constexpr int RPI = 64 / SPR;  // rows per instruction
     const uint32_t tok_stride = (uint32_t)a.p.B * (uint32_t)a.p.H;
-    const int t0 = CT * c, nv = min(CT, a.n_tok - t0);
+    const int t0 = CT * c, last = a.n_tok - 1 - t0;
     const size_t base = ((size_t)t0 * tok_stride + tile_row) * DK;
 #pragma unroll
-    for (int it = 0; it < TokenRegs<DK>::NL; ++it) {
-        const int e = lane + 64 * it;
-        const int row = e / CPR, col = (e % CPR) * 8;
-        const int t = row & 15;
-        // the 32 rows are k, q in blocks of 16: the block is fixed per load
-        constexpr int RPL = 64 / CPR;  // rows per load
-        const int which = (it * RPL) / CT;
+    for (int it = 0; it < 2 * CT / RPI; ++it) {
+        const int row = it * RPI + lane / SPR, slot = lane % SPR;
+        const int which = (it * RPI) / CT;  // k rows, then q rows
+        const int t = min(row & (CT - 1), last);
+        const int piece = slot ^ kq_swz<DK>(row);
         const uint16_t *src = (which == 0 ? a.k : a.q) + base;
-        R.val[it] = u32x4{0u, 0u, 0u, 0u};
-        if (t < nv)
-            R.val[it] = __builtin_nontemporal_load(
-                at((const u32x4 *)src, (uint32_t)(t * tok_stride * DK + col) * 2u));
+        __builtin_amdgcn_global_load_lds(at(src, (uint32_t)(t * tok_stride * DK + 8 * piece) * 2u),
+                                         (__attribute__((address_space(3))) void *)&N.kq[it * RPI][0], 16, 0, 0);
     }
-    R.ab = 0.f;
-    if (lane < 32) {
-        const int t = lane & 15;
-        const bool is_beta = lane >= 16;
-        R.ab = is_beta ? 0.f : 1.f;
-        if (t < nv) R.ab = (is_beta ? a.beta : a.alpha)[((size_t)t0 + t) * tok_stride + tile_row];
-    }
+    const int t = min(lane & (CT - 1), last);
+    const float *gsrc = (lane < CT ? a.alpha : a.beta) + ((size_t)t0 + t) * tok_stride + tile_row;
+    __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void *)&N.ab[0], 4, 0, 0);
 }
 
-// Producer, part 2: write the loaded chunk into LDS.
+// kk[t][s] = k_{t0+t} . k_{s0+s}, qk[t][s] = q_{t0+t} . k_{s0+s} for one
+// 16 x 16 block: the A row m is token t0 + 4 (m % 4) + m / 4, so output row
+// 4 g + r is token t0 + 4 r + g
 template <int DK>
-__device__ __attribute__((always_inline)) inline void stage_chunk(const TokenRegs<DK> &R, ChunkLds &L, PrepScratch &S, int lane) {
-    constexpr int CPR = TokenRegs<DK>::CPR;
+__device__ inline void gram_block(const uint16_t (*kq)[DK], int t0, int s0, float (*kk)[KS],
+                                  float (*qk)[KS], int lane) {
+    constexpr int NKS = DK / 32;
+    const int g = lane >> 4, n = lane & 15;
+    const int tok_n = 4 * (n & 3) + (n >> 2);
+    f32x4 GK = {0.f, 0.f, 0.f, 0.f}, GQ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int it = 0; it < TokenRegs<DK>::NL; ++it) {
-        const int e = lane + 64 * it;
-        const int row = e / CPR, col = (e % CPR) * 8;
-        const int t = row & 15, which = row >> 4;
-        uint16_t *dst = &L.kq[which * 16 + t][col];
-        *(u32x4 *)dst = R.val[it];
+    for (int ks = 0; ks < NKS; ++ks) {
+        const int p = 4 * ks + g;
+        const bf16x8 AK = __builtin_bit_cast(bf16x8, kq_piece<DK>(kq, t0 + tok_n, p));
+        const bf16x8 AQ = __builtin_bit_cast(bf16x8, kq_piece<DK>(kq, CT + t0 + tok_n, p));
+        const bf16x8 BS = __builtin_bit_cast(bf16x8, kq_piece<DK>(kq, s0 + n, p));
+        GK = mfma_bf16_k32(AK, BS, GK);
+        GQ = mfma_bf16_k32(AQ, BS, GQ);
     }
-    if (lane < 32) (lane >= 16 ? S.beta : S.alpha)[lane & 15] = R.ab;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        kk[4 * r + g][n] = GK[r];
+        qk[4 * r + g][n] = GQ[r];
+    }
 }
 
-// Producer, part 3: the staged chunk's token-only matrices, in two phases
-// of about equal length (Gram products and gates; UT solve and Lq T).
-template <int DK>
-__device__ __attribute__((always_inline)) inline void prep_a(ChunkLds &L, PrepScratch &S, int lane) {
-    wave_sync();
-    chunk16_gram<DK, PROW>(L.kq, S.kkA, S.qkLq, lane);
-    chunk16_gates(S.alpha, S.kkA, S.qkLq, S.kkA, S.qkLq, L.gam, L.gamC, lane);
+// D += X Y for 16 x 16 float matrices on float32 MFMA (output row 4 g + r,
+// column n), and D += (X Y)^T
+template <int XS, int YS>
+__device__ inline f32x4 mm16(const float (*X)[XS], const float (*Y)[YS], f32x4 D, int lane) {
+    const int g = lane >> 4, n = lane & 15;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) D = mfma_f32_k4(X[n][4 * st + g], Y[4 * st + g][n], D);
+    return D;
 }
-__device__ __attribute__((always_inline)) inline void prep_b(ChunkLds &L, PrepScratch &S, int lane) {
-    chunk16_ut(S.kkA, S.beta, L.Tt, lane);
-    chunk16_lqt(S.qkLq, L.Tt, L.LqT, lane);
+template <int XS, int YS>
+__device__ inline f32x4 mm16t(const float (*X)[XS], const float (*Y)[YS], f32x4 D, int lane) {
+    const int g = lane >> 4, n = lane & 15;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) D = mfma_f32_k4(Y[4 * st + g][n], X[n][4 * st + g], D);
+    return D;
+}
+
+// Producer, phase A: Gram blocks and gates of a loaded chunk.
+//   Gamma_{t,s} = prod_{s<r<=t} alpha_r; inside a half from its own gates,
+//   across the halves Gamma_{16+t, s} = gch[0][s] gh[1][t].
+template <int DK>
+__device__ __attribute__((always_inline)) inline void prep_a(ChunkLds<DK> &L, PrepScratch &S, int lane) {
+    launder(lane);
+    wave_sync();
+    gram_block<DK>(L.kq, 0, 0, S.kk[0], S.qk[0], lane);
+    gram_block<DK>(L.kq, HT, 0, S.kk[1], S.qk[1], lane);
+    gram_block<DK>(L.kq, HT, HT, S.kk[2], S.qk[2], lane);
+    wave_sync();
+    chunk16_gates<KS>(L.ab, S.kk[0], S.qk[0], S.kk[0], S.qk[0], S.gh[0], S.gch[0], lane);
+    chunk16_gates<KS>(L.ab + HT, S.kk[2], S.qk[2], S.kk[2], S.qk[2], S.gh[1], S.gch[1], lane);
+    {
+        const int t = lane >> 2, s0 = 4 * (lane & 3);
+        const float gt = S.gh[1][t];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float f = gt * S.gch[0][s0 + e];
+            S.kk[1][t][s0 + e] *= f;
+            S.qk[1][t][s0 + e] *= f;
+        }
+    }
+    if (lane < CT) {
+        L.gam[lane] = lane < HT ? S.gh[0][lane] : S.gh[0][HT - 1] * S.gh[1][lane - HT];
+        S.gcp[lane] = lane < HT ? S.gch[0][lane] * S.gh[1][HT - 1] : S.gch[1][lane - HT];
+    }
+    wave_sync();
+}
+
+// Producer, part 4 (phase B): T = (I + diag(beta) A)^-1 diag(beta) block by
+// block, diag(G') T and Lq T for the consumers.
+template <int DK>
+__device__ __attribute__((always_inline)) inline void prep_b(ChunkLds<DK> &L, PrepScratch &S, int lane) {
+    launder(lane);
+    const int g = lane >> 4, n = lane & 15;
+    {
+        // diagonal blocks by forward substitution, one column s per lane:
+        // lanes 0..15 the first half, lanes 32..47 the second (lanes 16..31
+        // and 48..63 repeat them and store nothing)
+        const int hb = lane >> 5, s = lane & 15;
+        const float(*A)[KS] = S.kk[2 * hb];
+        const float *be_p = L.ab + CT + HT * hb;
+        float be[HT], z[HT];
+#pragma unroll
+        for (int r = 0; r < HT; ++r) be[r] = be_p[r];
+#pragma unroll
+        for (int t = 0; t < HT; ++t) {
+            float sum = 0.f;
+#pragma unroll
+            for (int u = 0; u < t; ++u) sum = fmaf(A[t][u], z[u], sum);
+            z[t] = (t == s ? 1.f : 0.f) - be[t] * sum;
+        }
+        if ((lane & 31) < HT) {
+            const float bs = be_p[s];
+            float(*T)[HT] = S.T[2 * hb];
+            float(*TG)[HT] = L.TGt[2 * hb];
+            const float *gp = S.gcp + HT * hb;
+#pragma unroll
+            for (int t = 0; t < HT; ++t) T[t][s] = z[t] * bs;
+#pragma unroll
+            for (int q = 0; q < HT / 4; ++q)
+                *(f32x4 *)&TG[s][4 * q] = f32x4{gp[4 * q] * z[4 * q] * bs, gp[4 * q + 1] * z[4 * q + 1] * bs,
+                                                gp[4 * q + 2] * z[4 * q + 2] * bs,
+                                                gp[4 * q + 3] * z[4 * q + 3] * bs};
+        }
+    }
+    wave_sync();
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    // T21 = -T22 (A21 T11): block 1 of T holds A21 T11 until T21 replaces it
+    f32x4 D = mm16(S.kk[1], S.T[0], zero, lane);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) S.T[1][4 * g + r][n] = D[r];
+    wave_sync();
+    D = mm16(S.T[2], S.T[1], zero, lane);
+    wave_sync();  // A21 T11 is read before T21 replaces it
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float x = -D[r];
+        S.T[1][4 * g + r][n] = x;
+        L.TGt[1][n][4 * g + r] = S.gcp[HT + 4 * g + r] * x;
+    }
+    wave_sync();
+    // (Lq T)^T block by block, written row by row
+    D = mm16t(S.qk[0], S.T[0], zero, lane);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) L.LqTt[0][4 * g + r][n] = D[r];
+    D = mm16t(S.qk[2], S.T[2], zero, lane);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) L.LqTt[2][4 * g + r][n] = D[r];
+    D = mm16t(S.qk[2], S.T[1], mm16t(S.qk[1], S.T[0], zero, lane), lane);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) L.LqTt[1][4 * g + r][n] = D[r];
+    wave_sync();
 }
 
 // x - (low / high bf16 of pk) in one instruction: a bf16 dot product with
@@ -177,6 +325,48 @@ __device__ inline void split3(const f32x4 &x, uint32_t hi[2], uint32_t md[2], ui
     lo[1] = pk_bf16(sub_lo(md[1], r2), sub_hi(md[1], r3));
 }
 
+// Chunk layout <-> pool layout of a column block's state (lane (g, n); four
+// rows per register quad).  Pool layout: acc[2 ks + h][r] is row
+// 32 ks + 16 h + 4 g + r; chunk layout: acc[2 ks + h][r] is row
+// 32 ks + 8 g + 4 h + r.  Rows move between the four lane groups of column
+// n (ds_bpermute), once at the start of a prompt and once before the encode.
+template <int NKS>
+__device__ inline void to_chunk_layout(f32x4 *acc, int lane) {
+    const int g = lane >> 4, n = lane & 15;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        const f32x4 a0 = acc[2 * ks], a1 = acc[2 * ks + 1];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int src = 4 * ((((2 * g + h) & 3) << 4) | n);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x0 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(a0[r])));
+                const float x1 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(a1[r])));
+                acc[2 * ks + h][r] = (g >> 1) ? x1 : x0;
+            }
+        }
+    }
+}
+template <int NKS>
+__device__ inline void to_pool_layout(f32x4 *acc, int lane) {
+    const int g = lane >> 4, n = lane & 15;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        const f32x4 c0 = acc[2 * ks], c1 = acc[2 * ks + 1];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int src = 4 * (((2 * t + (g >> 1)) << 4) | n);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x0 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(c0[r])));
+                const float x1 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(c1[r])));
+                acc[2 * ks + t][r] = (g & 1) ? x1 : x0;
+            }
+        }
+    }
+}
+
 template <int DK, int BITS, bool ERR>
 __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int h, int slot,
                              int wave, int lane) {
@@ -197,166 +387,243 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
         : a.p.codes8 + ((size_t)b * a.p.n8 + slot) * tile_code_bytes(DK, DK, 8);
     float *scl = a.p.scales + tile_row * DK;
 
+    if (producer) {
+        // Two producers take alternate chunks.  Chunk c's tokens are copied
+        // into LDS during interval c - 3 (at the start of phase B of chunk
+        // c - 2, by the same producer), its Gram blocks and gates computed
+        // (phase A) while the consumers apply chunk c - 2, its UT solve and
+        // Lq T (phase B) while they apply chunk c - 1.  Each producer
+        // alternates A and B, so both carry half of the work every interval,
+        // on different SIMDs; a producer's only memory operations are its
+        // own buffer-to-LDS loads, so waiting for them all at the start of
+        // phase A waits for nothing else.  Phase B (the forward substitution
+        // is a long serial chain) runs at raised wave priority, ahead of the
+        // consumers sharing its SIMD.
+        const int p = wave - NCB;
+        PrepScratch &ps = L.ps[p];
+        auto phase_a = [&](int c) {
+            ChunkLds<DK> &N = L.ch[c % NBUF];
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): chunk c is in LDS
+            const int nv = a.n_tok - CT * c;
+            if (lane < CT && lane >= nv) {  // padding tokens leave the state alone
+                N.ab[lane] = 1.f;
+                N.ab[CT + lane] = 0.f;
+            }
+            prep_a<DK>(N, ps, lane);
+        };
+        auto phase_b = [&](int c) {
+            if (c + NPROD < n_chunks) issue_chunk<DK>(a, L.ch[(c + NPROD) % NBUF], tile_row, c + NPROD, lane);
+            __builtin_amdgcn_s_setprio(3);
+            prep_b<DK>(L.ch[c % NBUF], ps, lane);
+            __builtin_amdgcn_s_setprio(0);
+        };
+        if (p < n_chunks) {
+            issue_chunk<DK>(a, L.ch[p], tile_row, p, lane);
+            phase_a(p);
+            if (p == 0) phase_b(0);
+        }
+        producer_barrier();
+        producer_barrier();  // the consumers' key table of chunk 0
+        for (int c = 0; c < n_chunks; ++c) {
+            // this interval: phase B of chunk c + 1 (after issuing chunk
+            // c + 3's loads) or phase A of chunk c + 2
+            if ((c + 1) % NPROD == p) {
+                if (c + 1 < n_chunks) phase_b(c + 1);
+            } else if (c + 2 < n_chunks) {
+                phase_a(c + 2);
+            }
+            producer_barrier();  // chunk c+1 prepared, chunk c's outputs complete
+        }
+        return;
+    }
+
     // the column block's starting state: the stored codes decoded (zero after
-    // a zero initialisation)
+    // a zero initialisation), in chunk layout
     f32x4 acc[NRT];
-    if (!producer) {
+    {
         Loader<DK, BITS> ld;
         ld.load(codes, cb, lane);
         ld.codes_f32(acc);
         const float sk = scl[j] * (1.f / KAPPA);
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) acc[rt] *= sk;
+        to_chunk_layout<NKS>(acc, lane);
     }
-    // Output flush of chunk c, shared by every wave after the barrier that
-    // closes it: rows of DK floats, 16 bytes per lane.  Staging buffer c & 1
-    // is written again only in chunk c + 2, after the next barrier, by which
-    // every wave has finished this flush.
-    auto flush = [&](int c) {
+    // Output flush of chunk c by the consumers after the barrier that closes
+    // it: rows of DK floats, 16 bytes per lane.  Staging buffer c & 1 is
+    // written again only in chunk c + 2, after the next barrier, by which
+    // every consumer has finished this flush.
+    auto flush = [&](int c, int ln) {
         if (!a.out) return;
-        constexpr int PER_ROW = DK / 4;
-        const int e = wave * 64 + lane;
-        const int t = e / PER_ROW, c4 = (e % PER_ROW) * 4;
-        if (t < CT && t < a.n_tok - CT * c) {  // chunk c's real tokens
-            const f32x4 x = *(const f32x4 *)&L.o[c & 1][t][c4];
-            __builtin_nontemporal_store(
-                x, (f32x4 *)(a.out + (((size_t)CT * c + t) * tok_stride + tile_row) * DK + c4));
-        }
-    };
-
-    if (producer) {
-        // Two producers take alternate chunks.  Chunk c is staged and its
-        // Gram products and gates computed (phase A) while the consumers
-        // apply chunk c - 2, its UT solve and Lq T (phase B) while they apply
-        // chunk c - 1; its tokens were loaded into the producer's registers
-        // two intervals earlier.  Each producer alternates A and B, so both
-        // carry half of the work every interval, on different SIMDs.
-        const int p = wave - NCB;
-        PrepScratch &ps = L.ps[p];
-        TokenRegs<DK> R;
-        auto phase_a = [&](int c) {
-            ChunkLds &N = L.ch[c % NBUF];
-            stage_chunk<DK>(R, N, ps, lane);
-            if (c + NPROD < n_chunks) load_chunk<DK>(a, R, tile_row, c + NPROD, lane);
-            prep_a<DK>(N, ps, lane);
-        };
-        if (p < n_chunks) {
-            load_chunk<DK>(a, R, tile_row, p, lane);
-            phase_a(p);
-            if (p == 0) prep_b(L.ch[0], ps, lane);
-        }
-        lds_barrier();
-        lds_barrier();  // the consumers' key table of chunk 0
-        for (int c = 0; c < n_chunks; ++c) {
-            // this interval: phase B of chunk c + 1 or phase A of chunk c + 2
-            if ((c + 1) % NPROD == p) {
-                if (c + 1 < n_chunks) prep_b(L.ch[(c + 1) % NBUF], ps, lane);
-            } else if (c + 2 < n_chunks) {
-                phase_a(c + 2);
-            }
-            lds_barrier();  // chunk c+1 prepared, chunk c's outputs complete
-            flush(c);
-        }
-        return;
-    }
-
-    lds_barrier();
-    // this wave's 16 rows of a chunk's key table: lane -> (row, token group)
-    auto build_kt = [&](ChunkLds &N) {
-        const int i = 16 * wave + (lane >> 2), gg = lane & 3;
-        const uint32_t a01 = (uint32_t)N.kq[4 * gg][i] | ((uint32_t)N.kq[4 * gg + 1][i] << 16);
-        const uint32_t a23 = (uint32_t)N.kq[4 * gg + 2][i] | ((uint32_t)N.kq[4 * gg + 3][i] << 16);
-        *(u32x4 *)&N.kt[i][8 * (gg ^ ((i & 15) >> 2))] = u32x4{a01, a23, a01, a23};
-    };
-    build_kt(L.ch[0]);
-    lds_barrier();
-    // A operand rows: the K block's row m is token 4 (m % 4) + m / 4, so P_K's
-    // row 4 g + r is token 4 r + g (the B layout of the float32 chunk MFMAs);
-    // the Q block's row m is token m, so P_Q's rows line up with O's
-    const int tok_n = 4 * (n & 3) + (n >> 2);
-    // this lane's v values (tokens 4 r + g of a chunk, column j), read from
-    // the inputs one chunk ahead
-    auto load_v = [&](int c, uint32_t (&vv)[4]) {
+        constexpr int PER_ROW = DK / 4;          // lanes per output row
+        constexpr int ROWS = 64 * NCB / PER_ROW; // rows per pass
+        const int e = wave * 64 + ln;
+        const int nv = a.n_tok - CT * c;
+        float *obase = a.out + ((size_t)CT * c * tok_stride + tile_row) * DK;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = CT * c + 4 * r + g;
-            vv[r] = t < a.n_tok ? (uint32_t)a.v[((size_t)t * tok_stride + tile_row) * DK + j] : 0u;
+        for (int t0 = 0; t0 < CT; t0 += ROWS) {
+            const int t = t0 + e / PER_ROW, c4 = (e % PER_ROW) * 4;
+            if (t < nv) {  // chunk c's real tokens
+                const f32x4 x = *(const f32x4 *)&L.o[c & 1][t][c4];
+                __builtin_nontemporal_store(
+                    x, at((f32x4 *)obase, (uint32_t)(t * tok_stride * DK + c4) * 4u));
+            }
         }
     };
-    uint32_t vcur[4], vnext[4];
-    load_v(0, vcur);
-    for (int c = 0; c < n_chunks; ++c) {
-        if (c + 1 < n_chunks) load_v(c + 1, vnext);
-        ChunkLds &C = L.ch[c % NBUF];
-        if (c + 1 < n_chunks) build_kt(L.ch[(c + 1) % NBUF]);  // staged before the last barrier
+
+    lds_barrier();
+    // this wave's 16 rows of a chunk's key table: lane -> (state row, token group)
+    auto build_kt = [&](const ChunkLds<DK> &N, uint16_t (*KT)[32], int ln) {
+        const int i = 16 * wave + (ln >> 2), gg = ln & 3;
+        uint32_t w[4];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int t = HT * hh + 4 * gg;
+            uint32_t e[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                e[x] = N.kq[t + x][8 * ((i >> 3) ^ kq_swz<DK>(t + x)) + (i & 7)];
+            w[2 * hh] = e[0] | (e[1] << 16);
+            w[2 * hh + 1] = e[2] | (e[3] << 16);
+        }
+        *(u32x4 *)&KT[i][8 * (gg ^ ((i >> 3) & 3))] = u32x4{w[0], w[1], w[2], w[3]};
+    };
+    build_kt(L.ch[0], L.kt[0], lane);
+    lds_barrier();
+    // this lane's v values: tokens 4 e + g of a chunk (e = 0..7), column j,
+    // read from the inputs one chunk ahead
+    // Every chunk issues the same eight loads (past the prompt they repeat
+    // its last token: padding tokens have beta = 0, so their v never
+    // reaches the state or a real output), which keeps the count of memory
+    // operations static and the compiler's waits for them exact.
+    auto load_v = [&](int c, uint16_t (&vv)[8], int g, int j) {
+        const int cc = min(c, n_chunks - 1), last = a.n_tok - 1 - CT * cc;
+        const uint16_t *vbase = a.v + ((size_t)CT * cc * tok_stride + tile_row) * DK;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int t = min(4 * e + g, last);
+            vv[e] = *at(vbase, (uint32_t)(t * tok_stride * DK + j) * 2u);
+        }
+    };
+    // v values of the chunk being applied and of the next one, in two
+    // register sets that swap roles every chunk (the loop is unrolled by two,
+    // so no copies: a copy would have to wait for the loads, and a wait for
+    // loads may mean a wait for every memory operation issued after them)
+    uint16_t va[8], vb[8];
+    load_v(0, va, g, j);
+    // the first chunk's v values are waited for here, so that inside the loop
+    // the compiler's wait for them is not merged with the prologue's loads
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    auto step = [&](int c, const uint16_t (&vcur)[8], uint16_t (&vnext)[8]) __attribute__((always_inline)) {
+        // lane-derived offsets are recomputed per chunk rather than held
+        // across the loop (register pressure)
+        int ln = lane;
+        launder(ln);
+        const int g = ln >> 4, n = ln & 15, j = 16 * cb + n;
+        // A operand rows: the K blocks' row m is token 4 (m % 4) + m / 4 of
+        // its half, so P_K's row 4 g + r is token 4 r + g (the B layout of the
+        // float32 chunk MFMAs); the Q blocks' row m is token m, so P_Q's rows
+        // line up with O's
+        const int tok_n = 4 * (n & 3) + (n >> 2);
+        load_v(c + 1, vnext, g, j);
+        const ChunkLds<DK> &C = L.ch[c % NBUF];
+        const uint16_t(*KT)[32] = L.kt[c & 1];
+        if (c + 1 < n_chunks) build_kt(L.ch[(c + 1) % NBUF], L.kt[(c + 1) & 1], ln);
         {
             // P_K = K M0 over three bf16 parts of M0 (the state update needs
-            // float32 accuracy), P_Q = Q M0 over two (outputs only)
-            f32x4 PK = {0.f, 0.f, 0.f, 0.f}, PQ = {0.f, 0.f, 0.f, 0.f};
+            // float32 accuracy), P_Q = Q M0 over two (outputs only), both
+            // halves of the chunk; k-slot 8 g + e is state row 32 ks + 8 g + e
+            f32x4 PK1 = {0.f, 0.f, 0.f, 0.f}, PK2 = PK1, PQ1 = PK1, PQ2 = PK1;
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                const int c0 = 32 * ks + 4 * g, c1 = c0 + 16;
-                const u32x2 k0 = *(const u32x2 *)&C.kq[tok_n][c0], k1 = *(const u32x2 *)&C.kq[tok_n][c1];
-                const u32x2 q0 = *(const u32x2 *)&C.kq[16 + n][c0], q1 = *(const u32x2 *)&C.kq[16 + n][c1];
-                const bf16x8 AK = __builtin_bit_cast(bf16x8, u32x4{k0[0], k0[1], k1[0], k1[1]});
-                const bf16x8 AQ = __builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]});
+                const int pc = 4 * ks + g;
+                const bf16x8 AK1 = __builtin_bit_cast(bf16x8, kq_piece<DK>(C.kq, tok_n, pc));
+                const bf16x8 AK2 = __builtin_bit_cast(bf16x8, kq_piece<DK>(C.kq, HT + tok_n, pc));
+                const bf16x8 AQ1 = __builtin_bit_cast(bf16x8, kq_piece<DK>(C.kq, CT + n, pc));
+                const bf16x8 AQ2 = __builtin_bit_cast(bf16x8, kq_piece<DK>(C.kq, CT + HT + n, pc));
                 uint32_t h0[2], m0[2], l0[2], h1[2], m1[2], l1[2];
                 split3(acc[2 * ks], h0, m0, l0);
                 split3(acc[2 * ks + 1], h1, m1, l1);
                 const bf16x8 BH = __builtin_bit_cast(bf16x8, u32x4{h0[0], h0[1], h1[0], h1[1]});
                 const bf16x8 BM = __builtin_bit_cast(bf16x8, u32x4{m0[0], m0[1], m1[0], m1[1]});
                 const bf16x8 BL = __builtin_bit_cast(bf16x8, u32x4{l0[0], l0[1], l1[0], l1[1]});
-                PK = mfma_bf16_k32(AK, BH, PK);
-                PQ = mfma_bf16_k32(AQ, BH, PQ);
-                PK = mfma_bf16_k32(AK, BM, PK);
-                PQ = mfma_bf16_k32(AQ, BM, PQ);
-                PK = mfma_bf16_k32(AK, BL, PK);
+                PK1 = mfma_bf16_k32(AK1, BH, PK1);
+                PK2 = mfma_bf16_k32(AK2, BH, PK2);
+                PQ1 = mfma_bf16_k32(AQ1, BH, PQ1);
+                PQ2 = mfma_bf16_k32(AQ2, BH, PQ2);
+                PK1 = mfma_bf16_k32(AK1, BM, PK1);
+                PK2 = mfma_bf16_k32(AK2, BM, PK2);
+                PQ1 = mfma_bf16_k32(AQ1, BM, PQ1);
+                PQ2 = mfma_bf16_k32(AQ2, BM, PQ2);
+                PK1 = mfma_bf16_k32(AK1, BL, PK1);
+                PK2 = mfma_bf16_k32(AK2, BL, PK2);
             }
-            // X for tokens 4 r + g (the P_K rows this lane holds)
-            float X[4];
+            // X for tokens 4 r + g and 16 + 4 r + g (the P_K rows this lane holds)
+            float X1[4], X2[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) X[r] = fmaf(-C.gam[4 * r + g], PK[r], bf2f((uint16_t)vcur[r]));
-            // W (rows = tokens) and Lq T X on float32 MFMA; step st takes token 4 st + g
-            f32x4 W = {0.f, 0.f, 0.f, 0.f}, O = {0.f, 0.f, 0.f, 0.f};
-            const float gct = C.gamC[n];
+            for (int r = 0; r < 4; ++r) {
+                X1[r] = fmaf(-C.gam[4 * r + g], PK1[r], bf2f(vcur[r]));
+                X2[r] = fmaf(-C.gam[HT + 4 * r + g], PK2[r], bf2f(vcur[4 + r]));
+            }
+            // W = diag(G') T X and Lq T X on float32 MFMA (rows = tokens;
+            // step st takes token 4 st + g of each half)
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            f32x4 W1 = zero, W2 = zero, O1 = zero, O2 = zero;
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 const int s = 4 * st + g;
-                W = mfma_f32_k4(gct * C.Tt[s][n], X[st], W);
-                O = mfma_f32_k4(C.LqT[n][s], X[st], O);
+                W1 = mfma_f32_k4(C.TGt[0][s][n], X1[st], W1);
+                W2 = mfma_f32_k4(C.TGt[1][s][n], X1[st], W2);
+                O1 = mfma_f32_k4(C.LqTt[0][s][n], X1[st], O1);
+                O2 = mfma_f32_k4(C.LqTt[1][s][n], X1[st], O2);
+            }
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const int s = 4 * st + g;
+                W2 = mfma_f32_k4(C.TGt[2][s][n], X2[st], W2);
+                O2 = mfma_f32_k4(C.LqTt[2][s][n], X2[st], O2);
             }
             // O += diag(gamma) Q M0: rows 4 g + r of O and P_Q are the same tokens
+            const f32x4 gq1 = *(const f32x4 *)&C.gam[4 * g];
+            const f32x4 gq2 = *(const f32x4 *)&C.gam[HT + 4 * g];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) L.o[c & 1][4 * g + r][j] = fmaf(C.gam[4 * g + r], PQ[r], O[r]);
+            for (int r = 0; r < 4; ++r) {
+                L.o[c & 1][4 * g + r][j] = fmaf(gq1[r], PQ1[r], O1[r]);
+                L.o[c & 1][HT + 4 * g + r][j] = fmaf(gq2[r], PQ2[r], O2[r]);
+            }
 
-            // M <- gamma_C M + K^T W, W in three bf16 parts: hi and mid of
-            // tokens 4 g + e in one 32-deep product, lo (and zeros) in a
-            // second one of the same shape.  Both products accumulate into
-            // the same registers back to back; a 16-deep product there
-            // instead lost the 32-deep one's result on some row tiles (the
-            // compiler inserts no wait between the two shapes).
+            // M <- gamma_C M + K^T W, W in three bf16 parts: the lane's k-slots
+            // are tokens 4 g .. 4 g + 3 (first half) and 16 + 4 g .. 16 + 4 g + 3
+            // (second half), one 32-deep product per part; MFMA row m of row
+            // tile rt is state row chunk_row(rt, m)
             const float gC = C.gam[CT - 1];
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) acc[rt] *= gC;
-            uint32_t wh[2], wm[2], wl[2];
-            split3(W, wh, wm, wl);
-            const bf16x8 BHM = __builtin_bit_cast(bf16x8, u32x4{wh[0], wh[1], wm[0], wm[1]});
-            const bf16x8 BL0 = __builtin_bit_cast(bf16x8, u32x4{wl[0], wl[1], 0u, 0u});
+            uint32_t h1[2], m1[2], l1[2], h2[2], m2[2], l2[2];
+            split3(W1, h1, m1, l1);
+            split3(W2, h2, m2, l2);
+            const bf16x8 BH = __builtin_bit_cast(bf16x8, u32x4{h1[0], h1[1], h2[0], h2[1]});
+            const bf16x8 BM = __builtin_bit_cast(bf16x8, u32x4{m1[0], m1[1], m2[0], m2[1]});
+            const bf16x8 BL = __builtin_bit_cast(bf16x8, u32x4{l1[0], l1[1], l2[0], l2[1]});
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) {
-                // k of tokens 4 g .. 4 g + 3 at row 16 rt + n, twice
-                const bf16x8 A2 = __builtin_bit_cast(bf16x8, *(const u32x4 *)&C.kt[16 * rt + n][8 * (g ^ (n >> 2))]);
-                acc[rt] = mfma_bf16_k32(A2, BHM, acc[rt]);
-                acc[rt] = mfma_bf16_k32(A2, BL0, acc[rt]);
+                const int R = chunk_row(rt, n);
+                const bf16x8 A2 = __builtin_bit_cast(bf16x8, *(const u32x4 *)&KT[R][8 * (g ^ ((R >> 3) & 3))]);
+                acc[rt] = mfma_bf16_k32(A2, BH, acc[rt]);
+                acc[rt] = mfma_bf16_k32(A2, BM, acc[rt]);
+                acc[rt] = mfma_bf16_k32(A2, BL, acc[rt]);
             }
         }
         lds_barrier();  // chunk c+1 staged, chunk c's outputs complete
-        flush(c);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vcur[r] = vnext[r];
+        flush(c, ln);
+    };
+    for (int c = 0; c < n_chunks; c += 2) {
+        step(c, va, vb);
+        if (c + 1 < n_chunks) step(c + 1, vb, va);
     }
 
     // ---- encode each column block once: absmax, scale, codes ----
+    to_pool_layout<NKS>(acc, lane);
     {
         float am = 0.f;
 #pragma unroll
@@ -408,8 +675,8 @@ __global__ void __launch_bounds__(64 * (DK / 16 + NPROD)) prefill_mfma_kernel(Pr
 }  // namespace
 
 bool prefill_mfma_supported(int dk, int dv, int in_bf16, long long rows_per_token) {
-    // per-lane token offsets inside a chunk (16 tokens x rows x d x 2 bytes)
-    // and the output offsets are kept in 32 bits
+    // per-lane token offsets inside a chunk (32 tokens x rows x d x 4 bytes
+    // for the outputs) are kept in 32 bits
     return in_bf16 && dk == dv && (dk == 128 || dk == 64) &&
            (long long)CT * rows_per_token * dk * 4 < (1ll << 31);
 }

@@ -49,12 +49,15 @@ def _run(w, seed, n_tok, warm, sample=None, outputs=True):
 
 
 @pytest.mark.parametrize("name,kw,n_tok,warm", [
-    ("pf-mixed", dict(B=2, H=3, n_int8=1, n_outliers=8), 100, False),   # 6 chunks + 4 tokens
+    ("pf-mixed", dict(B=2, H=3, n_int8=1, n_outliers=8), 100, False),   # 3 chunks of 32 + 4 tokens
     ("pf-warm", dict(B=3, H=5, n_int8=2, n_outliers=8), 37, True),      # from a warm stored state
     ("pf-d64", dict(B=4, H=4, dk=64, dv=64, n_int8=1), 50, False),
     ("pf-one", dict(B=2, H=2, n_int8=1), 1, True),
-    ("pf-16", dict(B=2, H=3, n_int8=1), 16, False),                      # one whole chunk
-    ("pf-two", dict(B=3, H=2, n_int8=1), 20, True),                      # two chunks: one per producer
+    ("pf-16", dict(B=2, H=3, n_int8=1), 16, False),                      # one half chunk
+    ("pf-32", dict(B=2, H=3, n_int8=1), 32, True),                       # one whole chunk
+    ("pf-two", dict(B=3, H=2, n_int8=1), 40, True),                      # two chunks: one per producer
+    ("pf-three", dict(B=2, H=3, n_int8=1), 65, False),                   # odd chunk count, 1-token tail
+    ("pf-five-d64", dict(B=2, H=3, dk=64, dv=64, n_int8=1), 150, True),  # 5 chunks, 22-token tail
     ("pf-f32", dict(B=2, H=3, n_int8=1, dtype=inputs.DT_F32), 40, False),  # per-column kernel
 ])
 def test_prefill_encode(name, kw, n_tok, warm):
