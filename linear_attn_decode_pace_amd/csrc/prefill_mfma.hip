@@ -27,7 +27,8 @@
 //   P_K = K M0 with M0 split exactly into three bf16 parts (hi + mid + lo), so
 //   the state update keeps float32 accuracy; P_Q = Q M0 over hi + mid (it
 //   only reaches the outputs, and two parts leave ~1e-5 relative error);
-//   X = V - diag(g) P_K; W = diag(G') T X and Lq T X on float32 MFMA;
+//   X = V - diag(g) P_K; W = diag(G') T X on float32 MFMA; Lq T X on bf16
+//   MFMA over two parts of each factor (outputs only: ~1e-5 relative error);
 //   O = Lq T X + diag(g) P_Q; M <- g_C M + K^T W (bf16 MFMA, W in three
 //   parts, each a 32-deep product over the chunk's tokens).
 // While a chunk is applied, lane group g of a consumer holds state rows
@@ -93,7 +94,12 @@ template <int DK>
 struct alignas(16) ChunkLds {
     uint16_t kq[2 * CT][DK];  // rows 0..31: k_t, rows 32..63: q_t (bf16, pieces swizzled)
     float TGt[3][HT][HT];     // TGt[b][s][t] = G'_t T_b[t][s]   (diag(G') T, transposed)
-    float LqTt[3][HT][HT];    // LqTt[b][s][t] = (Lq T)_b[t][s]
+    // Lq T in two bf16 parts (hi, mid), as MFMA A operands whose k-slot
+    // 4 g + e (16 slots) / 8 g + e (32 slots) is token 4 e + g of the chunk:
+    // LqB1[p][t][.] the (H1, H1) block for the first half's outputs,
+    // LqB2[p][t][.] the (H2, H1) and (H2, H2) blocks for the second half's
+    uint16_t LqB1[2][HT][HT];
+    uint16_t LqB2[2][HT][2 * HT];
     float gam[CT];            // gamma_t = alpha_0 ... alpha_t
     float ab[2 * CT];         // alpha_t, then beta_t (padding tokens: 1, 0)
 };
@@ -202,9 +208,39 @@ __device__ inline f32x4 mm16t(const float (*X)[XS], const float (*Y)[YS], f32x4 
     return D;
 }
 
+// x from the lane CTRL names inside the lane's row of 16 (a DPP row shift),
+// 1 where that lane lies outside the row
+template <int CTRL>
+__device__ inline float row_shift_or_one(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// A = strictly lower (Gamma * kk), Lq = lower (Gamma * qk) of one diagonal
+// block in place: lane -> row t = lane / 4, columns s0 .. s0 + 3 with
+// s0 = 4 (lane % 4); Gamma_{t, s0+3} as one masked product, then the running
+// product down to s0
+__device__ inline void diag_gates(const float *alpha, float (*kk)[KS], float (*qk)[KS], int lane) {
+    float al[HT];
+#pragma unroll
+    for (int r = 0; r < HT; ++r) al[r] = alpha[r];
+    const int t = lane >> 2, s0 = 4 * (lane & 3);
+    float gts = 1.f;
+#pragma unroll
+    for (int r = 1; r < HT; ++r) gts *= (r > s0 + 3 && r <= t) ? al[r] : 1.f;
+#pragma unroll
+    for (int e = 3; e >= 0; --e) {
+        const int s = s0 + e;
+        kk[t][s] = s < t ? gts * kk[t][s] : 0.f;
+        qk[t][s] = s <= t ? gts * qk[t][s] : 0.f;
+        if (e > 0 && s <= t) gts *= alpha[s];  // Gamma_{t,s-1} = Gamma_{t,s} alpha_s
+    }
+}
+
 // Producer, phase A: Gram blocks and gates of a loaded chunk.
 //   Gamma_{t,s} = prod_{s<r<=t} alpha_r; inside a half from its own gates,
-//   across the halves Gamma_{16+t, s} = gch[0][s] gh[1][t].
+//   across the halves Gamma_{16+t, s} = gch[0][s] gh[1][t].  The per-half
+//   prefix products gh and the products over the rest of the half gch come
+//   from DPP scans (lane l: token l % 32, one half per row of 16 lanes).
 template <int DK>
 __device__ __attribute__((always_inline)) inline void prep_a(ChunkLds<DK> &L, PrepScratch &S, int lane) {
     launder(lane);
@@ -212,9 +248,31 @@ __device__ __attribute__((always_inline)) inline void prep_a(ChunkLds<DK> &L, Pr
     gram_block<DK>(L.kq, 0, 0, S.kk[0], S.qk[0], lane);
     gram_block<DK>(L.kq, HT, 0, S.kk[1], S.qk[1], lane);
     gram_block<DK>(L.kq, HT, HT, S.kk[2], S.qk[2], lane);
+    {
+        const float al = L.ab[lane & (CT - 1)];
+        float pre = al, suf = al;
+        pre *= row_shift_or_one<0x111>(pre);  // row_shr:1
+        pre *= row_shift_or_one<0x112>(pre);
+        pre *= row_shift_or_one<0x114>(pre);
+        pre *= row_shift_or_one<0x118>(pre);
+        suf *= row_shift_or_one<0x101>(suf);  // row_shl:1
+        suf *= row_shift_or_one<0x102>(suf);
+        suf *= row_shift_or_one<0x104>(suf);
+        suf *= row_shift_or_one<0x108>(suf);
+        const float after = row_shift_or_one<0x101>(suf);  // product over (t, half end]
+        const float tot1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pre), HT - 1));
+        const float tot2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pre), CT - 1));
+        if (lane < CT) {
+            const int hb = lane >> 4, t = lane & 15;
+            S.gh[hb][t] = pre;
+            S.gch[hb][t] = after;
+            L.gam[lane] = hb ? tot1 * pre : pre;
+            S.gcp[lane] = hb ? after : after * tot2;
+        }
+    }
     wave_sync();
-    chunk16_gates<KS>(L.ab, S.kk[0], S.qk[0], S.kk[0], S.qk[0], S.gh[0], S.gch[0], lane);
-    chunk16_gates<KS>(L.ab + HT, S.kk[2], S.qk[2], S.kk[2], S.qk[2], S.gh[1], S.gch[1], lane);
+    diag_gates(L.ab, S.kk[0], S.qk[0], lane);
+    diag_gates(L.ab + HT, S.kk[2], S.qk[2], lane);
     {
         const int t = lane >> 2, s0 = 4 * (lane & 3);
         const float gt = S.gh[1][t];
@@ -225,11 +283,34 @@ __device__ __attribute__((always_inline)) inline void prep_a(ChunkLds<DK> &L, Pr
             S.qk[1][t][s0 + e] *= f;
         }
     }
-    if (lane < CT) {
-        L.gam[lane] = lane < HT ? S.gh[0][lane] : S.gh[0][HT - 1] * S.gh[1][lane - HT];
-        S.gcp[lane] = lane < HT ? S.gch[0][lane] * S.gh[1][HT - 1] : S.gch[1][lane - HT];
-    }
     wave_sync();
+}
+
+// x - (low / high bf16 of pk) in one instruction: a bf16 dot product with
+// (-1, -0) / (0, -1) accumulated onto x (exact: the difference is a float32).
+// The low-half factor is (-1, -0), not (-1, 0): the compiler encodes the
+// packed (-1, 0) as the inline constant -1.0, which the dot product applies
+// to the high half.
+__device__ inline float sub_lo(uint32_t pk, float x) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
+                                           __builtin_bit_cast(bf16x2, 0x8000bf80u), x, false);
+}
+__device__ inline float sub_hi(uint32_t pk, float x) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
+                                           __builtin_bit_cast(bf16x2, 0xbf800000u), x, false);
+}
+
+// bf16 parts (hi, mid, lo) of the four floats x[0..3], as two packed dwords
+// each: x = hi + mid + lo exactly (8 + 8 + 8 significant bits)
+__device__ inline void split3(const f32x4 &x, uint32_t hi[2], uint32_t md[2], uint32_t lo[2]) {
+    hi[0] = pk_bf16(x[0], x[1]);
+    hi[1] = pk_bf16(x[2], x[3]);
+    const float r0 = sub_lo(hi[0], x[0]), r1 = sub_hi(hi[0], x[1]);
+    const float r2 = sub_lo(hi[1], x[2]), r3 = sub_hi(hi[1], x[3]);
+    md[0] = pk_bf16(r0, r1);
+    md[1] = pk_bf16(r2, r3);
+    lo[0] = pk_bf16(sub_lo(md[0], r0), sub_hi(md[0], r1));
+    lo[1] = pk_bf16(sub_lo(md[1], r2), sub_hi(md[1], r3));
 }
 
 // Producer, part 4 (phase B): T = (I + diag(beta) A)^-1 diag(beta) block by
@@ -285,44 +366,25 @@ __device__ __attribute__((always_inline)) inline void prep_b(ChunkLds<DK> &L, Pr
         L.TGt[1][n][4 * g + r] = S.gcp[HT + 4 * g + r] * x;
     }
     wave_sync();
-    // (Lq T)^T block by block, written row by row
+    // Lq T block by block: this lane holds (Lq T)[t = n][s = 4 g + r] of the
+    // block (computed transposed), stored as hi and mid bf16 parts at the
+    // k-slot of token s
+    auto put = [&](uint16_t *hi_row, uint16_t *mid_row, int slot0, int slot_r, const f32x4 &x) {
+        uint32_t h[2], m[2], l[2];
+        split3(x, h, m, l);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            hi_row[slot0 + slot_r * r] = (uint16_t)(h[r >> 1] >> (16 * (r & 1)));
+            mid_row[slot0 + slot_r * r] = (uint16_t)(m[r >> 1] >> (16 * (r & 1)));
+        }
+    };
     D = mm16t(S.qk[0], S.T[0], zero, lane);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) L.LqTt[0][4 * g + r][n] = D[r];
+    put(L.LqB1[0][n], L.LqB1[1][n], g, 4, D);          // s = 4 g + r -> slot 4 r + g
     D = mm16t(S.qk[2], S.T[2], zero, lane);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) L.LqTt[2][4 * g + r][n] = D[r];
+    put(L.LqB2[0][n], L.LqB2[1][n], 4 + g, 8, D);      // s = 16 + 4 g + r -> slot 8 r + 4 + g
     D = mm16t(S.qk[2], S.T[1], mm16t(S.qk[1], S.T[0], zero, lane), lane);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) L.LqTt[1][4 * g + r][n] = D[r];
+    put(L.LqB2[0][n], L.LqB2[1][n], g, 8, D);          // s = 4 g + r -> slot 8 r + g
     wave_sync();
-}
-
-// x - (low / high bf16 of pk) in one instruction: a bf16 dot product with
-// (-1, -0) / (0, -1) accumulated onto x (exact: the difference is a float32).
-// The low-half factor is (-1, -0), not (-1, 0): the compiler encodes the
-// packed (-1, 0) as the inline constant -1.0, which the dot product applies
-// to the high half.
-__device__ inline float sub_lo(uint32_t pk, float x) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
-                                           __builtin_bit_cast(bf16x2, 0x8000bf80u), x, false);
-}
-__device__ inline float sub_hi(uint32_t pk, float x) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
-                                           __builtin_bit_cast(bf16x2, 0xbf800000u), x, false);
-}
-
-// bf16 parts (hi, mid, lo) of the four floats x[0..3], as two packed dwords
-// each: x = hi + mid + lo exactly (8 + 8 + 8 significant bits)
-__device__ inline void split3(const f32x4 &x, uint32_t hi[2], uint32_t md[2], uint32_t lo[2]) {
-    hi[0] = pk_bf16(x[0], x[1]);
-    hi[1] = pk_bf16(x[2], x[3]);
-    const float r0 = sub_lo(hi[0], x[0]), r1 = sub_hi(hi[0], x[1]);
-    const float r2 = sub_lo(hi[1], x[2]), r3 = sub_hi(hi[1], x[3]);
-    md[0] = pk_bf16(r0, r1);
-    md[1] = pk_bf16(r2, r3);
-    lo[0] = pk_bf16(sub_lo(md[0], r0), sub_hi(md[0], r1));
-    lo[1] = pk_bf16(sub_lo(md[1], r2), sub_hi(md[1], r3));
 }
 
 // Chunk layout <-> pool layout of a column block's state (lane (g, n); four
@@ -565,24 +627,42 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
                 X1[r] = fmaf(-C.gam[4 * r + g], PK1[r], bf2f(vcur[r]));
                 X2[r] = fmaf(-C.gam[HT + 4 * r + g], PK2[r], bf2f(vcur[4 + r]));
             }
-            // W = diag(G') T X and Lq T X on float32 MFMA (rows = tokens;
-            // step st takes token 4 st + g of each half)
+            // W = diag(G') T X on float32 MFMA (rows = tokens; step st takes
+            // token 4 st + g of each half): the state needs its accuracy
             const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-            f32x4 W1 = zero, W2 = zero, O1 = zero, O2 = zero;
+            f32x4 W1 = zero, W2 = zero;
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 const int s = 4 * st + g;
                 W1 = mfma_f32_k4(C.TGt[0][s][n], X1[st], W1);
                 W2 = mfma_f32_k4(C.TGt[1][s][n], X1[st], W2);
-                O1 = mfma_f32_k4(C.LqTt[0][s][n], X1[st], O1);
-                O2 = mfma_f32_k4(C.LqTt[1][s][n], X1[st], O2);
             }
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const int s = 4 * st + g;
-                W2 = mfma_f32_k4(C.TGt[2][s][n], X2[st], W2);
-                O2 = mfma_f32_k4(C.LqTt[2][s][n], X2[st], O2);
+            for (int st = 0; st < 4; ++st) W2 = mfma_f32_k4(C.TGt[2][4 * st + g][n], X2[st], W2);
+            // Lq T X on bf16 MFMA with X and Lq T in two parts each (hi hi,
+            // hi mid, mid hi: ~1e-5 relative error, outputs only); the
+            // lane's k-slots are its own tokens 4 e + g
+            uint32_t xh[4], xm[4];
+            {
+                const f32x4 x1 = {X1[0], X1[1], X1[2], X1[3]}, x2 = {X2[0], X2[1], X2[2], X2[3]};
+                uint32_t l_[2];
+                split3(x1, xh, xm, l_);
+                split3(x2, xh + 2, xm + 2, l_);
             }
+            const s16x4 B1h = __builtin_bit_cast(s16x4, u32x2{xh[0], xh[1]});
+            const s16x4 B1m = __builtin_bit_cast(s16x4, u32x2{xm[0], xm[1]});
+            const bf16x8 B2h = __builtin_bit_cast(bf16x8, u32x4{xh[0], xh[1], xh[2], xh[3]});
+            const bf16x8 B2m = __builtin_bit_cast(bf16x8, u32x4{xm[0], xm[1], xm[2], xm[3]});
+            const s16x4 A1h = __builtin_bit_cast(s16x4, *(const u32x2 *)&C.LqB1[0][n][4 * g]);
+            const s16x4 A1m = __builtin_bit_cast(s16x4, *(const u32x2 *)&C.LqB1[1][n][4 * g]);
+            const bf16x8 A2h = __builtin_bit_cast(bf16x8, *(const u32x4 *)&C.LqB2[0][n][8 * g]);
+            const bf16x8 A2m = __builtin_bit_cast(bf16x8, *(const u32x4 *)&C.LqB2[1][n][8 * g]);
+            f32x4 O1 = mfma_bf16_k16(A1h, B1h, zero);
+            f32x4 O2 = mfma_bf16_k32(A2h, B2h, zero);
+            O1 = mfma_bf16_k16(A1h, B1m, O1);
+            O2 = mfma_bf16_k32(A2h, B2m, O2);
+            O1 = mfma_bf16_k16(A1m, B1h, O1);
+            O2 = mfma_bf16_k32(A2m, B2h, O2);
             // O += diag(gamma) Q M0: rows 4 g + r of O and P_Q are the same tokens
             const f32x4 gq1 = *(const f32x4 *)&C.gam[4 * g];
             const f32x4 gq2 = *(const f32x4 *)&C.gam[HT + 4 * g];
