@@ -528,7 +528,10 @@ __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int
 template <int DK, bool ERR, bool STEP>
 __global__ void __launch_bounds__(256) decode_mfma_kernel(MfmaArgs a) {
     constexpr int WPT = Split<DK>::WPT;
-    constexpr int TPB = WPT == 1 ? 4 : 1;  // tiles per workgroup
+    // tiles per workgroup: four for whole periods; one per step, where tiles
+    // that end their period (and write codes) run beside tiles that only
+    // read, and a workgroup holds its slot until its slowest wave is done
+    constexpr int TPB = WPT == 1 && !STEP ? 4 : 1;
     __shared__ TileLds tl[TPB];
     __shared__ WaveOut wo[TPB * WPT];
     const int lane = threadIdx.x & 63;
@@ -583,16 +586,16 @@ template <bool STEP>
 hipError_t launch(MfmaArgs &a, hipStream_t s) {
     const PoolView &p = a.p;
     const bool err = p.colerr != nullptr;
-    set_xcd_order(a, (p.dk == 128 ? Split<128>::WPT : Split<64>::WPT) == 1 ? 4 : 1);
+    set_xcd_order(a, (p.dk == 128 ? Split<128>::WPT : Split<64>::WPT) == 1 && !STEP ? 4 : 1);
     if (p.dk == 128) {
-        constexpr int WPT = Split<128>::WPT, TPB = WPT == 1 ? 4 : 1;
+        constexpr int WPT = Split<128>::WPT, TPB = WPT == 1 && !STEP ? 4 : 1;
         const dim3 grid((a.tiles + TPB - 1) / TPB), block(64 * WPT * TPB);
         if (err)
             hipLaunchKernelGGL((decode_mfma_kernel<128, true, STEP>), grid, block, 0, s, a);
         else
             hipLaunchKernelGGL((decode_mfma_kernel<128, false, STEP>), grid, block, 0, s, a);
     } else {
-        constexpr int WPT = Split<64>::WPT, TPB = WPT == 1 ? 4 : 1;
+        constexpr int WPT = Split<64>::WPT, TPB = WPT == 1 && !STEP ? 4 : 1;
         const dim3 grid((a.tiles + TPB - 1) / TPB), block(64 * WPT * TPB);
         if (err)
             hipLaunchKernelGGL((decode_mfma_kernel<64, true, STEP>), grid, block, 0, s, a);
