@@ -13,7 +13,7 @@ from tests.gpu_cases import say, tok_tiles
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, seed, n_tok, warm, sample=None, outputs=True):
+def _run(w, seed, n_tok, warm, sample=None, outputs=True, tok_hook=None):
     import torch
     from linear_attn_decode_pace_amd import pace, runtime
     n = w.B * w.H
@@ -33,6 +33,8 @@ def _run(w, seed, n_tok, warm, sample=None, outputs=True):
 
     c0, s0 = read()
     tok = inputs.tokens(w, seed, inputs.SEG_PROMPT, 0, n_tok)
+    if tok_hook is not None:
+        tok = tok_hook(tok)
     out = runtime.out_buffer(w, n_tok) if outputs else None
     st.prefill(runtime.DeviceTokens(tok), out)
     c1, s1 = read()
@@ -63,6 +65,22 @@ def _run(w, seed, n_tok, warm, sample=None, outputs=True):
 def test_prefill_encode(name, kw, n_tok, warm):
     w = inputs.ragged(name, 240, prompt=n_tok, warmup=0 if not warm else 32, **kw)
     _run(w, 0, n_tok, warm)
+
+
+@pytest.mark.parametrize("value", [1e-5, 0.0])
+def test_prefill_vanishing_decay(value):
+    # every token of the even sequences decays by `value`: inside a chunk the
+    # gate products underflow (1e-5) or are zero, so each chunk's state is
+    # built from its own last tokens only
+    import dataclasses
+    w = inputs.ragged("pf-vanish", 242, B=4, H=3, n_int8=1, prompt=70, warmup=32)
+
+    def hook(tok):
+        a = tok.alpha.copy()
+        a[:, 0::2] = np.float32(value)
+        return dataclasses.replace(tok, alpha=a)
+
+    _run(w, 0, 70, True, tok_hook=hook)
 
 
 def test_prefill_encode_4096_tokens_sampled():
