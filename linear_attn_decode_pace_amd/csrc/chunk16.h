@@ -1,7 +1,6 @@
-// Token-only matrices of a 16-token chunk, shared by the 16-token decode
-// kernel (decode_mfma16.hip) and the prefill (prefill_mfma.hip).  One
-// wavefront computes them from the chunk's k_t, q_t (bf16 rows in LDS, row
-// stride ROW elements) and alpha_t, beta_t:
+// Token-only matrices of a 16-token chunk for the 16-token decode kernel
+// (decode_mfma16.hip).  One wavefront computes them from the chunk's k_t,
+// q_t (bf16 rows in LDS, row stride ROW elements) and alpha_t, beta_t:
 //   kk[t][s] = k_t . k_s,  qk[t][s] = q_t . k_s                (Gram on MFMA)
 //   Gamma_ts = prod_{s<r<=t} alpha_r, gam[t] = Gamma_t,-1, gamC[t] = Gamma_15,t
 //   A = strictly lower (Gamma * kk),  Lq = lower incl. diagonal (Gamma * qk)

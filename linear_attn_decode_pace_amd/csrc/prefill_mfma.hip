@@ -36,7 +36,7 @@
 // are eight adjacent key columns (one 16-byte LDS read); the stored pool
 // layout is restored for the final encode.  Outputs of a chunk go through
 // double-buffered LDS and leave as whole rows.
-#include "chunk16.h"
+#include "mfma_common.h"
 #include "pace_prefill.h"
 
 namespace pace {
