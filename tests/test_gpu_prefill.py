@@ -93,6 +93,57 @@ def test_prefill_encode_4096_tokens_sampled():
     _run(w, 0, 4096, False, sample=np.array(pick))
 
 
+def test_prefill_full_batch_sampled():
+    # the prompt workload at its full size, in the launch bench.py times (512
+    # sequences x 32 heads, one 4096-token prompt, fused encode): the prompt
+    # is 64 distinct generated tokens repeated to 4096 on the device (bench.py
+    # repeats 256), checked on sampled tiles of both widths
+    import torch
+    from linear_attn_decode_pace_amd import pace, runtime
+    w = inputs.PREFILL
+    T, D = 4096, 64
+    n = w.B * w.H
+    bits = inputs.head_bits(w, 0)
+    say("[case] prefill-b512 full batch: generating 64 prompt tokens")
+    tok = inputs.tokens(w, 0, inputs.SEG_PROMPT, 0, D)
+    small = runtime.DeviceTokens(tok)
+    big = runtime.DeviceTokens.__new__(runtime.DeviceTokens)
+    for name in ("q", "k", "v", "alpha", "beta"):
+        x = getattr(small, name)
+        y = torch.empty((T,) + tuple(x.shape[1:]), dtype=x.dtype, device="cuda")
+        for t0 in range(0, T, D):
+            y[t0:t0 + D].copy_(x)
+        setattr(big, name, y)
+    big.T = T
+    del small
+    h8 = [int(h) for h in np.nonzero(bits == 8)[0][:2]]
+    h4 = [int(h) for h in np.nonzero(bits == 4)[0][[0, -1]]]
+    pairs = [(b, h) for b in (0, 255, 511) for h in h8 + h4]
+    idx = np.array([b * w.H + h for b, h in pairs])
+    tix = torch.as_tensor(idx, device="cuda")
+    st = runtime.State(w, bits, pace.PACE_INIT_ZERO)
+    out = runtime.out_buffer(w, T)
+    st.prefill(big, out)
+    torch.cuda.synchronize()
+    c, s = st.read_codes()
+    c1 = c.reshape(n, w.dk, w.dv)[tix].cpu().numpy()
+    s1 = s.reshape(n, w.dv)[tix].cpu().numpy()
+    o = out.reshape(T, n, w.dv)[:, tix].cpu().numpy()
+    st.free()
+    del big, out
+    sel = tok.select([b for b, _ in pairs], [h for _, h in pairs])
+    q, k, v, al, be = [np.tile(sel.f64(nm)[:, :, 0], (T // D,) + (1,) * (sel.f64(nm).ndim - 2))
+                       for nm in ("q", "k", "v", "alpha", "beta")]
+    bits_t = np.array([bits[h] for _, h in pairs], dtype=np.int64)
+    zc = np.zeros((len(pairs), w.dk, w.dv), dtype=np.int64)
+    zs = np.zeros((len(pairs), w.dv), dtype=np.float32)
+    O, rc, rs, Mpre = opace.period(zc, zs, bits_t, q, k, v, al, be)
+    what = f"prefill-b512 full batch, {T} tokens, {len(pairs)} sampled tiles"
+    rep = parity.check_encoded(c1, s1, rc, rs, Mpre, what)
+    m = parity.check_outputs(o, O, what)
+    say(f"[case] {what}: output rel err {m}, flips {rep.flips}")
+
+
 def test_prefill_encode_matches_float_prefill_then_encode():
     # the same prompt through pace_prefill_f32 + PACE_INIT_F32: both keep the
     # state in float32, so the stored states agree up to rounding ties
