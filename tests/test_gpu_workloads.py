@@ -52,6 +52,16 @@ def test_sweep_b256_whole_run_sampled(period):
              label=f"sweep-b256-k{period}")
 
 
+def test_prompt_decode_full_batch_sampled():
+    # the prompt workload's decode at its full size, in the launch the
+    # benchmark times (512 sequences x 32 heads, 8 at 8 bits, period 16: the
+    # 16-token chunk kernel), from a 32-token warm state; two periods checked
+    # on 32+ sampled tiles
+    w = inputs.PREFILL.replace(warmup=32)
+    run_case(w, 0, default_calls(w, 2), sample=_sample(w, 0, 32), workers=WORKERS,
+             label="prefill-b512-decode")
+
+
 def test_prompt_handoff_reduced_batch():
     # 4096-token prompts through the library's float32 prefill into the
     # quantized state, then decode at period 16 with 8 of 32 heads at 8 bits;
