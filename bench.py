@@ -75,6 +75,26 @@ def algorithmic_bytes_step(w: inputs.Workload, head_bits, k_eff=None) -> float:
     return w.B * per_period / k
 
 
+def step_bytes_exact(w: inputs.Workload, head_bits, fill_before, closed) -> float:
+    """Bytes of one per-step decode call from the states' buffer fills before
+    the call and whether the call closed their period: every state reads its
+    codes and scales, its buffered tokens and the call's q/k/v/alpha/beta and
+    writes its float32 outputs; a state that closes its period writes its
+    codes and scales, the others append the token to the buffer.  fill_before
+    and closed are [B, H] tensors."""
+    import torch
+    e_in = 2 if w.dtype == inputs.DT_BF16 else 4
+    state_h = torch.tensor([w.dk * w.dv * int(b) // 8 + 4 * w.dv for b in head_bits],
+                           dtype=torch.float64, device=fill_before.device)
+    buf_tok = (w.dk + w.dv) * e_in + 8
+    io_tok = (w.dk * 2 + w.dv) * e_in + 8 + 4 * w.dv
+    closed = closed.to(torch.float64)
+    total = (w.B * state_h.sum() + fill_before.to(torch.float64).sum() * buf_tok
+             + w.B * w.H * io_tok + (closed * state_h[None, :]).sum()
+             + (1.0 - closed).sum() * buf_tok)
+    return float(total.item())
+
+
 def kernel_sha() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -343,18 +363,28 @@ def main() -> int:
     log(f"timed {K} steps: {total_ms:.3f} ms on the device, {t_wall * 1e3:.1f} ms wall")
 
     k_eff = None
+    adapt_bytes = None
     if adaptive:
-        # realised mean period: replay the timed steps untimed, counting the
-        # states each step re-encodes (fill back to 0)
-        closes = 0
+        # realised mean period and exact bytes per call: replay as many steps
+        # untimed, reading every state's buffer fill before and after each
+        # call (a fill back to 0 closed the period)
+        closes, total = 0, 0.0
+        fill, _ = st.read_step()
         for i in range(K):
             call(ring[(args.warmup + K + i) % ring_n], out)
-            fill, _ = st.read_step()
-            closes += int((fill == 0).sum().item())
+            after, _ = st.read_step()
+            closed = after == 0
+            closes += int(closed.sum().item())
+            total += step_bytes_exact(w, head_bits, fill, closed)
+            fill = after
         k_eff = K * w.B * w.H / max(1, closes)
-        log(f"adaptive period: mean period {k_eff:.2f} tokens over {K} steps")
+        adapt_bytes = total / K
+        log(f"adaptive period: mean period {k_eff:.2f} tokens over {K} steps, "
+            f"{adapt_bytes / 1e6:.1f} MB per call")
     if window_mode:
         nbytes = window_bytes(w, head_bits, args.fp8_window)
+    elif adaptive:
+        nbytes = adapt_bytes
     elif step_mode:
         nbytes = algorithmic_bytes_step(w, head_bits, k_eff)
     else:
