@@ -23,8 +23,12 @@
 //   * the 8 x 8 chunk matrices applied to X and Y = diag(gamma) Q M0 give W
 //     (the update's right factor) and O: float32 MFMA (16x16x4), whose
 //     operand layout matches what each lane already holds;
-//   * K^T W (d x 8 x 16 per column block): bf16 MFMA with W split exactly into
-//     three bf16 parts (hi + mid + lo) stacked along the reduction dimension.
+//   * K^T W (d x 8 x 16 per column block): bf16 MFMA with W in two bf16
+//     parts (hi + mid: 16 significant bits, relative error below 2^-17)
+//     stacked along the reduction dimension, one 16-deep product per row
+//     tile.  A third part (exact W) cost eight more matrix instructions per
+//     column block and 3-7% of the kernel's time; its 2^-17 is far below
+//     the rounding the re-encode applies.
 // The state is accumulated in units of sigma_j = gamma_C s_j:
 //   acc = M_C / sigma_j = codes + K^T (W / sigma_j),
 // so the accumulator starts from the codes themselves (no per-entry multiply).
@@ -328,7 +332,7 @@ __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int
     TRACE(15, L.kk[lane >> 3][lane & 7]); TRACE(16, L.Lq[lane >> 3][lane & 7]);
 
     // K^T as the A operand of the update: row i = 16 rt + n, k index 4 g + e is
-    // token 4 (g % 2) + e (the same tokens for the hi / mid / lo parts)
+    // token 4 (g % 2) + e (the same tokens for the hi and mid parts)
     s16x4 AU[NRT];
     {
         const int t0 = 4 * (g & 1);
@@ -437,23 +441,17 @@ __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int
             if (!pend) continue;  // mid-period step: the stored state is only read
         }
 
-        // W split into three bf16 parts (hi + mid + lo)
+        // W in two bf16 parts: lanes g < 2 give hi (k-slots 0..7), lanes
+        // g >= 2 the rounded rest (k-slots 8..15), both for tokens 4 (g % 2) + r
         const uint32_t hi01 = pk_bf16(W[0], W[1]), hi23 = pk_bf16(W[2], W[3]);
         const float r0 = W[0] - lo_f32(hi01), r1 = W[1] - hi_f32(hi01);
         const float r2 = W[2] - lo_f32(hi23), r3 = W[3] - hi_f32(hi23);
         const uint32_t md01 = pk_bf16(r0, r1), md23 = pk_bf16(r2, r3);
-        const uint32_t lo01 = pk_bf16(r0 - lo_f32(md01), r1 - hi_f32(md01));
-        const uint32_t lo23 = pk_bf16(r2 - lo_f32(md23), r3 - hi_f32(md23));
         const bool first = g < 2;
-        u32x2 b1 = {first ? hi01 : md01, first ? hi23 : md23};
-        u32x2 b2 = {first ? lo01 : 0u, first ? lo23 : 0u};
+        const u32x2 b1 = {first ? hi01 : md01, first ? hi23 : md23};
         const s16x4 B1 = __builtin_bit_cast(s16x4, b1);
-        const s16x4 B2 = __builtin_bit_cast(s16x4, b2);
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) {
-            acc[rt] = mfma_bf16_k16(AU[rt], B1, acc[rt]);
-            acc[rt] = mfma_bf16_k16(AU[rt], B2, acc[rt]);
-        }
+        for (int rt = 0; rt < NRT; ++rt) acc[rt] = mfma_bf16_k16(AU[rt], B1, acc[rt]);
 
         // ---- re-encode the column ----
         float am = 0.f;

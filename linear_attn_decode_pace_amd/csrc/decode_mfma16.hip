@@ -13,7 +13,7 @@
 // which is exactly the reduction index the float32 16x16x4 MFMA steps take
 // from each lane; the chunk-mixing chain then returns W and O rows 4 g + r,
 // i.e. tokens 4 g + r, which are the reduction indices this lane feeds to the
-// K^T W update (16x16x16 bf16 MFMA, W split into hi + mid + lo): no
+// K^T W update (16x16x16 bf16 MFMA, W in two bf16 parts, hi + mid): no
 // cross-lane exchange is needed at C = 16.
 #include "chunk16.h"
 
@@ -245,21 +245,17 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
             }
         }
 
-        // W (tokens 4 g + r, units of sig) split into three bf16 parts
+        // W (tokens 4 g + r, units of sig) in two bf16 parts (hi + mid)
         const uint32_t hi01 = pk_bf16(W[0], W[1]), hi23 = pk_bf16(W[2], W[3]);
         const float r0 = W[0] - lo_f32(hi01), r1 = W[1] - hi_f32(hi01);
         const float r2 = W[2] - lo_f32(hi23), r3 = W[3] - hi_f32(hi23);
         const uint32_t md01 = pk_bf16(r0, r1), md23 = pk_bf16(r2, r3);
-        const uint32_t lo01 = pk_bf16(r0 - lo_f32(md01), r1 - hi_f32(md01));
-        const uint32_t lo23 = pk_bf16(r2 - lo_f32(md23), r3 - hi_f32(md23));
         const s16x4 BH = __builtin_bit_cast(s16x4, u32x2{hi01, hi23});
         const s16x4 BM = __builtin_bit_cast(s16x4, u32x2{md01, md23});
-        const s16x4 BL = __builtin_bit_cast(s16x4, u32x2{lo01, lo23});
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
             acc[rt] = mfma_bf16_k16(AU[rt], BH, acc[rt]);
             acc[rt] = mfma_bf16_k16(AU[rt], BM, acc[rt]);
-            acc[rt] = mfma_bf16_k16(AU[rt], BL, acc[rt]);
         }
 
         // ---- re-encode the column ----
