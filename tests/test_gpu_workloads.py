@@ -37,6 +37,46 @@ def test_headline_full_batch_sampled():
     run_case(w, 0, default_calls(w, 3), sample=_sample(w, 0, 64), workers=WORKERS)
 
 
+def test_headline_steps_equal_period_calls():
+    # the per-step form (one token per call, tokens buffered on the device)
+    # at the headline's full size, in the launch the benchmark times for it
+    # (one tile per workgroup, 65,536 tiles): a period of steps gives bitwise
+    # the outputs and the stored state of one period call, which the sampled
+    # oracle check above pins; mid-period steps leave the stored state alone
+    import torch
+
+    from linear_attn_decode_pace_amd import pace, runtime
+
+    w = inputs.HEADLINE.replace(warmup=8)
+    seed = 0
+    bits = inputs.head_bits(w, seed)
+    wtok = inputs.concat(inputs.iter_tokens(
+        w, seed, inputs.SEG_WARMUP, [(t, t + 1) for t in range(w.warmup)], WORKERS))
+    M0 = runtime.warmup_state(w, seed, tok=wtok)
+    per = runtime.State(w, bits, pace.PACE_INIT_F32, M0)
+    stp = runtime.State(w, bits, pace.PACE_INIT_F32, M0, flags=pace.PACE_STEP_BUFFER)
+    del M0
+    C = w.period
+    for p in range(2):
+        say(f"[case] headline steps vs period call, period {p}")
+        tok = inputs.concat(inputs.iter_tokens(
+            w, seed, inputs.SEG_DECODE, [(t, t + 1) for t in range(p * C, (p + 1) * C)], WORKERS))
+        dt = runtime.DeviceTokens(tok)
+        out_p = runtime.out_buffer(w, C)
+        per.decode(dt, out_p)
+        raw0 = stp.read_raw()
+        for t in range(C):
+            out_s = runtime.out_buffer(w, 1)
+            stp.step(dt.slice(t, t + 1), out_s)
+            assert torch.equal(out_s[0], out_p[t]), f"period {p} token {t}"
+            if t < C - 1:
+                assert torch.equal(stp.read_raw(), raw0), f"period {p} token {t} wrote"
+        assert torch.equal(stp.read_raw(), per.read_raw()), f"state after period {p}"
+        del raw0, out_p, dt
+    per.free()
+    stp.free()
+
+
 def test_mixed_b1024_whole_run_sampled():
     # 1024 sequences, all 512 decode steps (64 periods), outlier channels
     w = inputs.MIXED
