@@ -115,13 +115,15 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
     }
     wave_sync();
 
-    // ---- A operands: A row m of the K (Q) block is token 4 (m % 4) + m / 4, so
-    //      output row 4 g + r of P is token 4 r + g; k index e of slice ks is
-    //      state row 32 ks + 16 (e / 4) + 4 g + e % 4 ----
+    // ---- A operands: A row m of the K block is token 4 (m % 4) + m / 4, so
+    //      output row 4 g + r of P_K is token 4 r + g (the mixing steps'
+    //      reduction index); the Q block keeps token order, so row 4 g + r of
+    //      P_Q is token 4 g + r, the output row this lane holds; k index e of
+    //      slice ks is state row 32 ks + 16 (e / 4) + 4 g + e % 4 ----
     const int tok_n = 4 * (n & 3) + (n >> 2);
     auto ap_slice = [&](int blk, int ks) {
         const int c0 = 32 * ks + 4 * g, c1 = c0 + 16;
-        const int row = 16 * blk + tok_n;
+        const int row = blk == 0 ? tok_n : 16 + n;
         u32x2 r0 = *(const u32x2 *)&L.kq[row][c0];
         u32x2 r1 = *(const u32x2 *)&L.kq[row][c1];
         u32x4 w = {r0[0], r0[1], r1[0], r1[1]};
@@ -148,7 +150,8 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
     // ---- chunk-mixing operands (float32 16x16x4 MFMA; step st takes token
     //      4 st + g from lane group g):
     //      W chain, row m = token m: A = Gamma_{C-1,m} T[m][4 st + k]
-    //      O chain, row m = token m: A = (Lq T)[m][4 st + k] on X, identity on Y ----
+    //      O chain, row m = token m: A = (Lq T)[m][4 st + k] on X; Y is added
+    //      in place, its rows already in output order ----
     float CW[4], CO[4];
     {
         const float gct = L.gamC[n];
@@ -159,9 +162,12 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
             CO[st] = L.u.m.qkLq[n][s];  // (Lq T)[n][s]
         }
     }
-    float gam_r[4];
+    float gam_r[4], gam_o[4];  // gamma of tokens 4 r + g (X) and 4 g + r (Y)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) gam_r[r] = L.gam[4 * r + g];
+    for (int r = 0; r < 4; ++r) {
+        gam_r[r] = L.gam[4 * r + g];
+        gam_o[r] = L.gam[4 * g + r];
+    }
     const float gamC = L.gam[C16 - 1];
 
     // K^T as the update's A operand: row i = 16 rt + n, k index 4 g + e is token 4 g + e
@@ -192,7 +198,7 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
             sring[slot] = scl[j + 16 * PF];
         }
 
-        // P_K[r] = KAPPA k_{4r+g} . c_j,  P_Q[r] = KAPPA q_{4r+g} . c_j
+        // P_K[r] = KAPPA k_{4r+g} . c_j,  P_Q[r] = KAPPA q_{4g+r} . c_j
         f32x4 PK = {0.f, 0.f, 0.f, 0.f}, PQ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
@@ -213,13 +219,12 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
             for (int rt = 0; rt < NRT; ++rt) acc[rt] *= m0;
         }
         const float inv_sig = __builtin_amdgcn_rcpf(sig);
-        float X[4], Y[4];
+        float X[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float sg = gam_r[r] * sk;
             const uint32_t vv = vreg[cb][r >> 1];
             X[r] = fmaf(-sg, PK[r], bf2f((uint16_t)((r & 1) ? (vv >> 16) : (vv & 0xffffu))));
-            Y[r] = sg * PQ[r];
         }
         f32x4 W = {0.f, 0.f, 0.f, 0.f}, O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -227,8 +232,9 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
             W = mfma_f32_k4(CW[st], X[st] * inv_sig, W);
             O = mfma_f32_k4(CO[st], X[st], O);
         }
+        // + Y = diag(gamma) Q M0, tokens 4 g + r
 #pragma unroll
-        for (int st = 0; st < 4; ++st) O = mfma_f32_k4(n == 4 * st + g ? 1.f : 0.f, Y[st], O);
+        for (int r = 0; r < 4; ++r) O[r] = fmaf(gam_o[r] * sk, PQ[r], O[r]);
 
         // outputs: tokens 4 g + r of column j; flush 16 rows x 128 bytes every two blocks
 #pragma unroll
