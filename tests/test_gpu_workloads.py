@@ -77,6 +77,67 @@ def test_headline_steps_equal_period_calls():
     stp.free()
 
 
+def test_headline_fp8_window_sampled():
+    # the FP8 write window at the headline's full size in the launch its
+    # bench times (8 writes kept per state, 4096 x 16 states): ten steps, so
+    # the window fills and then merges its oldest write into the stored
+    # history twice; before each step the window oracle is rebuilt for 32+
+    # sampled tiles from what the GPU stores, then both take the step
+    import torch
+
+    from linear_attn_decode_pace_amd import pace, runtime
+    from tests import parity
+    from tests.gpu_cases import tok_tiles
+    from tests.test_gpu_window import _oracle_from
+
+    w = inputs.HEADLINE.replace(warmup=8)
+    S, seed = 8, 0
+    n = w.B * w.H
+    idx = _sample(w, seed, 32)
+    idx_t = torch.as_tensor(idx, device="cuda")
+    bits = np.tile(inputs.head_bits(w, seed), w.B).astype(np.int64)[idx]
+    wtok = inputs.concat(inputs.iter_tokens(
+        w, seed, inputs.SEG_WARMUP, [(t, t + 1) for t in range(w.warmup)], WORKERS))
+    M0 = runtime.warmup_state(w, seed, tok=wtok)
+    st = runtime.State(w, inputs.head_bits(w, seed), pace.PACE_INIT_F32, M0,
+                       flags=pace.PACE_FP8_WINDOW, fp8_window=S)
+    del M0
+
+    def sampled_state():
+        c, sc = st.read_codes()
+        wc, wf = st.read_window()
+        cnt, meta = st.read_step()
+        pick = lambda x, *shape: x.reshape(n, *shape)[idx_t].cpu().numpy()
+        return (pick(c, w.dk, w.dv), pick(sc, w.dv), pick(wc, S, w.dk + w.dv), pick(wf, S, 3),
+                pick(cnt), pick(meta, 2))
+
+    merges = 0
+    for t in range(S + 2):
+        say(f"[case] headline fp8 window S={S}, step {t}")
+        before = sampled_state()
+        ref = _oracle_from(before, bits, S, w.dk)
+        tok = inputs.tokens(w, seed, inputs.SEG_DECODE, t, t + 1)
+        out = runtime.out_buffer(w, 1)
+        st.step(runtime.DeviceTokens(tok), out)
+        q, k, v, a, b = [x[0] for x in tok_tiles(tok, idx, w.H)]
+        o_ref = ref.step(q, k, v, a, b)
+        o = out.reshape(n, w.dv)[idx_t].cpu().numpy()
+        parity.check_outputs(o[None], o_ref[None], f"headline window step {t}")
+        c, sc, wc, wf, cnt, meta = sampled_state()
+        np.testing.assert_array_equal(cnt, [len(ref.win[i]) for i in range(len(idx))])
+        np.testing.assert_allclose(meta[:, 0], ref.lam, rtol=1e-6)
+        merged = before[4] == S
+        if merged.any():
+            merges += int(merged.sum())
+            pre = np.stack([ref.last_pre[i] for i in np.nonzero(merged)[0]])
+            parity.check_encoded(c[merged], sc[merged], ref.codes[merged], ref.scales[merged], pre,
+                                 f"headline window step {t} merge", lattice_ties=True)
+        else:
+            np.testing.assert_array_equal(c, before[0])   # no merge: history untouched
+    assert merges == 2 * len(idx)
+    st.free()
+
+
 def test_mixed_b1024_whole_run_sampled():
     # 1024 sequences, all 512 decode steps (64 periods), outlier channels
     w = inputs.MIXED
