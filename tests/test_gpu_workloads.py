@@ -138,6 +138,75 @@ def test_headline_fp8_window_sampled():
     st.free()
 
 
+@pytest.mark.parametrize("tau", [1.0, 2.5])
+def test_headline_adaptive_period_sampled(tau):
+    # the adaptive period at the headline's full size in the launch its bench
+    # times (per-step calls, one tile per workgroup, maximum period 8):
+    # twelve steps of the whole batch; on 32+ sampled tiles every close
+    # decision, output, encode and (A, R) against the buffered oracle, which
+    # follows the GPU only where its A sits within 1e-4 of tau R
+    import torch
+
+    from linear_attn_decode_pace_amd import pace, runtime
+    from oracle import buffered
+    from tests import parity
+    from tests.gpu_cases import tok_tiles
+
+    w = inputs.HEADLINE.replace(warmup=8)
+    seed = 0
+    n = w.B * w.H
+    idx = _sample(w, seed, 32)
+    m = len(idx)
+    idx_t = torch.as_tensor(idx, device="cuda")
+    bits = inputs.head_bits(w, seed)
+    wtok = inputs.concat(inputs.iter_tokens(
+        w, seed, inputs.SEG_WARMUP, [(t, t + 1) for t in range(w.warmup)], WORKERS))
+    M0 = runtime.warmup_state(w, seed, tok=wtok)
+    st = runtime.State(w, bits, pace.PACE_INIT_F32, M0,
+                       flags=pace.PACE_STEP_BUFFER | pace.PACE_ADAPTIVE, adapt_tau=tau)
+    del M0
+
+    def read():
+        c, sc = st.read_codes()
+        fl, ar = st.read_step()
+        pick = lambda x, *shape: x.reshape(n, *shape)[idx_t].cpu().numpy()
+        return pick(c, w.dk, w.dv), pick(sc, w.dv), pick(fl), pick(ar, 2).astype(np.float64)
+
+    codes, scales, fill, ar = read()
+    ref = buffered.Buffered(codes, scales, np.tile(bits, w.B).astype(np.int64)[idx], w.period, tau=tau)
+    np.testing.assert_allclose(ar[:, 1], ref.R, rtol=1e-5)
+    closes = 0
+    for t in range(12):
+        say(f"[case] headline adaptive period tau={tau}, step {t}")
+        expect = np.array([ref.closes(i) for i in range(m)])
+        marg = np.array([abs(ref.margin(i)) if ref.tau * ref.R[i] > 0 else np.inf for i in range(m)])
+        tok = inputs.tokens(w, seed, inputs.SEG_DECODE, t, t + 1)
+        out = runtime.out_buffer(w, 1)
+        st.step(runtime.DeviceTokens(tok), out)
+        nc, ns, nfill, nar = read()
+        closed = nfill == 0
+        bad = (closed != expect) & (marg >= 1e-4)
+        assert not bad.any(), f"step {t}: close decisions differ at tiles {idx[bad]}"
+        q, k, v, a, b = [x[0] for x in tok_tiles(tok, idx, w.H)]
+        o_ref = ref.step(q, k, v, a, b, np.ones(m, dtype=bool), decide=closed)
+        o = out.reshape(n, w.dv)[idx_t].cpu().numpy()
+        parity.check_outputs(o[None], o_ref[None], f"adaptive step {t}")
+        np.testing.assert_array_equal(nfill, ref.fill)
+        if closed.any():
+            closes += int(closed.sum())
+            pre = np.stack([ref.last_pre[i] for i in np.nonzero(closed)[0]])
+            parity.check_encoded(nc[closed], ns[closed], ref.codes[closed], ref.scales[closed], pre,
+                                 f"adaptive step {t} encode")
+            ref.codes[closed], ref.scales[closed] = nc[closed], ns[closed]
+            for i in np.nonzero(closed)[0]:
+                ref.R[i] = ref._norm(i)
+        np.testing.assert_array_equal(nc, ref.codes)
+        np.testing.assert_allclose(nar[:, 1], ref.R, rtol=1e-5)
+        np.testing.assert_allclose(nar[:, 0], ref.A, rtol=1e-4, atol=1e-6 * ref.R.max())
+    assert closes > 0
+    st.free()
+
+
 def test_mixed_b1024_whole_run_sampled():
     # 1024 sequences, all 512 decode steps (64 periods), outlier channels
     w = inputs.MIXED
