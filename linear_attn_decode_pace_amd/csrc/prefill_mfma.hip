@@ -29,7 +29,7 @@
 //   only reaches the outputs, and two parts leave ~1e-5 relative error);
 //   X = V - diag(g) P_K; W = diag(G') T X on float32 MFMA; Lq T X on bf16
 //   MFMA over two parts of each factor (outputs only: ~1e-5 relative error);
-//   O = Lq T X + diag(g) P_Q; M <- g_C M + K^T W (bf16 MFMA, W in three
+//   O = Lq T X + diag(g) P_Q; M <- g_C M + K^T W (bf16 MFMA, W in two
 //   parts, each a 32-deep product over the chunk's tokens).
 // While a chunk is applied, lane group g of a consumer holds state rows
 // 32 ks + 8 g .. 32 ks + 8 g + 7 of each 32-row slice ks, so its MFMA k-slots
@@ -311,6 +311,15 @@ __device__ inline void split3(const f32x4 &x, uint32_t hi[2], uint32_t md[2], ui
     md[1] = pk_bf16(r2, r3);
     lo[0] = pk_bf16(sub_lo(md[0], r0), sub_hi(md[0], r1));
     lo[1] = pk_bf16(sub_lo(md[1], r2), sub_hi(md[1], r3));
+}
+
+// bf16 parts (hi, mid) of the four floats x[0..3]: x = hi + mid to 16
+// significant bits
+__device__ inline void split2(const f32x4 &x, uint32_t hi[2], uint32_t md[2]) {
+    hi[0] = pk_bf16(x[0], x[1]);
+    hi[1] = pk_bf16(x[2], x[3]);
+    md[0] = pk_bf16(sub_lo(hi[0], x[0]), sub_hi(hi[0], x[1]));
+    md[1] = pk_bf16(sub_lo(hi[1], x[2]), sub_hi(hi[1], x[3]));
 }
 
 // Producer, part 4 (phase B): T = (I + diag(beta) A)^-1 diag(beta) block by
@@ -672,26 +681,26 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
                 L.o[c & 1][HT + 4 * g + r][j] = fmaf(gq2[r], PQ2[r], O2[r]);
             }
 
-            // M <- gamma_C M + K^T W, W in three bf16 parts: the lane's k-slots
+            // M <- gamma_C M + K^T W, W in two bf16 parts (hi + mid, relative
+            // error below 2^-17; a third part cost 8 more MFMAs per chunk and
+            // 3% of the time): the lane's k-slots
             // are tokens 4 g .. 4 g + 3 (first half) and 16 + 4 g .. 16 + 4 g + 3
             // (second half), one 32-deep product per part; MFMA row m of row
             // tile rt is state row chunk_row(rt, m)
             const float gC = C.gam[CT - 1];
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) acc[rt] *= gC;
-            uint32_t h1[2], m1[2], l1[2], h2[2], m2[2], l2[2];
-            split3(W1, h1, m1, l1);
-            split3(W2, h2, m2, l2);
+            uint32_t h1[2], m1[2], h2[2], m2[2];
+            split2(W1, h1, m1);
+            split2(W2, h2, m2);
             const bf16x8 BH = __builtin_bit_cast(bf16x8, u32x4{h1[0], h1[1], h2[0], h2[1]});
             const bf16x8 BM = __builtin_bit_cast(bf16x8, u32x4{m1[0], m1[1], m2[0], m2[1]});
-            const bf16x8 BL = __builtin_bit_cast(bf16x8, u32x4{l1[0], l1[1], l2[0], l2[1]});
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) {
                 const int R = chunk_row(rt, n);
                 const bf16x8 A2 = __builtin_bit_cast(bf16x8, *(const u32x4 *)&KT[R][8 * (g ^ ((R >> 3) & 3))]);
                 acc[rt] = mfma_bf16_k32(A2, BH, acc[rt]);
                 acc[rt] = mfma_bf16_k32(A2, BM, acc[rt]);
-                acc[rt] = mfma_bf16_k32(A2, BL, acc[rt]);
             }
         }
         lds_barrier();  // chunk c+1 staged, chunk c's outputs complete
