@@ -24,9 +24,9 @@
 //   * one workgroup barrier per chunk, ordering LDS only (global loads and
 //     stores stay in flight across it).
 // Per chunk and column block:
-//   P_K = K M0 with M0 split exactly into three bf16 parts (hi + mid + lo), so
-//   the state update keeps float32 accuracy; P_Q = Q M0 over hi + mid (it
-//   only reaches the outputs, and two parts leave ~1e-5 relative error);
+//   P_K = K M0 and P_Q = Q M0 with M0 in two bf16 parts (hi + mid, 16
+//   significant bits: ~1e-5 relative error, far below the final encode's
+//   rounding; tie flips of the 4096-token parity cases did not change);
 //   X = V - diag(g) P_K; W = diag(G') T X on float32 MFMA; Lq T X on bf16
 //   MFMA over two parts of each factor (outputs only: ~1e-5 relative error);
 //   O = Lq T X + diag(g) P_Q; M <- g_C M + K^T W (bf16 MFMA, W in two
@@ -601,8 +601,9 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
         const uint16_t(*KT)[32] = L.kt[c & 1];
         if (c + 1 < n_chunks) build_kt(L.ch[(c + 1) % NBUF], L.kt[(c + 1) & 1], ln);
         {
-            // P_K = K M0 over three bf16 parts of M0 (the state update needs
-            // float32 accuracy), P_Q = Q M0 over two (outputs only), both
+            // P_K = K M0 and P_Q = Q M0 over two bf16 parts of M0 (hi + mid,
+            // 16 significant bits; a third part for P_K cost 8 more MFMAs
+            // per chunk and 5% of the time without moving a code), both
             // halves of the chunk; k-slot 8 g + e is state row 32 ks + 8 g + e
             f32x4 PK1 = {0.f, 0.f, 0.f, 0.f}, PK2 = PK1, PQ1 = PK1, PQ2 = PK1;
 #pragma unroll
@@ -612,12 +613,11 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
                 const bf16x8 AK2 = __builtin_bit_cast(bf16x8, kq_piece<DK>(C.kq, HT + tok_n, pc));
                 const bf16x8 AQ1 = __builtin_bit_cast(bf16x8, kq_piece<DK>(C.kq, CT + n, pc));
                 const bf16x8 AQ2 = __builtin_bit_cast(bf16x8, kq_piece<DK>(C.kq, CT + HT + n, pc));
-                uint32_t h0[2], m0[2], l0[2], h1[2], m1[2], l1[2];
-                split3(acc[2 * ks], h0, m0, l0);
-                split3(acc[2 * ks + 1], h1, m1, l1);
+                uint32_t h0[2], m0[2], h1[2], m1[2];
+                split2(acc[2 * ks], h0, m0);
+                split2(acc[2 * ks + 1], h1, m1);
                 const bf16x8 BH = __builtin_bit_cast(bf16x8, u32x4{h0[0], h0[1], h1[0], h1[1]});
                 const bf16x8 BM = __builtin_bit_cast(bf16x8, u32x4{m0[0], m0[1], m1[0], m1[1]});
-                const bf16x8 BL = __builtin_bit_cast(bf16x8, u32x4{l0[0], l0[1], l1[0], l1[1]});
                 PK1 = mfma_bf16_k32(AK1, BH, PK1);
                 PK2 = mfma_bf16_k32(AK2, BH, PK2);
                 PQ1 = mfma_bf16_k32(AQ1, BH, PQ1);
@@ -626,8 +626,6 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
                 PK2 = mfma_bf16_k32(AK2, BM, PK2);
                 PQ1 = mfma_bf16_k32(AQ1, BM, PQ1);
                 PQ2 = mfma_bf16_k32(AQ2, BM, PQ2);
-                PK1 = mfma_bf16_k32(AK1, BL, PK1);
-                PK2 = mfma_bf16_k32(AK2, BL, PK2);
             }
             // X for tokens 4 r + g and 16 + 4 r + g (the P_K rows this lane holds)
             float X1[4], X2[4];
