@@ -118,7 +118,8 @@ extern "C" {
 #define PACE_STEP_BUFFER 0x2u
 /* PACE_ADAPTIVE (with PACE_STEP_BUFFER): the period becomes adaptive ('PACE:
  * four-bit recurrent state by rounding less often', section 'Research angle':
- * round when the accumulated update norm crosses a threshold).  Each state
+ * the size of the updates since the last encode, not a token count, decides
+ * when to re-encode).  Each state
  * keeps A, the sum over its buffered tokens of the norm of their write into
  * the state, ||k_t|| * ||u_t|| with u_t = beta_t (v_t - alpha_t M_{t-1}^T k_t),
  * and R, the Frobenius norm of its stored state as of its last encode.  A

@@ -21,9 +21,9 @@ Readings where the pages are silent:
 * ``flush`` ends every partial period early: buffered tokens are applied and
   the state is encoded, as a shorter final period would be.
 
-Adaptive period (``tau`` given; the same page, section 'Research angle':
-round when the accumulated update norm crosses a threshold instead of every
-k tokens).  Reading taken:
+Adaptive period (``tau`` given; the same page, section 'Research angle',
+proposes tying the re-encode to how much the state has changed since the
+last one, not to a fixed token count).  Reading taken:
 
 * The update norm of token t is the Frobenius norm of its write into the
   state, ||k_t|| * ||u_t|| with u_t = beta_t (v_t - alpha_t M_{t-1}^T k_t)

@@ -1,11 +1,11 @@
 """Periodic rounding of a column-scaled low-bit GDN state (float64 reference).
 
 Follows 'PACE: four-bit recurrent state by rounding less often': TL;DR point
-(1) (keep the state in high precision across a few tokens, buffer them, and
-quantize once per period) and the flowchart 'Fewer roundings, less compounded
-error' (new tokens -> small buffer -> every k tokens a high-precision state
-update -> per-column 4-bit encode, 8-bit for long-memory heads -> stored
-state); also 'PACE: A New 4-Bit Recurrent State Quantization Method ...',
+(1) (the state is left unquantized while a short run of tokens is applied and
+is rounded once when the run ends) and the flowchart 'Fewer roundings, less
+compounded error' (tokens wait in a buffer; each k tokens the state is updated
+in high precision, then encoded column by column at 4 bits, or 8 bits for the
+heads that keep their errors longest); also 'PACE: A New 4-Bit Recurrent State Quantization Method ...',
 section 'Periodic Rounding: Reducing Error Accumulation'.
 
 Readings where the pages are silent:

@@ -122,3 +122,95 @@ def test_quant_pins_catch(bad, monkeypatch):
         except (AssertionError, ValueError, IndexError):
             caught += 1
     assert caught >= 1, bad.__name__
+
+
+# ---- FP8 window flush (oracle/window.py Window.flush) ----
+
+from oracle import window  # noqa: E402
+from tests import test_oracle_window as tw  # noqa: E402
+
+
+def _flush_variant(no_lam=False, no_delta=False, swap_delta=False):
+    def flush(self):
+        for i in range(self.codes.shape[0]):
+            if not self.win[i]:
+                continue
+            lam = 1.0 if no_lam else self.lam[i]
+            H = lam * quant.decode(self.codes[i], self.scales[i])
+            deltas = [e[4] for e in self.win[i]]
+            if swap_delta:
+                deltas = deltas[::-1]
+            for (kc, ks, uc, us, _), delta in zip(self.win[i], deltas):
+                dl = 1.0 if no_delta else delta
+                H = H + dl * np.outer(window.fp8_decode(kc, ks), window.fp8_decode(uc, us))
+            c, s = quant.encode(H[None], self.bits[i:i + 1])
+            self.codes[i], self.scales[i] = c[0], s[0]
+            self.lam[i] = 1.0
+            self.win[i] = []
+            self.last_pre[i] = H
+    return flush
+
+
+FLUSH_PINS = [lambda: [tw.test_flush_equals_encode_of_the_recurrence(s) for s in (0, 1, 2)]]
+
+
+@pytest.mark.parametrize("bad", [dict(no_lam=True), dict(no_delta=True), dict(swap_delta=True)],
+                         ids=["lam_dropped", "delta_dropped", "delta_order_reversed"])
+def test_flush_pins_catch(bad, monkeypatch):
+    monkeypatch.setattr(window.Window, "flush", _flush_variant(**bad))
+    caught = 0
+    for pin in FLUSH_PINS:
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught >= 1, bad
+
+
+def test_flush_variant_without_mistakes_passes(monkeypatch):
+    # the planted variants differ from the oracle only by their mistake
+    monkeypatch.setattr(window.Window, "flush", _flush_variant())
+    for pin in FLUSH_PINS:
+        pin()
+
+
+# ---- quotients (oracle/quant.py quotients) ----
+
+def _quot_row_scales(M, scales):
+    s64 = np.asarray(scales, dtype=np.float64)[..., :, None]
+    safe = np.where(s64 > 0, s64, 1.0)
+    return np.where(s64 > 0, np.asarray(M, dtype=np.float64) / safe, 0.0)
+
+
+def _quot_float32(M, scales):
+    s32 = np.asarray(scales, dtype=np.float32)[..., None, :]
+    safe = np.where(s32 > 0, s32, np.float32(1))
+    return np.where(s32 > 0, np.asarray(M, dtype=np.float32) / safe, 0).astype(np.float64)
+
+
+def _quot_no_zero_guard(M, scales):
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return np.asarray(M, dtype=np.float64) / np.asarray(scales, dtype=np.float64)[..., None, :]
+
+
+def _quot_recomputed_scale(M, scales):
+    a = np.max(np.abs(np.asarray(M, dtype=np.float64)), axis=-2)[..., None, :]
+    return np.where(a > 0, M / np.where(a > 0, a / 7, 1), 0.0)
+
+
+QUOT_PINS = [tq.test_quotients_constructed_values, tq.test_quotients_keep_float64_precision_near_ties,
+             lambda: [tq.test_quotients_round_to_the_encoded_codes(b) for b in (4, 8)]]
+
+
+@pytest.mark.parametrize("bad", [_quot_row_scales, _quot_float32, _quot_no_zero_guard,
+                                 _quot_recomputed_scale])
+def test_quotient_pins_catch(bad, monkeypatch):
+    monkeypatch.setattr(quant, "quotients", bad)
+    caught = 0
+    for pin in QUOT_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught >= 1, bad.__name__

@@ -148,3 +148,47 @@ def test_roundtrip_error_bounds(bits):
     # a decoded state encodes without error
     e2, _ = quant.roundtrip_error(quant.decode(c, s), bits)
     assert np.all(e2 == 0)
+
+
+def test_quotients_constructed_values():
+    # scales differ per column and the state is not square, so a quotient taken
+    # against the wrong axis's scale, or against a recomputed absmax, fails
+    s = np.array([0.0123, 0.5, 3.0e-4], dtype=np.float32)
+    x = np.array([[2.5, -7.0, 0.5],
+                  [-1.5, 6.5, 127.0],
+                  [0.0, 3.0, -126.5],
+                  [4.0, -0.5, 1.0]])
+    M = (x * s.astype(np.float64)[None, :])[None]      # exact: x has few significant bits
+    got = quant.quotients(M, s[None])
+    assert got.shape == (1, 4, 3)
+    assert np.array_equal(got[0], x)
+    # the given scales are used as they are: twice the scale halves the quotient
+    assert np.array_equal(quant.quotients(M, 2 * s[None])[0], x / 2)
+    # a zero scale gives zero quotients whatever the state holds
+    z = s.copy()
+    z[1] = 0
+    got = quant.quotients(M, z[None])
+    assert np.all(got[0, :, 1] == 0) and np.array_equal(got[0, :, [0, 2]], x[:, [0, 2]].T)
+
+
+def test_quotients_keep_float64_precision_near_ties():
+    # a quotient 1e-10 away from a half-integer: its tie distance must come out
+    # as 1e-10 (a float32 quotient would report 0 or ~1e-7)
+    s = np.float32(0.0123)
+    eps = 1e-10
+    n = np.array([0.5, 2.5, -3.5, 6.5])
+    M = ((n + eps) * float(s))[None, :, None]
+    d = quant.tie_distance(quant.quotients(M, np.array([[s]])))
+    np.testing.assert_allclose(d[0, :, 0], eps, rtol=1e-3)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_quotients_round_to_the_encoded_codes(bits):
+    # encode's codes are the clamped nearest-even rounding of the quotients
+    # against its own stored scales
+    rng = np.random.default_rng(11)
+    M = rng.standard_normal((5, 32, 16)) * rng.uniform(0.01, 10, (5, 1, 16))
+    M[0, :, 3] = 0
+    c, s = quant.encode(M, bits)
+    qm = quant.qmax(bits)
+    assert np.array_equal(np.clip(np.rint(quant.quotients(M, s)), -qm, qm).astype(np.int16), c)

@@ -113,3 +113,68 @@ def test_window_tracks_the_recurrence_closely():
     assert rel < 0.05, rel
     st.flush()
     assert all(len(w) == 0 for w in st.win) and np.all(st.lam == 1.0)
+
+
+def _flush_case(seed, T=5, d=16, S=8):
+    """A history on rows 0..d/2-1 (exactly representable codes) and T writes
+    on distinct rows of the other half: each key row of the state is still
+    zero when its token arrives, so every write is u_t = beta v_t, exact in
+    E4M3, and all float64 sums below are exact (dyadic gates)."""
+    rng = np.random.default_rng(seed)
+    H0 = rng.standard_normal((1, d, d))
+    H0[:, d // 2:, :] = 0
+    c0, s0 = quant.encode(H0, 8)
+    q = rng.standard_normal((T, 1, d))
+    k = np.zeros((T, 1, d))
+    k[np.arange(T), 0, d // 2 + rng.permutation(d // 2)[:T]] = 0.875
+    v = rng.choice([-6.0, -4.0, -3.5, -2.0, -1.75, 1.0, 2.0, 3.5, 4.0, 6.0], size=(T, 1, d))
+    v[:, 0, 0] = 7.0
+    a = rng.choice([0.5, 0.75], size=(T, 1))    # every gate decays history and writes
+    b = np.full((T, 1), 0.5)
+    return c0, s0, q, k, v, a, b, S
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_flush_equals_encode_of_the_recurrence(seed):
+    # a flush with no merge before it must store encode(M_T) of the plain
+    # recurrence: the history decayed by every gate (lam), each write decayed
+    # by the gates after it (delta), all in one encode
+    c0, s0, q, k, v, a, b, S = _flush_case(seed)
+    T = q.shape[0]
+    st = window.Window(c0, s0, 8, S=S)
+    for t in range(T):
+        st.step(q[t], k[t], v[t], a[t], b[t])
+    # no write has left the window yet: the stored history is untouched
+    assert len(st.win[0]) == T and np.array_equal(st.codes[0], c0[0])
+    MT, _ = gdn.run(quant.decode(c0, s0), q, k, v, a, b)
+    st.flush()
+    rc, rs = quant.encode(MT, 8)
+    np.testing.assert_array_equal(st.last_pre[0], MT[0])      # exact sums
+    np.testing.assert_array_equal(st.codes[0], rc[0])
+    np.testing.assert_array_equal(st.scales[0], rs[0])
+    assert st.lam[0] == 1.0 and st.win[0] == []
+
+
+@pytest.mark.parametrize("seed", [3, 4])
+def test_flush_encodes_the_state_it_holds(seed):
+    # with real data (and merges before it), a flush encodes exactly the state
+    # that state() reports just before it
+    rng = np.random.default_rng(seed)
+    n, d, T, S = 3, 16, 11, 4
+    c0, s0 = quant.encode(rng.standard_normal((n, d, d)), np.array([4, 8, 4]))
+    st = window.Window(c0, s0, np.array([4, 8, 4]), S=S)
+    q = rng.standard_normal((T, n, d))
+    k = rng.standard_normal((T, n, d))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, n, d))
+    a = rng.uniform(0.5, 1.0, (T, n))
+    b = rng.uniform(0.2, 0.8, (T, n))
+    for t in range(T):
+        st.step(q[t], k[t], v[t], a[t], b[t])
+    before = [st.state(i) for i in range(n)]
+    st.flush()
+    for i in range(n):
+        np.testing.assert_allclose(st.last_pre[i], before[i], rtol=1e-14, atol=1e-15)
+        rc, rs = quant.encode(before[i][None], st.bits[i:i + 1])
+        np.testing.assert_array_equal(st.codes[i], rc[0])
+        np.testing.assert_array_equal(st.scales[i], rs[0])
