@@ -26,12 +26,25 @@
  *    period (PACE wiki page, TL;DR point (1) and flowchart; 'PACE: A New
  *    4-Bit ...', section 'Periodic Rounding').  Outputs are read from the
  *    high-precision state, before the period-end encode.
+ *    "In float32" means: the state, every accumulation and the outputs are
+ *    float32.  The fused kernels (bf16 inputs, d_k = d_v = 64 or 128) run
+ *    the period's matrix products on bf16 matrix cores, exactly where the
+ *    operands are exact in bf16 (codes times tokens; the period's key and
+ *    query Gram products) and with the update's right factor split into two
+ *    bf16 parts (relative error below 2^-17); the prefill hand-off also
+ *    splits the decoded state and its in-chunk output product into two bf16
+ *    parts (about 1e-5 relative).
  *
  *  - Channel-aligned encoding: one scale per column, s_j = absmax_i |M_ij| / qmax
  *    in float32 (qmax = 7 for 4 bits, 127 for 8 bits), codes
  *    c_ij = round_to_nearest_even(M_ij / s_j); a zero column has s_j = 0 and
  *    zero codes ('PACE: A New 4-Bit ...', section 'Channel-Aligned Encoding';
- *    PACE wiki page, TL;DR point (2)).
+ *    PACE wiki page, TL;DR point (2)).  The per-column kernels divide
+ *    (correctly rounded); the fused kernels compute s_j = absmax *
+ *    float32(1 / qmax), within one ulp of the quotient, and take M_ij / s_j
+ *    through the hardware reciprocal (about one ulp), so a code can differ
+ *    from exact rounding only where M_ij / s_j sits within about 1e-6 of a
+ *    half-integer.
  *
  *  - Mixed heads: each head has a bit width (4 or 8), the same for every
  *    sequence; 8-bit heads are meant for heads whose rounding error persists
@@ -62,7 +75,7 @@
 extern "C" {
 #endif
 
-#define PACE_ABI_VERSION 2
+#define PACE_ABI_VERSION 3
 
 /* status codes */
 #define PACE_OK 0
@@ -225,6 +238,10 @@ int pace_raw_bytes(const pace_state *st, uint64_t *out);
  *   alpha, beta: device float32 [n_tok, B, H], 4-byte aligned; alpha is the
  *          gate (0 < alpha <= 1 expected), beta the write strength.
  *   out:   device float32 [n_tok, B, H, d_v], 16-byte aligned; may not alias inputs.
+ * Kernels: bf16 inputs with d_k = d_v = 64 or 128 and n_tok <= 16 run the
+ * fused matrix-core kernels, for any batch the pools can hold (offsets
+ * between tokens are 64-bit); float32 inputs, d_v != d_k and calls of more
+ * than 16 tokens run a per-column kernel, correct but about 50x slower.
  * Errors: EINVAL (null handle or pointer, n_tok out of range, misalignment,
  *         a handle allocated with PACE_STEP_BUFFER),
  *         EDEVICE (launch failure or an earlier asynchronous fault).
@@ -302,7 +319,8 @@ int pace_quant_stats(const pace_state *st, pace_stats *out, void *stream);
  *          16-byte aligned.  alpha, beta: device float32 [n_tok, B, H].
  *   out:   device float32 [n_tok, B, H, d_v] (16-byte aligned), or NULL.
  * bf16 inputs with d_k = d_v = 64 or 128 run the fused kernel (the state stays
- * on chip for the whole prompt); other shapes run the per-column kernel.
+ * on chip for the whole prompt) for any batch; other shapes run the
+ * per-column kernel.
  * Errors: EINVAL (null or misaligned pointer, n_tok < 1, a PACE_STEP_BUFFER
  *         handle), EDEVICE.
  */
@@ -325,6 +343,18 @@ int pace_prefill_f32(int32_t batch, int32_t heads, int32_t d_k, int32_t d_v, int
                      int32_t in_dtype, const void *q, const void *k, const void *v,
                      const float *alpha, const float *beta, float *state, float *out,
                      void *stream);
+
+/*
+ * Measurement utility, not part of the method: copy `bytes` from src to dst
+ * (both device, 16-byte aligned, not overlapping; bytes a multiple of 16)
+ * with 16-byte non-temporal loads and stores, one per lane, as the decode
+ * kernels stream their codes.  Its bandwidth is the attainable reference for
+ * the decode kernels' fraction of the HBM peak, and a copy of known size
+ * calibrates byte counters of a profiler.  bytes = 0 is a no-op.
+ * Errors: EINVAL (null or misaligned pointer, bytes not a multiple of 16),
+ *         EDEVICE.
+ */
+int pace_stream_copy(void *dst, const void *src, uint64_t bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -109,7 +109,9 @@ __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int
     static_assert(CPW % 2 == 0, "outputs are flushed every two column blocks");
     constexpr float QMAX = BITS == 4 ? 7.f : 127.f;
     const int g = lane >> 4, n = lane & 15;
-    const uint32_t tok_stride = (uint32_t)a.p.B * (uint32_t)a.p.H;  // (sequence, head) rows per token
+    // (sequence, head) rows per token; offsets between tokens are 64-bit, so
+    // any batch the pools can hold runs here
+    const size_t tok_stride = (size_t)a.p.B * (size_t)a.p.H;
     const size_t tile_row = (size_t)b * a.p.H + h;
     const int cb0 = q * CPW;
     // STEP (a PACE_STEP_BUFFER step): the chunk is the state's f buffered
@@ -154,12 +156,18 @@ __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int
         constexpr int CPR = DK / 8;                         // 16-byte chunks per token row
         constexpr int NL = (24 * CPR + 64 * WPT - 1) / (64 * WPT);  // loads per lane
         const uint16_t *srcs[3] = {a.k + tile_row * DK, a.q + tile_row * DK, a.v + tile_row * DK};
+        // load it of this lane reads token row (c / CPR) & 7 with c = lane +
+        // 64 (q + WPT it): token lane / CPR plus a wave-uniform step, so one
+        // per-lane 64-bit product serves every load
+        const size_t tok_elems = tok_stride * DK;
+        const size_t lane_off = (size_t)(lane / CPR) * tok_elems + (lane % CPR) * 8;
         u32x4 val[NL];
 #pragma unroll
         for (int it = 0; it < NL; ++it) {
             const int c = lane + 64 * (q + WPT * it);
             const int row = c / CPR, col = (c % CPR) * 8;
             const int t = row & 7, which = row >> 3;
+            const size_t off = lane_off + (size_t)(((64 / CPR) * (q + WPT * it)) & 7) * tok_elems;
             val[it] = u32x4{0u, 0u, 0u, 0u};
             if constexpr (STEP) {
                 // token f from the step's inputs [B, H, d]; earlier tokens (k, v
@@ -170,8 +178,7 @@ __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int
                     val[it] = *at((const u32x4 *)sbuf,
                                   (uint32_t)(t * 2 * DK + (which == 2 ? DK : 0) + col) * 2u);
             } else if (row < 24 && t < n_tok) {
-                val[it] = __builtin_nontemporal_load(
-                    at((const u32x4 *)srcs[which], (uint32_t)(t * tok_stride * DK + col) * 2u));
+                val[it] = __builtin_nontemporal_load((const u32x4 *)(srcs[which] + off));
             }
         }
         float ab = 0.f;
@@ -182,8 +189,7 @@ __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int
             if (STEP && t < f)
                 ab = sab[2 * t + is_beta];
             else if (t < n_tok)
-                ab = *at(is_beta ? a.beta + tile_row : a.alpha + tile_row,
-                         STEP ? 0u : (uint32_t)t * tok_stride * 4u);
+                ab = (is_beta ? a.beta : a.alpha)[tile_row + (STEP ? 0 : t * tok_stride)];
         }
 #pragma unroll
         for (int it = 0; it < NL; ++it) {
@@ -348,8 +354,9 @@ __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int
         }
     }
 
-    float *obase = a.out + tile_row * DK;
-    const uint32_t o_tok = tok_stride * DK * 4u;  // bytes between tokens of out
+    // this lane's part of an output flush: token row lane / 8, 16-byte chunk
+    // lane % 8 of the 32 staged columns
+    float *olane = a.out + (tile_row + (STEP ? 0 : (size_t)(lane >> 3) * tok_stride)) * DK + (lane & 7) * 4;
 
     // ---- this wave's column blocks (unrolled: ring slots stay in fixed registers) ----
 #pragma unroll
@@ -427,9 +434,7 @@ __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int
             wave_sync();
             const int t = lane >> 3, c4 = (lane & 7) * 4;
             const f32x4 x = *(const f32x4 *)&WO_lds.o[t][c4];
-            if (STEP ? t == f : t < n_tok)
-                __builtin_nontemporal_store(
-                    x, at((f32x4 *)obase, (STEP ? 0u : (uint32_t)t * o_tok) + (uint32_t)(16 * cb - 16 + c4) * 4u));
+            if (STEP ? t == f : t < n_tok) __builtin_nontemporal_store(x, (f32x4 *)(olane + 16 * cb - 16));
         }
         if constexpr (STEP) {
             if (adaptive && !pend) {
@@ -553,10 +558,10 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(MfmaArgs a) {
 }  // namespace
 
 bool mfma_supported(int dk, int dv, int n_tok, int in_bf16, long long rows_per_token) {
-    // per-lane byte offsets (tokens x rows x d x 4 bytes) are kept in 32 bits
-    // (periods of 9..16 tokens take the 16-token chunk kernel)
-    return in_bf16 && dk == dv && (dk == 128 || dk == 64) && n_tok >= 1 && n_tok <= 2 * CH &&
-           (long long)2 * CH * rows_per_token * dk * 4 < (1ll << 31);
+    // periods of 9..16 tokens take the 16-token chunk kernel; offsets between
+    // tokens are 64-bit, so the batch is not limited here
+    (void)rows_per_token;
+    return in_bf16 && dk == dv && (dk == 128 || dk == 64) && n_tok >= 1 && n_tok <= 2 * CH;
 }
 
 namespace {

@@ -57,7 +57,9 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
     constexpr float KAPPA = Loader<DK, BITS>::KAPPA;
     const int g = lane >> 4, n = lane & 15;
     const int n_tok = a.n_tok;
-    const uint32_t tok_stride = (uint32_t)a.p.B * (uint32_t)a.p.H;
+    // (sequence, head) rows per token; offsets between tokens are 64-bit
+    const size_t tok_stride = (size_t)a.p.B * (size_t)a.p.H;
+    const size_t tok_elems = tok_stride * DK;
     const size_t tile_row = (size_t)b * a.p.H + h;
 
     uint8_t *codes = BITS == 4
@@ -79,16 +81,18 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
         constexpr int CPR = DK / 8;                // 16-byte chunks per token row
         constexpr int NL = 3 * C16 * CPR / 64;     // loads per lane (12 for d = 128)
         const uint16_t *srcs[3] = {a.k + tile_row * DK, a.q + tile_row * DK, a.v + tile_row * DK};
+        // load it reads token row (lane / CPR + (64 / CPR) it) & 15: the lane's
+        // own token plus a wave-uniform step (one per-lane 64-bit product)
+        const size_t lane_off = (size_t)(lane / CPR) * tok_elems + (lane % CPR) * 8;
         u32x4 val[NL];
 #pragma unroll
         for (int it = 0; it < NL; ++it) {
             const int c = lane + 64 * it;
-            const int row = c / CPR, col = (c % CPR) * 8;
-            const int t = row & 15, which = row >> 4;  // uniform per load
+            const int row = c / CPR;
+            const int t = row & 15, which = row >> 4;  // which is uniform per load
+            const size_t off = lane_off + (size_t)(((64 / CPR) * it) & 15) * tok_elems;
             val[it] = u32x4{0u, 0u, 0u, 0u};
-            if (t < n_tok)
-                val[it] = __builtin_nontemporal_load(
-                    at((const u32x4 *)srcs[which], (uint32_t)(t * tok_stride * DK + col) * 2u));
+            if (t < n_tok) val[it] = __builtin_nontemporal_load((const u32x4 *)(srcs[which] + off));
         }
         float ab = 0.f;
         if (lane < 32) {
@@ -96,7 +100,7 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
             const bool is_beta = lane >= 16;
             ab = is_beta ? 0.f : 1.f;
             if (t < n_tok)
-                ab = *at(is_beta ? a.beta + tile_row : a.alpha + tile_row, (uint32_t)t * tok_stride * 4u);
+                ab = (is_beta ? a.beta : a.alpha)[tile_row + t * tok_stride];
         }
 #pragma unroll
         for (int it = 0; it < NL; ++it) {
@@ -182,8 +186,9 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
     }
     wave_sync();  // the chunk matrices are dead from here on: their LDS holds outputs
 
-    float *obase = a.out + tile_row * DK;
-    const uint32_t o_tok = tok_stride * DK * 4u;
+    // this lane's part of an output flush: token rows lane / 8 (+ 8), 16-byte
+    // chunk lane % 8 of the 32 staged columns
+    float *olane = a.out + (tile_row + (size_t)(lane >> 3) * tok_stride) * DK + (lane & 7) * 4;
 
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
@@ -246,8 +251,7 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
                 const int t = (lane >> 3) + 8 * half, c4 = (lane & 7) * 4;
                 const f32x4 x = *(const f32x4 *)&L.u.o[t][c4];
                 if (t < n_tok)
-                    __builtin_nontemporal_store(
-                        x, at((f32x4 *)obase, (uint32_t)t * o_tok + (uint32_t)(16 * cb - 16 + c4) * 4u));
+                    __builtin_nontemporal_store(x, (f32x4 *)(olane + half * 8 * tok_elems + 16 * cb - 16));
             }
         }
 

@@ -36,6 +36,8 @@
 // are eight adjacent key columns (one 16-byte LDS read); the stored pool
 // layout is restored for the final encode.  Outputs of a chunk go through
 // double-buffered LDS and leave as whole rows.
+#include <type_traits>
+
 #include "mfma_common.h"
 #include "pace_prefill.h"
 
@@ -137,17 +139,34 @@ struct PrefillArgs {
     int tiles;
 };
 
+// Element x of token t (inside a chunk) of a token-major [T, B, H, d] tensor,
+// from that chunk's base: 32-bit lane offsets when a chunk's whole span fits
+// in 32 bits (WIDE_OFF = false, fewer instructions in the chunk loop), 64-bit
+// otherwise.
+template <bool WIDE_OFF, int DK, class T>
+__device__ inline T *tok_at(T *base, int t, const PrefillArgs &a, uint32_t x) {
+    if constexpr (WIDE_OFF) {
+        return base + (size_t)t * ((size_t)a.p.B * (size_t)a.p.H) * DK + x;
+    } else {
+        const uint32_t tok_stride = (uint32_t)a.p.B * (uint32_t)a.p.H;
+        return at(base, (uint32_t)(t * tok_stride * DK + x) * (uint32_t)sizeof(T));
+    }
+}
+
 // Producer: copy chunk c's k and q rows and its alpha / beta from HBM into
 // LDS (buffer-to-LDS loads: lane l of each instruction fills 16 bytes at
 // 16 l).  Tokens past the prompt repeat its last token; phase A resets their
 // gates.
 template <int DK>
 __device__ __attribute__((always_inline)) inline void issue_chunk(const PrefillArgs &a, ChunkLds<DK> &N,
-                                                                  size_t tile_row, int c, int lane) {
+                                                                  size_t tile_row, int c, int lane,
+                                                                  bool wide) {
     launder(lane);
     constexpr int SPR = DK / 8;    // 16-byte slots per row
     constexpr int RPI = 64 / SPR;  // rows per instruction
-    const uint32_t tok_stride = (uint32_t)a.p.B * (uint32_t)a.p.H;
+    // rows per token (32-bit arithmetic unless the launch needs 64-bit offsets)
+    const size_t tok_stride = wide ? (size_t)a.p.B * (size_t)a.p.H
+                                   : (size_t)((uint32_t)a.p.B * (uint32_t)a.p.H);
     const int t0 = CT * c, last = a.n_tok - 1 - t0;
     const size_t base = ((size_t)t0 * tok_stride + tile_row) * DK;
 #pragma unroll
@@ -157,7 +176,9 @@ __device__ __attribute__((always_inline)) inline void issue_chunk(const PrefillA
         const int t = min(row & (CT - 1), last);
         const int piece = slot ^ kq_swz<DK>(row);
         const uint16_t *src = (which == 0 ? a.k : a.q) + base;
-        __builtin_amdgcn_global_load_lds(at(src, (uint32_t)(t * tok_stride * DK + 8 * piece) * 2u),
+        const uint16_t *at_t = wide ? tok_at<true, DK>(src, t, a, 8 * piece)
+                                    : tok_at<false, DK>(src, t, a, 8 * piece);
+        __builtin_amdgcn_global_load_lds(at_t,
                                          (__attribute__((address_space(3))) void *)&N.kq[it * RPI][0], 16, 0, 0);
     }
     const int t = min(lane & (CT - 1), last);
@@ -438,7 +459,7 @@ __device__ inline void to_pool_layout(f32x4 *acc, int lane) {
     }
 }
 
-template <int DK, int BITS, bool ERR>
+template <int DK, int BITS, bool ERR, bool WIDE_OFF>
 __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int h, int slot,
                              int wave, int lane) {
     constexpr int NKS = DK / 32;  // k-slices of 32 rows
@@ -448,7 +469,9 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
     constexpr float KAPPA = Loader<DK, BITS>::KAPPA;
     const int g = lane >> 4, n = lane & 15;
     const size_t tile_row = (size_t)b * a.p.H + h;
-    const uint32_t tok_stride = (uint32_t)a.p.B * (uint32_t)a.p.H;
+    // rows per token: 32-bit arithmetic unless the launch needs 64-bit offsets
+    using TokStride = typename std::conditional<WIDE_OFF, size_t, uint32_t>::type;
+    const TokStride tok_stride = (TokStride)a.p.B * (TokStride)a.p.H;
     const int n_chunks = (a.n_tok + CT - 1) / CT;
     const bool producer = wave >= NCB;
     const int cb = wave, j = 16 * cb + n;
@@ -483,13 +506,13 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
             prep_a<DK>(N, ps, lane);
         };
         auto phase_b = [&](int c) {
-            if (c + NPROD < n_chunks) issue_chunk<DK>(a, L.ch[(c + NPROD) % NBUF], tile_row, c + NPROD, lane);
+            if (c + NPROD < n_chunks) issue_chunk<DK>(a, L.ch[(c + NPROD) % NBUF], tile_row, c + NPROD, lane, WIDE_OFF);
             __builtin_amdgcn_s_setprio(3);
             prep_b<DK>(L.ch[c % NBUF], ps, lane);
             __builtin_amdgcn_s_setprio(0);
         };
         if (p < n_chunks) {
-            issue_chunk<DK>(a, L.ch[p], tile_row, p, lane);
+            issue_chunk<DK>(a, L.ch[p], tile_row, p, lane, WIDE_OFF);
             phase_a(p);
             if (p == 0) phase_b(0);
         }
@@ -536,8 +559,7 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
             const int t = t0 + e / PER_ROW, c4 = (e % PER_ROW) * 4;
             if (t < nv) {  // chunk c's real tokens
                 const f32x4 x = *(const f32x4 *)&L.o[c & 1][t][c4];
-                __builtin_nontemporal_store(
-                    x, at((f32x4 *)obase, (uint32_t)(t * tok_stride * DK + c4) * 4u));
+                __builtin_nontemporal_store(x, (f32x4 *)tok_at<WIDE_OFF, DK>(obase, t, a, c4));
             }
         }
     };
@@ -573,7 +595,7 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int t = min(4 * e + g, last);
-            vv[e] = *at(vbase, (uint32_t)(t * tok_stride * DK + j) * 2u);
+            vv[e] = *tok_at<WIDE_OFF, DK>(vbase, t, a, j);
         }
     };
     // v values of the chunk being applied and of the next one, in two
@@ -745,7 +767,7 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
     }
 }
 
-template <int DK, bool ERR>
+template <int DK, bool ERR, bool WIDE_OFF>
 __global__ void __launch_bounds__(64 * (DK / 16 + NPROD)) prefill_mfma_kernel(PrefillArgs a) {
     __shared__ PrefillLds<DK> L;
     const int lane = threadIdx.x & 63;
@@ -754,19 +776,21 @@ __global__ void __launch_bounds__(64 * (DK / 16 + NPROD)) prefill_mfma_kernel(Pr
     const int b = w / a.p.H, h = w - b * a.p.H;
     const int m = a.p.head_map[h];
     if ((m >> 16) == 8)
-        prefill_tile<DK, 8, ERR>(a, L, b, h, m & 0xffff, wave, lane);
+        prefill_tile<DK, 8, ERR, WIDE_OFF>(a, L, b, h, m & 0xffff, wave, lane);
     else
-        prefill_tile<DK, 4, ERR>(a, L, b, h, m & 0xffff, wave, lane);
+        prefill_tile<DK, 4, ERR, WIDE_OFF>(a, L, b, h, m & 0xffff, wave, lane);
 }
 
 }  // namespace
 
 bool prefill_mfma_supported(int dk, int dv, int in_bf16, long long rows_per_token) {
-    // per-lane token offsets inside a chunk (32 tokens x rows x d x 4 bytes
-    // for the outputs) are kept in 32 bits
-    return in_bf16 && dk == dv && (dk == 128 || dk == 64) &&
-           (long long)CT * rows_per_token * dk * 4 < (1ll << 31);
+    // any batch: launches whose chunk span exceeds 32-bit offsets take the
+    // 64-bit instantiation
+    (void)rows_per_token;
+    return in_bf16 && dk == dv && (dk == 128 || dk == 64);
 }
+
+
 
 hipError_t launch_prefill_mfma(const PoolView &p, int n_tok, const void *q, const void *k,
                                const void *v, const float *alpha, const float *beta, float *out,
@@ -782,17 +806,35 @@ hipError_t launch_prefill_mfma(const PoolView &p, int n_tok, const void *q, cons
     a.n_tok = n_tok;
     a.tiles = p.B * p.H;
     const bool err = p.colerr != nullptr;
+    // byte span of one chunk's outputs (float32): 32-bit lane offsets suffice below 2^32
+    const bool wide = (unsigned long long)CT * a.tiles * p.dk * sizeof(float) >= (1ull << 32);
+    const dim3 grid(a.tiles), block(64 * (p.dk / 16 + NPROD));
+#define PACE_PREFILL_LAUNCH(DK_, ERR_, WIDE_) \
+    hipLaunchKernelGGL((prefill_mfma_kernel<DK_, ERR_, WIDE_>), grid, block, 0, s, a)
     if (p.dk == 128) {
         if (err)
-            hipLaunchKernelGGL((prefill_mfma_kernel<128, true>), dim3(a.tiles), dim3(64 * (8 + NPROD)), 0, s, a);
+            {
+            if (wide) PACE_PREFILL_LAUNCH(128, true, true);
+            else PACE_PREFILL_LAUNCH(128, true, false);
+        }
         else
-            hipLaunchKernelGGL((prefill_mfma_kernel<128, false>), dim3(a.tiles), dim3(64 * (8 + NPROD)), 0, s, a);
+            {
+            if (wide) PACE_PREFILL_LAUNCH(128, false, true);
+            else PACE_PREFILL_LAUNCH(128, false, false);
+        }
     } else {
         if (err)
-            hipLaunchKernelGGL((prefill_mfma_kernel<64, true>), dim3(a.tiles), dim3(64 * (4 + NPROD)), 0, s, a);
+            {
+            if (wide) PACE_PREFILL_LAUNCH(64, true, true);
+            else PACE_PREFILL_LAUNCH(64, true, false);
+        }
         else
-            hipLaunchKernelGGL((prefill_mfma_kernel<64, false>), dim3(a.tiles), dim3(64 * (4 + NPROD)), 0, s, a);
+            {
+            if (wide) PACE_PREFILL_LAUNCH(64, false, true);
+            else PACE_PREFILL_LAUNCH(64, false, false);
+        }
     }
+#undef PACE_PREFILL_LAUNCH
     return hipGetLastError();
 }
 

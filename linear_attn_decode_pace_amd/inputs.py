@@ -221,6 +221,8 @@ def mean_alpha(w: Workload, seed: int) -> np.ndarray:
     """Mean gate per head over the pre-decode tokens (warm-up or prompt), [H]."""
     seg, n = (SEG_PROMPT, w.prompt) if w.prompt else (SEG_WARMUP, w.warmup)
     acc = np.zeros(w.H, dtype=np.float64)
+    if n == 0:   # no tokens before decode: every head ties (lowest indices win)
+        return acc
     for blk in range((n + TB - 1) // TB):
         a = _block(w, seed, seg, blk, alpha_only=True).astype(np.float64)
         m = min(TB, n - blk * TB)
