@@ -79,3 +79,12 @@ def test_vanishing_decay(period, value):
     w = inputs.ragged(f"vanish-k{period}", 107, B=4, H=3, n_int8=1, period=period, steps=2 * period)
     run_case(w, 8, default_calls(w), tok_hook=_vanishing_alpha(value),
              label=f"vanish-k{period}-{value:g}")
+
+
+@pytest.mark.parametrize("dv", [48, 80])
+def test_dv_differs_from_dk(dv):
+    # d_v != d_k (the per-column kernels) with column blocks that do not fill
+    # a wavefront (48 columns) or end part way into one (80), mixed heads,
+    # column outliers, and a short final call
+    w = inputs.ragged(f"dv{dv}", 108, B=3, H=3, dk=128, dv=dv, n_int8=1, n_outliers=4, steps=21)
+    run_case(w, 9, default_calls(w, 2) + [(16, 21)])

@@ -25,6 +25,8 @@ CASES = [
     # steps of periods above 8 run the per-column kernel, period calls the
     # 16-token fused kernel: checked against the oracle only
     ("step-k12", dict(B=3, H=3, n_int8=1, period=12, steps=24)),
+    # d_v != d_k: the per-column step and flush kernels
+    ("step-dv48", dict(B=3, H=3, dv=48, n_int8=1, n_outliers=4, period=4, steps=12)),
 ]
 
 
@@ -37,7 +39,7 @@ def _states(w, seed):
     return bits, per, stp
 
 
-@pytest.mark.parametrize("name,kw", CASES[:3])
+@pytest.mark.parametrize("name,kw", CASES[:3] + [CASES[4]])
 def test_steps_equal_period_calls(name, kw):
     import torch
     from linear_attn_decode_pace_amd import runtime
@@ -63,7 +65,7 @@ def test_steps_equal_period_calls(name, kw):
     stp.free()
 
 
-@pytest.mark.parametrize("name,kw", [CASES[0], CASES[1], CASES[3]])
+@pytest.mark.parametrize("name,kw", [CASES[0], CASES[1], CASES[3], CASES[4]])
 def test_masked_steps_against_buffered_oracle(name, kw):
     import torch
     from linear_attn_decode_pace_amd import pace, runtime
@@ -155,6 +157,7 @@ ADAPT_CASES = [
     ("adapt-k8-mask", dict(B=3, H=5, n_int8=2, n_outliers=8, period=8, steps=40), 2.5, True),
     ("adapt-d64", dict(B=4, H=4, dk=64, dv=64, n_int8=1, period=8, steps=32), 1.0, False),
     ("adapt-f32", dict(B=2, H=3, n_int8=1, dtype=inputs.DT_F32, period=6, steps=30), 1.0, True),  # per-column
+    ("adapt-dv80", dict(B=3, H=3, dv=80, n_int8=1, n_outliers=4, period=6, steps=24), 1.0, True),  # per-column
 ]
 
 

@@ -70,6 +70,9 @@ CASES = [
     ("win-s12", dict(B=2, H=3, n_int8=1, steps=16), 12),
     # 256 states in 64 workgroups: two whole groups of the XCD order
     ("win-xcd", dict(B=16, H=16, dk=64, dv=64, n_int8=4, steps=5), 3),
+    # d_v != d_k: the per-column window kernels
+    ("win-dv80", dict(B=2, H=3, dv=80, n_int8=1, n_outliers=4, steps=8), 3),
+    ("win-dv48", dict(B=2, H=2, dk=64, dv=48, n_int8=1, steps=6), 2),
 ]
 
 
@@ -78,7 +81,7 @@ def test_window_steps_against_oracle(name, kw, S):
     _run(name, kw, S, masked=False)
 
 
-@pytest.mark.parametrize("name,kw,S", [CASES[0], CASES[2], CASES[3]])
+@pytest.mark.parametrize("name,kw,S", [CASES[0], CASES[2], CASES[3], CASES[6]])
 def test_window_masked_steps(name, kw, S):
     _run(name + "-mask", kw, S, masked=True)
 
