@@ -545,6 +545,15 @@ PACE_API int pace_quant_stats(const pace_state *st, pace_stats *out, void *strea
     return ok();
 }
 
+PACE_API int pace_stream_copy(void *dst, const void *src, uint64_t bytes, void *stream) {
+    if (!dst || !src) return fail(PACE_EINVAL, "null pointer");
+    if (!aligned(dst, 16) || !aligned(src, 16)) return fail(PACE_EINVAL, "dst and src must be 16-byte aligned");
+    if (bytes % 16) return fail(PACE_EINVAL, "bytes must be a multiple of 16");
+    hipError_t e = pace::launch_stream_copy(dst, src, (size_t)bytes, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "stream copy launch");
+    return ok();
+}
+
 PACE_API int pace_prefill_f32(int32_t batch, int32_t heads, int32_t d_k, int32_t d_v,
                               int32_t n_tok, int32_t in_dtype, const void *q, const void *k,
                               const void *v, const float *alpha, const float *beta,

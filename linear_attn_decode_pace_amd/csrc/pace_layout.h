@@ -84,6 +84,8 @@ hipError_t launch_read(const PoolView &p, int what, void *dst, float *scales_dst
                        hipStream_t s);
 hipError_t launch_count_zero_scales(const PoolView &p, unsigned long long *counter,
                                     hipStream_t s);
+// streaming copy of `bytes` (a multiple of 16) between 16-byte aligned buffers
+hipError_t launch_stream_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
 // per head h: out[2 h] = sum of colerr[b, h, j, 0], out[2 h + 1] = sum of
 // colerr[b, h, j, 1] over b and j, in float64
 hipError_t launch_reduce_colerr(const PoolView &p, double *out, hipStream_t s);

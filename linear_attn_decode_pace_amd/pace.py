@@ -15,7 +15,9 @@ import os
 from typing import Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpace.so")
+# PACE_LIBRARY may name another build of the same ABI (e.g. the host-sanitizer
+# build the CPU tests make); by default the in-tree libpace.so is loaded
+LIB_PATH = os.environ.get("PACE_LIBRARY") or os.path.join(_HERE, "libpace.so")
 
 PACE_OK = 0
 PACE_EINVAL = -1
@@ -45,7 +47,7 @@ PACE_STATS_MAX_HEADS = 256
 EXPORTED = ("pace_abi_version", "pace_last_error", "pace_state_alloc", "pace_state_free",
             "pace_state_config", "pace_raw_bytes", "pace_decode_period", "pace_read_state",
             "pace_quant_stats", "pace_prefill_f32", "pace_decode_step", "pace_flush_steps",
-            "pace_prefill_encode")
+            "pace_prefill_encode", "pace_stream_copy")
 
 
 class PaceError(RuntimeError):
@@ -106,6 +108,7 @@ def _load():
         "pace_decode_step": ([vp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "pace_flush_steps": ([vp, vp], ctypes.c_int),
         "pace_prefill_encode": ([vp, i32, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+        "pace_stream_copy": ([vp, vp, ctypes.c_uint64, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -194,6 +197,10 @@ def pace_decode_step(st: int, q, k, v, alpha, beta, out, active=None, stream=Non
 def pace_prefill_encode(st: int, n_tok: int, q, k, v, alpha, beta, out=None, stream=None) -> None:
     _check(LIB.pace_prefill_encode(st, n_tok, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                    _ptr(out), _stream(stream)))
+
+
+def pace_stream_copy(dst, src, nbytes: int, stream=None) -> None:
+    _check(LIB.pace_stream_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)))
 
 
 def pace_flush_steps(st: int, stream=None) -> None:

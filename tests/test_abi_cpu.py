@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert pace.pace_abi_version() == 2
+    assert pace.pace_abi_version() == 3
 
 
 def _cfg(**kw):
@@ -135,3 +135,37 @@ def test_binding_raises_with_message():
     with pytest.raises(pace.PaceError) as e:
         pace.pace_state_alloc(1, 1, 96, 128, 8, pace.PACE_DTYPE_BF16, [4], stream=0)
     assert e.value.status == pace.PACE_EUNSUPPORTED and "d_k" in e.value.message
+
+
+def test_stream_copy_rejects_bad_arguments():
+    f = pace.LIB.pace_stream_copy
+    assert f(None, 16, 32, None) == pace.PACE_EINVAL
+    assert f(16, None, 32, None) == pace.PACE_EINVAL
+    assert f(24, 16, 32, None) == pace.PACE_EINVAL   # misaligned dst
+    assert f(16, 40, 32, None) == pace.PACE_EINVAL   # misaligned src
+    assert f(16, 32, 40, None) == pace.PACE_EINVAL   # not a multiple of 16
+    assert "multiple of 16" in pace.pace_last_error()
+
+
+def _gpu_present() -> bool:
+    import torch
+    return torch.cuda.device_count() > 0   # counts devices without initialising them
+
+
+def test_valid_alloc_without_a_device_is_edevice():
+    # every argument is valid, so the call reaches the HIP runtime, which has
+    # no device here: PACE_EDEVICE with the runtime's message, no handle
+    if _gpu_present():
+        pytest.skip("a GPU is present: a valid alloc succeeds")
+    hb = (ctypes.c_uint8 * 2)(4, 8)
+    cfg = pace.pace_config(2, 2, 128, 128, 8, pace.PACE_DTYPE_BF16,
+                           ctypes.cast(hb, ctypes.POINTER(ctypes.c_uint8)), 0, 0.0, 0)
+    out = ctypes.c_void_p()
+    assert pace.LIB.pace_state_alloc(ctypes.byref(cfg), pace.PACE_INIT_ZERO, None, None,
+                                     ctypes.byref(out)) == pace.PACE_EDEVICE
+    assert out.value is None
+    assert pace.pace_last_error() != ""
+    # the same holds for the stateless entry points once their arguments pass
+    assert pace.LIB.pace_stream_copy(16, 32, 64, None) == pace.PACE_EDEVICE
+    assert pace.LIB.pace_prefill_f32(1, 1, 128, 128, 1, 1, 16, 32, 48, 64, 80, 96, None,
+                                     None) == pace.PACE_EDEVICE
