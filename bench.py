@@ -13,8 +13,10 @@ of distinct periods is resident in HBM before timing.  The initial state comes
 from 32 unquantized warm-up tokens run by the library's prefill kernel.
 
 Prints one JSON line: token-steps/s (sequences x tokens per second), the
-decode kernel's achieved HBM bandwidth against MI355X's 8 TB/s, and the float64
-CPU oracle timed on a bounded sample of the same workload.
+decode kernel's achieved HBM bandwidth against MI355X's 8 TB/s with per-launch
+minimum, median and maximum, the attainable bandwidth of a streaming
+device-to-device copy timed after the decode region, and the float64 CPU
+oracle timed over the whole batch on the host's cores (one process per core).
 """
 from __future__ import annotations
 
@@ -128,39 +130,135 @@ def traffic_from_profile(name: str, sha: str, n_launch_bytes: int):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(w, seed, warm_tok, periods_tok, head_bits, n_seq):
-    """Time the float64 oracle over the first n_seq sequences (all heads) for
-    the given periods, from the oracle's own warm-up state (warm-up untimed)."""
+# What the decode path computes in: 4/8-bit codes with float32 column scales,
+# bf16 tokens, float32 state, accumulators and outputs; matrix products on bf16
+# MFMA with exact operands (codes, tokens) or two bf16 parts (the update's W,
+# relative error below 2^-17); scale = absmax * float32(1 / qmax), quotients
+# through the hardware reciprocal.
+ARITHMETIC_DTYPE = "f32+bf16"
+ARITHMETIC = ("float32 state/accumulators/outputs; bf16 MFMA on exact code and token operands; "
+              "update W in two bf16 parts (rel. err < 2^-17); 4/8-bit codes, float32 scales")
+
+
+def copy_calibration(nbytes: int, reps: int = 10) -> dict:
+    """Attainable device bandwidth, timed after the decode region (so it
+    cannot warm anything up for it): the library's streaming copy (16-byte
+    non-temporal loads and stores, the decode kernels' pattern) and torch's
+    device-to-device copy of the same buffers, best of `reps` each; GB/s
+    count read + write bytes."""
+    import torch
+
+    from linear_attn_decode_pace_amd import pace
+
+    nbytes -= nbytes % 16
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+
+    def best(fn):
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return 2 * nbytes / (min(ts) * 1e-3) / 1e9
+
+    stream_gbs = best(lambda: pace.pace_stream_copy(dst, src, nbytes))
+    torch_gbs = best(lambda: dst.copy_(src))
+    del src, dst
+    return {"stream_copy_gbs": stream_gbs, "torch_copy_gbs": torch_gbs, "bytes": nbytes,
+            "unit": "GB/s", "frac_of_peak": stream_gbs / PEAK_HBM_GBS,
+            "note": "read + write bytes; best of %d; timed after the decode region" % reps}
+
+
+def _cpu_model() -> str:
+    try:
+        return next((l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
+                     if l.startswith("model name")), platform.processor())
+    except OSError:
+        return platform.processor()
+
+
+def _oracle_shard(args):
+    """One worker of the CPU baseline: the float64 oracle over sequences
+    [b0, b1), all heads.  Its warm-up state and initial encode are untimed;
+    the timed periods start when every worker has reached the barrier."""
+    (dk, dv, H, head_bits, warm, periods, barrier, results) = args
     import numpy as np
+    from threadpoolctl import threadpool_limits
 
     from oracle import gdn
     from oracle import pace as opace
     from oracle import quant
 
-    b = np.repeat(np.arange(n_seq), w.H)
-    h = np.tile(np.arange(w.H), n_seq)
-    bits = np.tile(np.asarray(head_bits), n_seq).astype(np.int64)
+    with threadpool_limits(limits=1):
+        n = warm[0].shape[1]
+        bits = np.tile(np.asarray(head_bits), n // H).astype(np.int64)
+        M0 = gdn.from_zero(dk, dv, *warm)
+        codes, scales = quant.encode(M0, bits)
+        del M0
+        barrier.wait()
+        t0 = time.perf_counter()
+        for a in periods:
+            _, codes, scales, _ = opace.period(codes, scales, bits, *a)
+        results.put(time.perf_counter() - t0)
 
-    def arr(tok):
-        return [tok.f64(x)[:, b, h] for x in ("q", "k", "v", "alpha", "beta")]
 
-    M0 = gdn.from_zero(w.dk, w.dv, *arr(warm_tok))
-    codes, scales = quant.encode(M0, bits)
-    toks = [arr(t) for t in periods_tok]
-    t0 = time.perf_counter()
-    for a in toks:
-        _, codes, scales, _ = opace.period(codes, scales, bits, *a)
-    dt = time.perf_counter() - t0
-    n_tok = sum(t.T for t in periods_tok)
+def cpu_baseline(w, warm_tok, periods_tok, head_bits, workers):
+    """Time the float64 oracle over the whole batch (all sequences and heads)
+    for the given periods, the batch split across `workers` processes with
+    one BLAS thread each (fresh interpreters: none inherits the parent's GPU
+    context).  The value is batch x tokens over the slowest worker's time."""
+    import multiprocessing as mp
+
+    import numpy as np
+
+    def f64(tok, name, b0, b1):
+        a = getattr(tok, name)[:, b0:b1]
+        if name in ("q", "k", "v") and tok.dtype == inputs.DT_BF16:
+            a = inputs.bf16_to_f32(a)
+        a = a.astype(np.float64)
+        return a.reshape((a.shape[0], (b1 - b0) * w.H) + a.shape[3:])
+
+    def arrays(tok, b0, b1):
+        return [f64(tok, x, b0, b1) for x in ("q", "k", "v", "alpha", "beta")]
+
+    ctx = mp.get_context("spawn")
+    workers = max(1, min(workers, w.B))
+    barrier, results = ctx.Barrier(workers, timeout=1800), ctx.Queue()
+    cuts = np.linspace(0, w.B, workers + 1).astype(int)
+    procs = []
+    for i in range(workers):
+        b0, b1 = int(cuts[i]), int(cuts[i + 1])
+        args = (w.dk, w.dv, w.H, list(map(int, head_bits)), arrays(warm_tok, b0, b1),
+                [arrays(t, b0, b1) for t in periods_tok], barrier, results)
+        p = ctx.Process(target=_oracle_shard, args=(args,))
+        p.start()
+        procs.append(p)
+    import queue as _queue
+    times = []
     try:
-        cpu = next((l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
-                    if l.startswith("model name")), platform.processor())
-    except OSError:
-        cpu = platform.processor()
-    return {"value": n_seq * n_tok / dt, "unit": "token-steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_seq} of {w.B} sequences x {w.H} heads, {len(periods_tok)} periods "
-                      f"of {w.period} tokens ({n_tok} decode steps), float64 numpy, "
-                      f"{dt:.1f} s on one core ({cpu})",
+        while len(times) < len(procs):
+            try:
+                times.append(results.get(timeout=2.0))
+            except _queue.Empty:
+                dead = [p.exitcode for p in procs if p.exitcode not in (None, 0)]
+                if dead:
+                    raise RuntimeError(f"CPU baseline worker exited with {dead[0]}")
+    finally:
+        for p in procs:
+            if p.exitcode is None and len(times) < len(procs):
+                p.terminate()
+            p.join()
+    dt = max(times)
+    n_tok = sum(t.T for t in periods_tok)
+    return {"value": w.B * n_tok / dt, "unit": "token-steps/s", "cores": workers, "kind": "oracle",
+            "sample": f"all {w.B} sequences x {w.H} heads, {len(periods_tok)} period(s) of "
+                      f"{periods_tok[0].T} tokens ({n_tok} decode steps), float64 numpy oracle, "
+                      f"{workers} processes x 1 BLAS thread, {dt:.1f} s for the slowest shard "
+                      f"({_cpu_model()}); warm-up and initial encode untimed",
             "seconds": dt}
 
 
@@ -186,6 +284,26 @@ def prefill_bytes(w: inputs.Workload, n_tok: int, head_bits) -> int:
     return w.B * (2 * state + n_tok * per_tok)
 
 
+def device_prompt(tok, T: int):
+    """The generated prompt tokens `tok` (D of them) repeated on the device to
+    a prompt of T tokens [T, B, H, d]."""
+    import torch
+
+    from linear_attn_decode_pace_amd import runtime
+
+    small = runtime.DeviceTokens(tok)
+    D = small.T
+    big = runtime.DeviceTokens.__new__(runtime.DeviceTokens)
+    for name in ("q", "k", "v", "alpha", "beta"):
+        x = getattr(small, name)
+        y = torch.empty((T,) + tuple(x.shape[1:]), dtype=x.dtype, device="cuda")
+        for t0 in range(0, T, D):
+            y[t0:t0 + D].copy_(x[:min(D, T - t0)])
+        setattr(big, name, y)
+    big.T = T
+    return big
+
+
 def bench_prefill(args) -> int:
     """Time pace_prefill_encode over whole prompts (the hand-off workload)."""
     import torch
@@ -207,16 +325,7 @@ def bench_prefill(args) -> int:
                       args.workers)
     log(f"generated {D} distinct prompt tokens in {time.time() - t:.1f} s")
     # device prompt [T, B, H, d]: the D generated tokens repeated to length T
-    small = runtime.DeviceTokens(inputs.concat(blocks))
-    big = runtime.DeviceTokens.__new__(runtime.DeviceTokens)
-    for name in ("q", "k", "v", "alpha", "beta"):
-        x = getattr(small, name)
-        y = torch.empty((T,) + tuple(x.shape[1:]), dtype=x.dtype, device="cuda")
-        for t0 in range(0, T, D):
-            y[t0:t0 + D].copy_(x[:min(D, T - t0)])
-        setattr(big, name, y)
-    big.T = T
-    del small
+    big = device_prompt(inputs.concat(blocks), T)
     out = runtime.out_buffer(w, T)
     st = runtime.State(w, head_bits, pace.PACE_INIT_ZERO)
     torch.cuda.synchronize()
@@ -238,7 +347,7 @@ def bench_prefill(args) -> int:
         "metric": "prefill prompt tokens/s into the quantized state (seqs x prompt tokens)",
         "value": w.B * T / (ms * 1e-3), "unit": "token-steps/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "vs_baseline": None, "dtype": ARITHMETIC_DTYPE, "data": "synthetic",
         "config": {"workload": w.name, "mode": "prefill", "batch": w.B, "heads": w.H,
                    "d_k": w.dk, "d_v": w.dv, "prompt_tokens": T, "distinct_prompt_tokens": D,
                    "heads_int8": int((head_bits == 8).sum()), "inputs": w.dtype},
@@ -273,12 +382,15 @@ def main() -> int:
     ap.add_argument("--period", type=int, default=None, help="override the workload's period")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--ring", type=int, default=4, help="distinct input periods resident in HBM")
-    ap.add_argument("--cpu-seqs", type=int, default=512)
-    ap.add_argument("--cpu-periods", type=int, default=4)
+    ap.add_argument("--cpu-periods", type=int, default=2,
+                    help="periods of the whole batch the CPU oracle baseline is timed on")
+    ap.add_argument("--cpu-workers", type=int, default=min(16, len(os.sched_getaffinity(0))),
+                    help="processes of the CPU baseline (one BLAS thread each)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workers", type=int, default=min(16, len(os.sched_getaffinity(0))))
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run a plain 1 GiB device-to-device copy (profiler traffic calibration)")
+    ap.add_argument("--copy-bytes", type=int, default=2 << 30,
+                    help="bytes of the device-to-device copy timed after the decode region "
+                         "(attainable-bandwidth reference; 0 skips it)")
     args = ap.parse_args()
 
     if args.mode == "prefill":
@@ -302,27 +414,48 @@ def main() -> int:
 
     t = time.time()
     ring_n = max(1, args.ring)
-    # starting state: the warm-up tokens, or for a prompt workload the first
-    # PROMPT_HEAD prompt tokens (decode throughput depends on the state's
-    # shape, not its values, so the full prompt is not replayed here)
-    warm = (inputs.SEG_PROMPT, 0, min(w.prompt, PROMPT_HEAD)) if w.prompt else \
-        (inputs.SEG_WARMUP, 0, w.warmup)
-    jobs = [warm] + [(inputs.SEG_DECODE, p * C, (p + 1) * C) for p in range(ring_n)]
+    # starting state: the workload's warm-up tokens from zero, or for a prompt
+    # workload the hand-off of its whole prompt (the first `prompt_distinct`
+    # generated prompt tokens repeated to the prompt's length on the device)
+    # through pace_prefill_encode
+    if w.prompt:
+        D = min(w.prompt, args.prompt_distinct)
+        warm_jobs = [(inputs.SEG_PROMPT, t0, min(D, t0 + 64)) for t0 in range(0, D, 64)]
+    else:
+        warm_jobs = [(inputs.SEG_WARMUP, 0, w.warmup)]
+    jobs = warm_jobs + [(inputs.SEG_DECODE, p * C, (p + 1) * C) for p in range(ring_n)]
     toks = generate(w, args.seed, jobs, args.workers)
-    warm_tok, ring_tok = toks[0], toks[1:]
+    warm_tok, ring_tok = inputs.concat(toks[:len(warm_jobs)]), toks[len(warm_jobs):]
     log(f"generated inputs in {time.time() - t:.1f} s")
 
-    M0 = torch.zeros((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
-    runtime.prefill(w, runtime.DeviceTokens(warm_tok), M0)
     step_mode = args.mode in ("step", "window")
     window_mode = args.mode == "window"
     adaptive = step_mode and args.adapt_tau > 0
     flags = (pace.PACE_STEP_BUFFER if step_mode and not window_mode else 0) | \
         (pace.PACE_ADAPTIVE if adaptive else 0) | (pace.PACE_FP8_WINDOW if window_mode else 0)
-    st = runtime.State(w, head_bits, pace.PACE_INIT_F32, M0, flags=flags,
-                       adapt_tau=args.adapt_tau if adaptive else 0.0,
-                       fp8_window=args.fp8_window if window_mode else 0)
-    del M0
+    kw = dict(flags=flags, adapt_tau=args.adapt_tau if adaptive else 0.0,
+              fp8_window=args.fp8_window if window_mode else 0)
+    if w.prompt:
+        h0 = runtime.State(w, head_bits, pace.PACE_INIT_ZERO)
+        big = device_prompt(warm_tok, w.prompt)
+        h0.prefill(big)
+        del big
+        raw = h0.read_raw()
+        h0.free()
+        st = runtime.State(w, head_bits, pace.PACE_INIT_RAW, raw, **kw)
+        del raw
+        start_state = (f"hand-off of a {w.prompt}-token prompt ({D} distinct generated tokens "
+                       f"repeated) through pace_prefill_encode")
+        # the CPU oracle starts from a short prompt prefix instead: the cost of
+        # a decode period does not depend on the state's values
+        cpu_warm = warm_tok.slice(0, min(D, PROMPT_HEAD))
+    else:
+        M0 = torch.zeros((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+        runtime.prefill(w, runtime.DeviceTokens(warm_tok), M0)
+        st = runtime.State(w, head_bits, pace.PACE_INIT_F32, M0, **kw)
+        del M0
+        start_state = f"{w.warmup} warm-up tokens from zero"
+        cpu_warm = warm_tok
     ring = [runtime.DeviceTokens(tk) for tk in ring_tok]
     if step_mode:   # one token per call: the ring's periods cut into tokens
         ring = [r.slice(t, t + 1) for r in ring for t in range(C)]
@@ -331,14 +464,6 @@ def main() -> int:
     call = st.step if step_mode else st.decode
     torch.cuda.synchronize()
     log(f"state and {ring_n} input periods resident ({sum(r.nbytes for r in ring) / 1e9:.2f} GB)")
-
-    if args.calibrate_copy:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     for i in range(args.warmup):
         call(ring[i % ring_n], out)
@@ -359,8 +484,10 @@ def main() -> int:
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(end)
-    launch_ms = sum(a.elapsed_time(b) for a, b in ev) / K
+    per_launch = [a.elapsed_time(b) for a, b in ev]
+    launch_ms = sum(per_launch) / K
     log(f"timed {K} steps: {total_ms:.3f} ms on the device, {t_wall * 1e3:.1f} ms wall")
+    log("per-launch ms: " + " ".join(f"{x:.4f}" for x in per_launch))
 
     k_eff = None
     adapt_bytes = None
@@ -404,7 +531,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": ARITHMETIC_DTYPE,
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "d_k": w.dk, "d_v": w.dv,
                    "period": C, "heads_int8": int((head_bits == 8).sum()),
@@ -413,20 +540,23 @@ def main() -> int:
                    "adapt_tau": args.adapt_tau if adaptive else None,
                    "fp8_window": args.fp8_window if window_mode else None,
                    "mean_period": k_eff,
-                   "input_ring_calls": ring_n,
-                   "start_state": f"{warm[2]} {'prompt' if w.prompt else 'warm-up'} tokens from zero"},
+                   "input_ring_calls": ring_n, "arithmetic": ARITHMETIC,
+                   "start_state": start_state},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS,
                      "traffic": None if step_mode else traffic_from_profile(w.name, sha, nbytes),
                      "algorithmic_bytes_per_launch": nbytes, "launch_ms": launch_ms,
+                     "launch_ms_min": min(per_launch),
+                     "launch_ms_median": sorted(per_launch)[K // 2],
+                     "launch_ms_max": max(per_launch),
                      "kernel_sha": sha},
     }
     st.free()
     del ring, out
+    res["copy_calibration"] = copy_calibration(args.copy_bytes) if args.copy_bytes else None
     if not args.no_cpu_baseline:
-        n_seq = min(args.cpu_seqs, w.B)
-        cb = cpu_baseline(w, args.seed, warm_tok, ring_tok[:max(1, args.cpu_periods)],
-                          head_bits, n_seq)
+        cb = cpu_baseline(w, cpu_warm, ring_tok[:max(1, args.cpu_periods)], head_bits,
+                          args.cpu_workers)
         res["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
     else:
         res["cpu_baseline"] = None

@@ -258,3 +258,75 @@ def test_prompt_handoff_reduced_batch():
     # hand-off state: float32 chunk-free prefill vs float64, 2e-3 relative L2
     run_case(w, seed, default_calls(w), sample=idx, workers=WORKERS, M0_gpu=M, M0_ref=Mr,
              label="prefill-b8-handoff", warm_rel=2e-3)
+
+
+def test_prompt_handoff_full_batch_then_decode():
+    # the prompt workload end to end at its full size: 512 prompts x 32 heads
+    # (8 at 8 bits) of 4096 tokens through pace_prefill_encode into the
+    # quantized state (the prompt is 64 distinct generated tokens repeated on
+    # the device), then two period-16 decode calls from that stored state;
+    # the hand-off and every decode transition checked on 32+ sampled tiles
+    import torch
+
+    from linear_attn_decode_pace_amd import pace, runtime
+    from oracle import pace as opace
+    from tests import parity
+    from tests.gpu_cases import tok_tiles
+
+    w = inputs.PREFILL
+    T, D, seed = w.prompt, 64, 0
+    n = w.B * w.H
+    bits = inputs.head_bits(w, seed)
+    idx = _sample(w, seed, 32)
+    bits_t = np.tile(bits, w.B)[idx].astype(np.int64)
+    tix = torch.as_tensor(idx, device="cuda")
+    say(f"[case] prefill-b512 hand-off + decode: {T}-token prompts ({D} distinct), {len(idx)} tiles")
+    tok = inputs.concat(inputs.iter_tokens(
+        w, seed, inputs.SEG_PROMPT, [(t, t + inputs.TB) for t in range(0, D, inputs.TB)], WORKERS))
+    small = runtime.DeviceTokens(tok)
+    big = runtime.DeviceTokens.__new__(runtime.DeviceTokens)
+    for name in ("q", "k", "v", "alpha", "beta"):
+        x = getattr(small, name)
+        y = torch.empty((T,) + tuple(x.shape[1:]), dtype=x.dtype, device="cuda")
+        for t0 in range(0, T, D):
+            y[t0:t0 + D].copy_(x)
+        setattr(big, name, y)
+    big.T = T
+    del small
+    st = runtime.State(w, bits, pace.PACE_INIT_ZERO)
+    st.prefill(big)
+    del big
+
+    def read():
+        c, s = st.read_codes()
+        return (c.reshape(n, w.dk, w.dv)[tix].cpu().numpy(), s.reshape(n, w.dv)[tix].cpu().numpy())
+
+    codes, scales = read()
+    q, k, v, a, b = [np.tile(x, (T // D,) + (1,) * (x.ndim - 1)) for x in tok_tiles(tok, idx, w.H)]
+    zc = np.zeros((len(idx), w.dk, w.dv), dtype=np.int64)
+    zs = np.zeros((len(idx), w.dv), dtype=np.float32)
+    _, rc, rs, Mpre = opace.period(zc, zs, bits_t, q, k, v, a, b)
+    del q, k, v, a, b
+    rep = parity.check_encoded(codes, scales, rc, rs, Mpre, f"prefill-b512 hand-off of {T} tokens")
+    fc, fs = rc, rs   # free-running oracle from its own hand-off
+    diverged = np.any(codes.astype(np.int16) != fc, axis=(1, 2))
+    calls = default_calls(w, 2)
+    for ci, dtok in enumerate(inputs.iter_tokens(w, seed, inputs.SEG_DECODE, calls, WORKERS)):
+        out = runtime.out_buffer(w, dtok.T)
+        st.decode(runtime.DeviceTokens(dtok), out)
+        o = out.reshape(dtok.T, n, w.dv)[:, tix].cpu().numpy()
+        nc, ns = read()
+        args = tok_tiles(dtok, idx, w.H)
+        what = f"prefill-b512 decode call {ci} after the hand-off"
+        O, c2, s2, M2 = opace.period(codes, scales, bits_t, *args)
+        parity.check_outputs(o, O, what)
+        rep = rep.merge(parity.check_encoded(nc, ns, c2, s2, M2, what))
+        Of, fc, fs, Mf = opace.period(fc, fs, bits_t, *args)
+        live = ~diverged
+        if live.any():
+            parity.check_outputs(o[:, live], Of[:, live], what + " (free-running)")
+        diverged |= np.any(nc.astype(np.int16) != fc, axis=(1, 2))
+        codes, scales = nc, ns
+    st.free()
+    say(f"[case] prefill-b512 hand-off + decode: ok, {rep.flips} tie flips, "
+        f"{int(diverged.sum())} tiles diverged by a tie")
