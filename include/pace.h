@@ -308,6 +308,23 @@ int pace_read_state(const pace_state *st, int what, void *dst, float *scales_dst
 int pace_quant_stats(const pace_state *st, pace_stats *out, void *stream);
 
 /*
+ * For callers that cannot allocate device memory at the call (code that must
+ * not call hipMalloc, tight serving loops, harnesses that forbid it): the
+ * same result as pace_quant_stats, but its device scratch (the zero-column
+ * counter and the per-head float64 error sums) lives in a fixed array the
+ * library holds on each device until the process ends (8 + 2 * 256 * 8
+ * bytes: error sums of at most PACE_STATS_MAX_HEADS heads) instead of the
+ * handle's buffers.  Nothing is allocated: no hipMalloc, hipFree or
+ * allocating library routine.  The first call on a device looks the array's
+ * address up once.  Every call on one device shares that array: calls that
+ * overlap on one device (other host threads, other streams) race and must
+ * be ordered by the caller.  Waits for `stream`, like pace_quant_stats.
+ * Errors: EINVAL (null argument; an error-tracking handle with more heads
+ *         than the array holds), EDEVICE.
+ */
+int pace_quant_stats_static(const pace_state *st, pace_stats *out, void *stream);
+
+/*
  * Prefill hand-off: apply a prompt of n_tok tokens (any n_tok >= 1) to every
  * stored state and encode once at the end, i.e. one period of n_tok tokens
  * (the stored state decoded -- zero after PACE_INIT_ZERO --, the tokens

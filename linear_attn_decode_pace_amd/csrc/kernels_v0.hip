@@ -11,6 +11,8 @@
 // A thread owns one column j of one (sequence, head) state, so every code
 // byte it reads or writes belongs to its column only (see pace_layout.h) and
 // decode can update the pool in place without synchronisation between threads.
+#include <mutex>
+
 #include "column_codec.h"
 #include "pace_step.h"
 
@@ -345,6 +347,39 @@ hipError_t launch_read(const PoolView &p, int what, void *dst, float *scales_dst
     else
         hipLaunchKernelGGL(read_kernel<64>, grid, block, 0, s, p, what, dst, scales_dst);
     return hipGetLastError();
+}
+
+// Scratch of the statistics entry point that allocates nothing (for callers
+// that cannot allocate device memory): word 0 counts zero columns, words
+// 1 .. 2 * STATS_SCRATCH_HEADS hold the per-head float64 error sums.  One copy
+// per device, held until the process ends; calls that overlap on one device
+// share it and race.
+static __device__ __align__(256) unsigned long long scratch[1 + 2 * STATS_SCRATCH_HEADS];
+
+hipError_t stats_scratch(int device, unsigned long long **out) {
+    // in host code `scratch` names a host-side stand-in: the device address of
+    // each device's copy is looked up once, with that device current
+    constexpr int MAX_DEVICES = 64;
+    static std::mutex mu;
+    static unsigned long long *addr[MAX_DEVICES] = {};
+    if (device < 0 || device >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[device]) {
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != device) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        addr[device] = (unsigned long long *)p;
+    }
+    *out = addr[device];
+    return hipSuccess;
 }
 
 hipError_t launch_count_zero_scales(const PoolView &p, unsigned long long *counter,

@@ -502,9 +502,14 @@ PACE_API int pace_read_state(const pace_state *st, int what, void *dst, float *s
     return ok();
 }
 
-PACE_API int pace_quant_stats(const pace_state *st, pace_stats *out, void *stream) {
-    if (!st || !out) return fail(PACE_EINVAL, "null argument");
-    hipStream_t s = (hipStream_t)stream;
+namespace {
+
+// Storage accounting plus the device reductions of pace_quant_stats, with the
+// zero-column counter and the per-head error sums in `counter` / `sums`
+// (device memory, sums holding 2 doubles per head).  Host memory is a fixed
+// array: nothing is allocated here.
+int quant_stats(const pace_state *st, pace_stats *out, hipStream_t s, unsigned long long *counter,
+                double *sums, const char *what) {
     const pace_config &c = st->cfg;
     pace_stats r = {};
     r.bytes_codes4 = st->bytes4;
@@ -518,20 +523,17 @@ PACE_API int pace_quant_stats(const pace_state *st, pace_stats *out, void *strea
     r.periods = st->periods;
     r.tokens = st->tokens;
     unsigned long long zeros = 0;
-    hipError_t e = hipMemsetAsync(st->d_counter, 0, sizeof zeros, s);
-    if (e == hipSuccess) e = pace::launch_count_zero_scales(st->view(), st->d_counter, s);
-    if (e == hipSuccess)
-        e = hipMemcpyAsync(&zeros, st->d_counter, sizeof zeros, hipMemcpyDeviceToHost, s);
-    std::vector<double> err;
+    double err[2 * PACE_STATS_MAX_HEADS];
+    hipError_t e = hipMemsetAsync(counter, 0, sizeof zeros, s);
+    if (e == hipSuccess) e = pace::launch_count_zero_scales(st->view(), counter, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(&zeros, counter, sizeof zeros, hipMemcpyDeviceToHost, s);
     if (st->colerr) {
-        err.resize(2 * (size_t)c.heads);
-        if (e == hipSuccess) e = pace::launch_reduce_colerr(st->view(), st->d_err, s);
+        if (e == hipSuccess) e = pace::launch_reduce_colerr(st->view(), sums, s);
         if (e == hipSuccess)
-            e = hipMemcpyAsync(err.data(), st->d_err, sizeof(double) * err.size(),
-                               hipMemcpyDeviceToHost, s);
+            e = hipMemcpyAsync(err, sums, sizeof(double) * 2 * c.heads, hipMemcpyDeviceToHost, s);
     }
     if (e == hipSuccess) e = hipStreamSynchronize(s);
-    if (e != hipSuccess) return hip_fail(e, "quant_stats");
+    if (e != hipSuccess) return hip_fail(e, what);
     r.zero_columns = zeros;
     r.bytes_step_buffer = st->bytes_step;
     if (st->colerr) {
@@ -543,6 +545,26 @@ PACE_API int pace_quant_stats(const pace_state *st, pace_stats *out, void *strea
     }
     *out = r;
     return ok();
+}
+
+}  // namespace
+
+PACE_API int pace_quant_stats(const pace_state *st, pace_stats *out, void *stream) {
+    if (!st || !out) return fail(PACE_EINVAL, "null argument");
+    return quant_stats(st, out, (hipStream_t)stream, st->d_counter, st->d_err, "quant_stats");
+}
+
+PACE_API int pace_quant_stats_static(const pace_state *st, pace_stats *out, void *stream) {
+    if (!st || !out) return fail(PACE_EINVAL, "null argument");
+    static_assert(pace::STATS_SCRATCH_HEADS == PACE_STATS_MAX_HEADS, "scratch holds every tracked head");
+    if (st->colerr && st->cfg.heads > pace::STATS_SCRATCH_HEADS)
+        return fail(PACE_EINVAL, "pace_quant_stats_static sums errors of at most %d heads (handle has %d)",
+                    pace::STATS_SCRATCH_HEADS, st->cfg.heads);
+    unsigned long long *scratch = nullptr;
+    hipError_t e = pace::stats_scratch(st->device, &scratch);
+    if (e != hipSuccess) return hip_fail(e, "quant_stats_static scratch");
+    return quant_stats(st, out, (hipStream_t)stream, scratch, (double *)(scratch + 1),
+                       "quant_stats_static");
 }
 
 PACE_API int pace_stream_copy(void *dst, const void *src, uint64_t bytes, void *stream) {

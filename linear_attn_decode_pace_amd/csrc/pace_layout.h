@@ -86,6 +86,11 @@ hipError_t launch_count_zero_scales(const PoolView &p, unsigned long long *count
                                     hipStream_t s);
 // streaming copy of `bytes` (a multiple of 16) between 16-byte aligned buffers
 hipError_t launch_stream_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
+// heads the statistics scratch of the allocation-free stats entry point holds
+constexpr int STATS_SCRATCH_HEADS = 256;
+// device address of that scratch on `device` (looked up once per device): a
+// zero-column counter, then 2 * STATS_SCRATCH_HEADS float64 error sums
+hipError_t stats_scratch(int device, unsigned long long **out);
 // per head h: out[2 h] = sum of colerr[b, h, j, 0], out[2 h + 1] = sum of
 // colerr[b, h, j, 1] over b and j, in float64
 hipError_t launch_reduce_colerr(const PoolView &p, double *out, hipStream_t s);

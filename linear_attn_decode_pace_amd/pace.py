@@ -47,7 +47,7 @@ PACE_STATS_MAX_HEADS = 256
 EXPORTED = ("pace_abi_version", "pace_last_error", "pace_state_alloc", "pace_state_free",
             "pace_state_config", "pace_raw_bytes", "pace_decode_period", "pace_read_state",
             "pace_quant_stats", "pace_prefill_f32", "pace_decode_step", "pace_flush_steps",
-            "pace_prefill_encode", "pace_stream_copy")
+            "pace_prefill_encode", "pace_stream_copy", "pace_quant_stats_static")
 
 
 class PaceError(RuntimeError):
@@ -109,6 +109,7 @@ def _load():
         "pace_flush_steps": ([vp, vp], ctypes.c_int),
         "pace_prefill_encode": ([vp, i32, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "pace_stream_copy": ([vp, vp, ctypes.c_uint64, vp], ctypes.c_int),
+        "pace_quant_stats_static": ([vp, ctypes.POINTER(pace_stats), vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -214,6 +215,12 @@ def pace_read_state(st: int, what: int, dst, scales_dst=None, stream=None) -> No
 def pace_quant_stats(st: int, stream=None) -> dict:
     s = pace_stats()
     _check(LIB.pace_quant_stats(st, ctypes.byref(s), _stream(stream)))
+    return s.as_dict(pace_state_config(st)["heads"])
+
+
+def pace_quant_stats_static(st: int, stream=None) -> dict:
+    s = pace_stats()
+    _check(LIB.pace_quant_stats_static(st, ctypes.byref(s), _stream(stream)))
     return s.as_dict(pace_state_config(st)["heads"])
 
 

@@ -113,6 +113,7 @@ def test_null_arguments():
     assert pace.LIB.pace_decode_period(None, 1, 16, 16, 16, 16, 16, 16, None) == pace.PACE_EINVAL
     assert pace.LIB.pace_read_state(None, 0, 16, 16, None) == pace.PACE_EINVAL
     assert pace.LIB.pace_quant_stats(None, None, None) == pace.PACE_EINVAL
+    assert pace.LIB.pace_quant_stats_static(None, None, None) == pace.PACE_EINVAL
     assert pace.LIB.pace_raw_bytes(None, None) == pace.PACE_EINVAL
     assert pace.LIB.pace_decode_step(None, 16, 16, 16, 16, 16, None, 16, None) == pace.PACE_EINVAL
     assert pace.LIB.pace_flush_steps(None, None) == pace.PACE_EINVAL
