@@ -8,8 +8,10 @@
 // Chunks of 32 tokens in the WY / UT form, split into two 16-token halves H1,
 // H2 (one MFMA tile of rows each).  One workgroup per state tile, resident
 // for the whole prompt:
-//   * NCB consumer waves (one per 16-column block) hold the tile's float32
-//     state in registers from the first token to the final encode;
+//   * DK / 32 consumer waves, two 16-column blocks each, hold the tile's
+//     float32 state in registers from the first token to the final encode
+//     (the K, Q, T and Lq operands a chunk reads from LDS serve both blocks,
+//     and the two blocks' dependency chains interleave in one wave);
 //   * two producer waves, on different SIMDs, take alternate chunks.  A
 //     producer copies a chunk's keys, queries, values and gates from HBM
 //     straight into LDS (no registers; whole rows, so every byte fetched is
@@ -70,6 +72,14 @@ __device__ inline void producer_barrier() {
 // whole prompt.
 __device__ inline void launder(int &x) { asm volatile("" : "+v"(x)); }
 
+// Keep memory accesses on their side of this point (the loads above it stay
+// ahead of the work below; their waits are placed at first use)
+__device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// Make y's next uses come after x is computed (an empty asm that reads x and
+// redefines both), so that a register y occupied can be reused in place.
+__device__ inline void order_after(f32x4 &x, f32x4 &y) { asm volatile("" : "+v"(x), "+v"(y)); }
+
 constexpr int CT = 32;      // tokens per chunk
 constexpr int HT = 16;      // tokens per half chunk
 
@@ -124,6 +134,7 @@ struct alignas(16) PrepScratch {
 
 constexpr int NBUF = 4;  // chunk buffers: applied, prepared (B), prepared (A), loading
 constexpr int NPROD = 2; // producer waves
+constexpr int CPW = 2;   // column blocks per consumer wave
 
 template <int DK>
 struct PrefillLds {
@@ -432,7 +443,7 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
                              int wave, int lane) {
     constexpr int NKS = DK / 32;  // k-slices of 32 rows
     constexpr int NRT = DK / 16;  // row tiles of 16 rows
-    constexpr int NCB = DK / 16;  // column blocks = consumer waves
+    constexpr int NCW = DK / 16 / CPW;  // consumer waves
     constexpr float QMAX = BITS == 4 ? 7.f : 127.f;
     constexpr float KAPPA = Loader<DK, BITS>::KAPPA;
     const int g = lane >> 4, n = lane & 15;
@@ -441,8 +452,8 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
     using TokStride = typename std::conditional<WIDE_OFF, size_t, uint32_t>::type;
     const TokStride tok_stride = (TokStride)a.p.B * (TokStride)a.p.H;
     const int n_chunks = (a.n_tok + CT - 1) / CT;
-    const bool producer = wave >= NCB;
-    const int cb = wave, j = 16 * cb + n;
+    const bool producer = wave >= NCW;
+    const int cb0 = CPW * wave;  // a consumer's first column block
 
     uint8_t *codes = BITS == 4
         ? a.p.codes4 + ((size_t)b * a.p.n4 + slot) * tile_code_bytes(DK, DK, 4)
@@ -462,7 +473,7 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
         // interval (long dependent chains through LDS, the forward
         // substitution), so they run at raised wave priority throughout,
         // ahead of the consumers sharing their SIMDs.
-        const int p = wave - NCB;
+        const int p = wave - NCW;
         PrepScratch &ps = L.ps[p];
         auto phase_a = [&](int c) {
             ChunkLds<DK> &N = L.ch[c % NBUF];
@@ -499,53 +510,95 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
         return;
     }
 
-    // the column block's starting state: the stored codes decoded (zero after
+    // the column blocks' starting state: the stored codes decoded (zero after
     // a zero initialisation), in chunk layout
-    f32x4 acc[NRT];
-    {
-        Loader<DK, BITS> ld;
-        ld.load(codes, cb, lane);
-        ld.codes_f32(acc);
-        const float sk = scl[j] * (1.f / KAPPA);
+    f32x4 acc[CPW][NRT];
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) acc[rt] *= sk;
-        to_chunk_layout<NKS>(acc, lane);
+    for (int e = 0; e < CPW; ++e) {
+        Loader<DK, BITS> ld;
+        ld.load(codes, cb0 + e, lane);
+        ld.codes_f32(acc[e]);
+        const float sk = scl[16 * (cb0 + e) + n] * (1.f / KAPPA);
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) acc[e][rt] *= sk;
+        to_chunk_layout<NKS>(acc[e], lane);
     }
 
     lds_barrier();
-    // this wave's 16 rows of a chunk's key table: lane -> (state row, token group)
-    auto build_kt = [&](const ChunkLds<DK> &N, uint16_t (*KT)[32], int ln) {
-        const int i = 16 * wave + (ln >> 2), gg = ln & 3;
-        uint32_t w[4];
+    // this wave's DK / NCW rows of a chunk's key table, 16 per pass: lane ->
+    // (state row, token group)
+    auto build_kt = [&](const ChunkLds<DK> &N, uint16_t (*KT)[32]) {
+        constexpr int ROWS = DK / NCW;
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const int t = HT * hh + 4 * gg;
-            uint32_t e[4];
+        for (int pass = 0; pass < ROWS / 16; ++pass) {
+            const int i = ROWS * wave + 16 * pass + (lane >> 2), gg = lane & 3;
+            uint32_t w[4];
 #pragma unroll
-            for (int x = 0; x < 4; ++x)
-                e[x] = N.kq[t + x][8 * ((i >> 3) ^ kq_swz<DK>(t + x)) + (i & 7)];
-            w[2 * hh] = e[0] | (e[1] << 16);
-            w[2 * hh + 1] = e[2] | (e[3] << 16);
+            for (int hh = 0; hh < 2; ++hh) {
+                const int t = HT * hh + 4 * gg;
+                uint32_t x4[4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    x4[x] = N.kq[t + x][8 * ((i >> 3) ^ kq_swz<DK>(t + x)) + (i & 7)];
+                w[2 * hh] = x4[0] | (x4[1] << 16);
+                w[2 * hh + 1] = x4[2] | (x4[3] << 16);
+            }
+            *(u32x4 *)&KT[i][8 * (gg ^ ((i >> 3) & 3))] = u32x4{w[0], w[1], w[2], w[3]};
         }
-        *(u32x4 *)&KT[i][8 * (gg ^ ((i >> 3) & 3))] = u32x4{w[0], w[1], w[2], w[3]};
     };
-    build_kt(L.ch[0], L.kt[0], lane);
+    build_kt(L.ch[0], L.kt[0]);
     lds_barrier();
+    // A operand rows of P_K: the K blocks' row m is token 4 (m % 4) + m / 4 of
+    // its half, so P_K's row 4 g + r is token 4 r + g (the B layout of the
+    // float32 chunk MFMAs)
+    const int tok_n = 4 * (n & 3) + (n >> 2);
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     for (int c = 0; c < n_chunks; ++c) {
-        const int ln = lane;
-        // A operand rows: the K blocks' row m is token 4 (m % 4) + m / 4 of
-        // its half, so P_K's row 4 g + r is token 4 r + g (the B layout of the
-        // float32 chunk MFMAs)
-        const int tok_n = 4 * (n & 3) + (n >> 2);
         const ChunkLds<DK> &C = L.ch[c % NBUF];
         const uint16_t(*KT)[32] = L.kt[c & 1];
-        if (c + 1 < n_chunks) build_kt(L.ch[(c + 1) % NBUF], L.kt[(c + 1) & 1], ln);
+        if (c + 1 < n_chunks) build_kt(L.ch[(c + 1) % NBUF], L.kt[(c + 1) & 1]);
+        // Operands of the X and Y stages, read before the P stage so that
+        // their LDS latency hides behind it: the values v (tokens 4 r + g and
+        // 16 + 4 r + g of column 16 cb + n: vv[e][r] and vv[e][4 + r]),
+        // gamma and G' of the lane's tokens, and its entries of T11, A21t, T22
+        uint16_t vv[CPW][8];
+        float gk1[4], gk2[4], t11[4], a21[4], t22[4];
+        f32x4 gp1, gp2;
+        {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                gk1[r] = C.gam[4 * r + g];
+                gk2[r] = C.gam[HT + 4 * r + g];
+                t11[r] = C.Tt[0][4 * r + g][n];
+                a21[r] = C.A21t[4 * g + r][n];
+                t22[r] = C.Tt[1][4 * r + g][n];
+            }
+            gp1 = *(const f32x4 *)&C.gp[4 * g];
+            gp2 = *(const f32x4 *)&C.gp[HT + 4 * g];
+#pragma unroll
+            for (int e = 0; e < CPW; ++e) {
+                const uint16_t *vl = &C.v[g][8 * ((2 * (cb0 + e) + (n >> 3)) ^ v_swz(g)) + (n & 7)];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    vv[e][r] = vl[4 * r * DK];
+                    vv[e][4 + r] = vl[(HT + 4 * r) * DK];
+                }
+            }
+            compiler_fence();
+        }
         // P_K = K M0 and, transposed, P_Q^T = M0^T Q^T over two bf16 parts of
         // M0 (hi + mid, 16 significant bits; a third part for P_K cost 8 more
         // MFMAs per chunk and 5% of the time without moving a code), both
         // halves of the chunk; k-slot 8 g + e is state row 32 ks + 8 g + e.
-        // P_Q^T's lane (g, n) holds P_Q[token n][column 16 cb + 4 g + r].
-        f32x4 PK1 = {0.f, 0.f, 0.f, 0.f}, PK2 = PK1, PQ1 = PK1, PQ2 = PK1;
+        // The K and Q operands serve both column blocks.  P_Q^T's lane (g, n)
+        // holds P_Q[token n][column 16 cb + 4 g + r].
+        // The gated state gamma_C M of the update (M <- gamma_C M + K^T W) is
+        // taken as each slice is split, so the split consumes the old values
+        // in place (no copies).
+        const float gC = C.gam[CT - 1];
+        f32x4 PK1[CPW], PK2[CPW], PQ1[CPW], PQ2[CPW];
+#pragma unroll
+        for (int e = 0; e < CPW; ++e) PK1[e] = PK2[e] = PQ1[e] = PQ2[e] = zero;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const int pc = 4 * ks + g;
@@ -553,125 +606,162 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
             const bf16x8 AK2 = __builtin_bit_cast(bf16x8, kq_piece<DK>(C.kq, HT + tok_n, pc));
             const bf16x8 AQ1 = __builtin_bit_cast(bf16x8, kq_piece<DK>(C.kq, CT + n, pc));
             const bf16x8 AQ2 = __builtin_bit_cast(bf16x8, kq_piece<DK>(C.kq, CT + HT + n, pc));
-            uint32_t h0[2], m0[2], h1[2], m1[2];
-            split2(acc[2 * ks], h0, m0);
-            split2(acc[2 * ks + 1], h1, m1);
-            const bf16x8 BH = __builtin_bit_cast(bf16x8, u32x4{h0[0], h0[1], h1[0], h1[1]});
-            const bf16x8 BM = __builtin_bit_cast(bf16x8, u32x4{m0[0], m0[1], m1[0], m1[1]});
-            PK1 = mfma_bf16_k32(AK1, BH, PK1);
-            PK2 = mfma_bf16_k32(AK2, BH, PK2);
-            PQ1 = mfma_bf16_k32(BH, AQ1, PQ1);
-            PQ2 = mfma_bf16_k32(BH, AQ2, PQ2);
-            PK1 = mfma_bf16_k32(AK1, BM, PK1);
-            PK2 = mfma_bf16_k32(AK2, BM, PK2);
-            PQ1 = mfma_bf16_k32(BM, AQ1, PQ1);
-            PQ2 = mfma_bf16_k32(BM, AQ2, PQ2);
-        }
-        // X for tokens 4 r + g and 16 + 4 r + g (the P_K rows this lane
-        // holds), column j; those value rows keep piece 2 cb + n / 8 in slot
-        // (2 cb + n / 8) ^ 2 g
-        float X1[4], X2[4];
-        {
-            const uint16_t *vl = &C.v[g][8 * ((2 * cb + (n >> 3)) ^ v_swz(g)) + (n & 7)];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                X1[r] = fmaf(-C.gam[4 * r + g], PK1[r], bf2f(vl[4 * r * DK]));
-                X2[r] = fmaf(-C.gam[HT + 4 * r + g], PK2[r], bf2f(vl[(HT + 4 * r) * DK]));
+            for (int e = 0; e < CPW; ++e) {
+                uint32_t h0[2], m0[2], h1[2], m1[2];
+                f32x4 x0 = acc[e][2 * ks], x1 = acc[e][2 * ks + 1];
+                acc[e][2 * ks] *= gC;
+                acc[e][2 * ks + 1] *= gC;
+                // the gated copies exist before the split, which then consumes
+                // x0 and x1 in place
+                order_after(acc[e][2 * ks], x0);
+                order_after(acc[e][2 * ks + 1], x1);
+                split2(x0, h0, m0);
+                split2(x1, h1, m1);
+                const bf16x8 BH = __builtin_bit_cast(bf16x8, u32x4{h0[0], h0[1], h1[0], h1[1]});
+                const bf16x8 BM = __builtin_bit_cast(bf16x8, u32x4{m0[0], m0[1], m1[0], m1[1]});
+                PK1[e] = mfma_bf16_k32(AK1, BH, PK1[e]);
+                PK2[e] = mfma_bf16_k32(AK2, BH, PK2[e]);
+                PQ1[e] = mfma_bf16_k32(BH, AQ1, PQ1[e]);
+                PQ2[e] = mfma_bf16_k32(BH, AQ2, PQ2[e]);
+                PK1[e] = mfma_bf16_k32(AK1, BM, PK1[e]);
+                PK2[e] = mfma_bf16_k32(AK2, BM, PK2[e]);
+                PQ1[e] = mfma_bf16_k32(BM, AQ1, PQ1[e]);
+                PQ2[e] = mfma_bf16_k32(BM, AQ2, PQ2[e]);
             }
         }
+        // X for tokens 4 r + g and 16 + 4 r + g (the P_K rows this lane
+        // holds), column 16 cb + n
+        float X1[CPW][4], X2[CPW][4];
+#pragma unroll
+        for (int e = 0; e < CPW; ++e)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                X1[e][r] = fmaf(-gk1[r], PK1[e][r], bf2f(vv[e][r]));
+                X2[e][r] = fmaf(-gk2[r], PK2[e][r], bf2f(vv[e][4 + r]));
+            }
         // W = diag(G') T X with T = [T11 0; T21 T22], T21 = -T22 A21 T11:
         // Y1 = T11 X1, X2' = X2 - A21 Y1, Y2 = T22 X2', W = diag(G') [Y1; Y2]
         // (float32 MFMA: the state needs its accuracy).  Y1 and Y2 come out
         // in natural row order (lane (g, n): token 4 g + r of the half)
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        f32x4 Y1 = zero, D21 = zero, Y2 = zero;
+        f32x4 Y1[CPW], D21[CPW], Y2[CPW];
 #pragma unroll
-        for (int st = 0; st < 4; ++st) Y1 = mfma_f32_k4(C.Tt[0][4 * st + g][n], X1[st], Y1);
+        for (int e = 0; e < CPW; ++e) Y1[e] = D21[e] = Y2[e] = zero;
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int e = 0; e < CPW; ++e) Y1[e] = mfma_f32_k4(t11[st], X1[e][st], Y1[e]);
         // step st takes Y1's own row 4 g + st; A21t's row order puts the
         // product in X2's layout (token 16 + 4 r + g)
 #pragma unroll
-        for (int st = 0; st < 4; ++st) D21 = mfma_f32_k4(C.A21t[4 * g + st][n], Y1[st], D21);
+        for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) X2[r] -= D21[r];
+            for (int e = 0; e < CPW; ++e) D21[e] = mfma_f32_k4(a21[st], Y1[e][st], D21[e]);
 #pragma unroll
-        for (int st = 0; st < 4; ++st) Y2 = mfma_f32_k4(C.Tt[1][4 * st + g][n], X2[st], Y2);
-        f32x4 W1, W2;
+        for (int e = 0; e < CPW; ++e)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) X2[e][r] -= D21[e][r];
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int e = 0; e < CPW; ++e) Y2[e] = mfma_f32_k4(t22[st], X2[e][st], Y2[e]);
+        f32x4 W1[CPW], W2[CPW];
         {
-            const f32x4 gp1 = *(const f32x4 *)&C.gp[4 * g], gp2 = *(const f32x4 *)&C.gp[HT + 4 * g];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                W1[r] = gp1[r] * Y1[r];
-                W2[r] = gp2[r] * Y2[r];
-            }
+            for (int e = 0; e < CPW; ++e)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    W1[e][r] = gp1[r] * Y1[e][r];
+                    W2[e][r] = gp2[r] * Y2[e][r];
+                }
         }
+        // key rows of the update, read ahead of the output stage
+        u32x4 ktr[NRT];
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+            const int R = chunk_row(rt, n);
+            ktr[rt] = *(const u32x4 *)&KT[R][8 * (g ^ ((R >> 3) & 3))];
+        }
+        compiler_fence();
         // (Lq T X)^T = ([Lq11 Y1; Lq21 Y1 + Lq22 Y2])^T on bf16 MFMA, Y and Lq
         // in two parts each (hi hi, hi mid, mid hi: ~1e-5 relative error,
-        // outputs only); the lane's k-slots are its own tokens 4 g + e
-        uint32_t yh[4], ym[4];
-        split2(Y1, yh, ym);
-        split2(Y2, yh + 2, ym + 2);
-        const s16x4 B1h = __builtin_bit_cast(s16x4, u32x2{yh[0], yh[1]});
-        const s16x4 B1m = __builtin_bit_cast(s16x4, u32x2{ym[0], ym[1]});
-        const bf16x8 B2h = __builtin_bit_cast(bf16x8, u32x4{yh[0], yh[1], yh[2], yh[3]});
-        const bf16x8 B2m = __builtin_bit_cast(bf16x8, u32x4{ym[0], ym[1], ym[2], ym[3]});
-        const s16x4 A1h = __builtin_bit_cast(s16x4, *(const u32x2 *)&C.LqB1[0][n][4 * g]);
-        const s16x4 A1m = __builtin_bit_cast(s16x4, *(const u32x2 *)&C.LqB1[1][n][4 * g]);
-        const bf16x8 A2h = __builtin_bit_cast(bf16x8, *(const u32x4 *)&C.LqB2[0][n][8 * g]);
-        const bf16x8 A2m = __builtin_bit_cast(bf16x8, *(const u32x4 *)&C.LqB2[1][n][8 * g]);
-        f32x4 O1 = mfma_bf16_k16(B1h, A1h, zero);
-        f32x4 O2 = mfma_bf16_k32(B2h, A2h, zero);
-        O1 = mfma_bf16_k16(B1m, A1h, O1);
-        O2 = mfma_bf16_k32(B2m, A2h, O2);
-        O1 = mfma_bf16_k16(B1h, A1m, O1);
-        O2 = mfma_bf16_k32(B2h, A2m, O2);
+        // outputs only); the lane's k-slots are its own tokens 4 g + e.  Then
         // O^T += (diag(gamma) Q M0)^T: this lane's outputs are token n (first
         // half) and 16 + n (second half), columns 16 cb + 4 g .. 16 cb + 4 g + 3
-        if (a.out) {
+        {
+            const s16x4 A1h = __builtin_bit_cast(s16x4, *(const u32x2 *)&C.LqB1[0][n][4 * g]);
+            const s16x4 A1m = __builtin_bit_cast(s16x4, *(const u32x2 *)&C.LqB1[1][n][4 * g]);
+            const bf16x8 A2h = __builtin_bit_cast(bf16x8, *(const u32x4 *)&C.LqB2[0][n][8 * g]);
+            const bf16x8 A2m = __builtin_bit_cast(bf16x8, *(const u32x4 *)&C.LqB2[1][n][8 * g]);
             const float gq1 = C.gam[n], gq2 = C.gam[HT + n];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                O1[r] = fmaf(gq1, PQ1[r], O1[r]);
-                O2[r] = fmaf(gq2, PQ2[r], O2[r]);
-            }
             const int nv = a.n_tok - CT * c;  // chunk c's real tokens
             float *obase = a.out + ((size_t)CT * c * tok_stride + tile_row) * DK;
-            const uint32_t x = 16 * cb + 4 * g;
-            if (n < nv) __builtin_nontemporal_store(O1, (f32x4 *)tok_at<WIDE_OFF, DK>(obase, n, a, x));
-            if (HT + n < nv) __builtin_nontemporal_store(O2, (f32x4 *)tok_at<WIDE_OFF, DK>(obase, HT + n, a, x));
+#pragma unroll
+            for (int e = 0; e < CPW; ++e) {
+                uint32_t yh[4], ym[4];
+                split2(Y1[e], yh, ym);
+                split2(Y2[e], yh + 2, ym + 2);
+                const s16x4 B1h = __builtin_bit_cast(s16x4, u32x2{yh[0], yh[1]});
+                const s16x4 B1m = __builtin_bit_cast(s16x4, u32x2{ym[0], ym[1]});
+                const bf16x8 B2h = __builtin_bit_cast(bf16x8, u32x4{yh[0], yh[1], yh[2], yh[3]});
+                const bf16x8 B2m = __builtin_bit_cast(bf16x8, u32x4{ym[0], ym[1], ym[2], ym[3]});
+                f32x4 O1 = mfma_bf16_k16(B1h, A1h, zero);
+                f32x4 O2 = mfma_bf16_k32(B2h, A2h, zero);
+                O1 = mfma_bf16_k16(B1m, A1h, O1);
+                O2 = mfma_bf16_k32(B2m, A2h, O2);
+                O1 = mfma_bf16_k16(B1h, A1m, O1);
+                O2 = mfma_bf16_k32(B2h, A2m, O2);
+                if (a.out) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        O1[r] = fmaf(gq1, PQ1[e][r], O1[r]);
+                        O2[r] = fmaf(gq2, PQ2[e][r], O2[r]);
+                    }
+                    const uint32_t x = 16 * (cb0 + e) + 4 * g;
+                    if (n < nv) __builtin_nontemporal_store(O1, (f32x4 *)tok_at<WIDE_OFF, DK>(obase, n, a, x));
+                    if (HT + n < nv)
+                        __builtin_nontemporal_store(O2, (f32x4 *)tok_at<WIDE_OFF, DK>(obase, HT + n, a, x));
+                }
+            }
         }
 
-        // M <- gamma_C M + K^T W, W in two bf16 parts (hi + mid, relative
+        // M <- gamma_C M + K^T W (acc already holds gamma_C M), W in two bf16 parts (hi + mid, relative
         // error below 2^-17; a third part cost 8 more MFMAs per chunk and
         // 3% of the time): the lane's k-slots are tokens 4 g .. 4 g + 3 (first
         // half) and 16 + 4 g .. 16 + 4 g + 3 (second half), one 32-deep
         // product per part; MFMA row m of row tile rt is state row
-        // chunk_row(rt, m)
-        const float gC = C.gam[CT - 1];
+        // chunk_row(rt, m).  The key rows serve both column blocks.
+        bf16x8 WH[CPW], WM[CPW];
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) acc[rt] *= gC;
-        uint32_t h1[2], m1[2], h2[2], m2[2];
-        split2(W1, h1, m1);
-        split2(W2, h2, m2);
-        const bf16x8 BH = __builtin_bit_cast(bf16x8, u32x4{h1[0], h1[1], h2[0], h2[1]});
-        const bf16x8 BM = __builtin_bit_cast(bf16x8, u32x4{m1[0], m1[1], m2[0], m2[1]});
+        for (int e = 0; e < CPW; ++e) {
+            uint32_t h1[2], m1[2], h2[2], m2[2];
+            split2(W1[e], h1, m1);
+            split2(W2[e], h2, m2);
+            WH[e] = __builtin_bit_cast(bf16x8, u32x4{h1[0], h1[1], h2[0], h2[1]});
+            WM[e] = __builtin_bit_cast(bf16x8, u32x4{m1[0], m1[1], m2[0], m2[1]});
+        }
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
-            const int R = chunk_row(rt, n);
-            const bf16x8 A2 = __builtin_bit_cast(bf16x8, *(const u32x4 *)&KT[R][8 * (g ^ ((R >> 3) & 3))]);
-            acc[rt] = mfma_bf16_k32(A2, BH, acc[rt]);
-            acc[rt] = mfma_bf16_k32(A2, BM, acc[rt]);
+            const bf16x8 A2 = __builtin_bit_cast(bf16x8, ktr[rt]);
+#pragma unroll
+            for (int e = 0; e < CPW; ++e) {
+                acc[e][rt] = mfma_bf16_k32(A2, WH[e], acc[e][rt]);
+                acc[e][rt] = mfma_bf16_k32(A2, WM[e], acc[e][rt]);
+            }
         }
         lds_barrier();  // chunk c+1 prepared and its key table built, chunk c's buffer free
     }
 
     // ---- encode each column block once: absmax, scale, codes ----
-    to_pool_layout<NKS>(acc, lane);
-    {
+#pragma unroll
+    for (int e = 0; e < CPW; ++e) {
+        const int cb = cb0 + e, j = 16 * cb + n;
+        to_pool_layout<NKS>(acc[e], lane);
         float am = 0.f;
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) am = fmaxf(am, fabsf(acc[rt][r]));
+            for (int r = 0; r < 4; ++r) am = fmaxf(am, fabsf(acc[e][rt][r]));
         am = xor_max(am, 16);
         am = xor_max(am, 32);
         const float s_new = am * (1.f / QMAX);
@@ -680,7 +770,7 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) y[rt][r] = __float_as_uint(fmaf(acc[rt][r], ratio, 12582912.f));
+            for (int r = 0; r < 4; ++r) y[rt][r] = __float_as_uint(fmaf(acc[e][rt][r], ratio, 12582912.f));
         Loader<DK, BITS> outc;
         if constexpr (BITS == 4) {
 #pragma unroll
@@ -696,12 +786,12 @@ __device__ void prefill_tile(const PrefillArgs &a, PrefillLds<DK> &L, int b, int
         }
         outc.store(codes, cb, lane);
         if (g == 0) scl[j] = s_new;
-        if constexpr (ERR) column_error<NRT>(acc, y, 1.f, s_new, a.p.colerr + (tile_row * DK + j) * 2, g);
+        if constexpr (ERR) column_error<NRT>(acc[e], y, 1.f, s_new, a.p.colerr + (tile_row * DK + j) * 2, g);
     }
 }
 
 template <int DK, bool ERR, bool WIDE_OFF>
-__global__ void __launch_bounds__(64 * (DK / 16 + NPROD)) prefill_mfma_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(64 * (DK / 16 / CPW + NPROD)) prefill_mfma_kernel(PrefillArgs a) {
     __shared__ PrefillLds<DK> L;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -741,7 +831,7 @@ hipError_t launch_prefill_mfma(const PoolView &p, int n_tok, const void *q, cons
     const bool err = p.colerr != nullptr;
     // byte span of one chunk's outputs (float32): 32-bit lane offsets suffice below 2^32
     const bool wide = (unsigned long long)CT * a.tiles * p.dk * sizeof(float) >= (1ull << 32);
-    const dim3 grid(a.tiles), block(64 * (p.dk / 16 + NPROD));
+    const dim3 grid(a.tiles), block(64 * (p.dk / 16 / CPW + NPROD));
 #define PACE_PREFILL_LAUNCH(DK_, ERR_, WIDE_) \
     hipLaunchKernelGGL((prefill_mfma_kernel<DK_, ERR_, WIDE_>), grid, block, 0, s, a)
     if (p.dk == 128) {
