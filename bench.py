@@ -141,7 +141,7 @@ ARITHMETIC = ("float32 state/accumulators/outputs; bf16 MFMA on exact code and t
 
 
 def copy_calibration(nbytes: int, reps: int = 10) -> dict:
-    """Attainable device bandwidth, timed after the decode region (so it
+    """Attainable device bandwidth, timed after the timed region (so it
     cannot warm anything up for it): the library's streaming copy (16-byte
     non-temporal loads and stores, the decode kernels' pattern) and torch's
     device-to-device copy of the same buffers, best of `reps` each; GB/s
@@ -170,7 +170,7 @@ def copy_calibration(nbytes: int, reps: int = 10) -> dict:
     del src, dst
     return {"stream_copy_gbs": stream_gbs, "torch_copy_gbs": torch_gbs, "bytes": nbytes,
             "unit": "GB/s", "frac_of_peak": stream_gbs / PEAK_HBM_GBS,
-            "note": "read + write bytes; best of %d; timed after the decode region" % reps}
+            "note": "read + write bytes; best of %d; timed after the timed region" % reps}
 
 
 def _cpu_model() -> str:
@@ -357,6 +357,7 @@ def bench_prefill(args) -> int:
         "cpu_baseline": None,
     }
     st.free()
+    res["copy_calibration"] = copy_calibration(args.copy_bytes) if args.copy_bytes else None
     print(json.dumps(res), flush=True)
     return 0
 
