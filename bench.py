@@ -39,10 +39,17 @@ PEAK_HBM_GBS = 8000.0
 PROMPT_HEAD = 64
 # sources of the timed kernel (8-token chunks): a stored traffic figure counts
 # only while their hash matches
+# sources of the fused decode kernel a period runs on: 1..8 tokens per call,
+# or 9..16 (the 16-token chunk kernel)
 KERNEL_SOURCES = ["linear_attn_decode_pace_amd/csrc/decode_mfma.hip",
                   "linear_attn_decode_pace_amd/csrc/mfma_common.h",
                   "linear_attn_decode_pace_amd/csrc/pace_mfma.h",
                   "linear_attn_decode_pace_amd/csrc/pace_layout.h"]
+KERNEL_SOURCES_16 = ["linear_attn_decode_pace_amd/csrc/decode_mfma16.hip",
+                     "linear_attn_decode_pace_amd/csrc/chunk16.h",
+                     "linear_attn_decode_pace_amd/csrc/mfma_common.h",
+                     "linear_attn_decode_pace_amd/csrc/pace_mfma.h",
+                     "linear_attn_decode_pace_amd/csrc/pace_layout.h"]
 
 
 def log(msg: str) -> None:
@@ -97,9 +104,9 @@ def step_bytes_exact(w: inputs.Workload, head_bits, fill_before, closed) -> floa
     return float(total.item())
 
 
-def kernel_sha() -> str:
+def kernel_sha(period: int = 8) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in (KERNEL_SOURCES_16 if period > 8 else KERNEL_SOURCES):
         fp = os.path.join(ROOT, p)
         if os.path.exists(fp):
             with open(fp, "rb") as f:
@@ -518,7 +525,7 @@ def main() -> int:
     else:
         nbytes = algorithmic_bytes(w, C, head_bits)
     achieved = nbytes / (launch_ms * 1e-3) / 1e9
-    sha = kernel_sha()
+    sha = kernel_sha(1 if step_mode else C)
     tokens_per_call = 1 if step_mode else C
     value = w.B * tokens_per_call * K / (total_ms * 1e-3)
     res = {

@@ -4,7 +4,7 @@
 //   kk[t][s] = k_t . k_s,  qk[t][s] = q_t . k_s                (Gram on MFMA)
 //   Gamma_ts = prod_{s<r<=t} alpha_r, gam[t] = Gamma_t,-1, gamC[t] = Gamma_15,t
 //   A = strictly lower (Gamma * kk),  Lq = lower incl. diagonal (Gamma * qk)
-//   Tt = ((I + diag(beta) A)^-1 diag(beta))^T                  (UT transform)
+//   Zt = ((I + diag(beta) A)^-1)^T, so that T = Z diag(beta)   (UT transform)
 //   LqT = Lq T                                                  (float32 MFMA)
 // Gates are products of alpha (no log / exp).  All arrays live in LDS; each
 // step ends with the wavefront's LDS writes visible to it (wave_sync).
@@ -58,9 +58,19 @@ __device__ inline void chunk16_gram(const uint16_t (*kq)[ROW], float (*kk)[STR],
     chunk16_gram2<DK, ROW, STR>(kq, kq, kk, qk, lane);
 }
 
+// x from lane n - K (SHR) or n + K (SHL) of the lane's row of 16, 1 where
+// that lane lies outside the row
+template <int CTRL>
+__device__ inline float row_move_or_one(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int DPP_SHL = 0x100, DPP_SHR = 0x110;
+
 // gates, A and Lq: lane -> row t = lane / 4, columns s0 .. s0 + 3 with
 // s0 = 4 (lane % 4): Gamma_{t,s0+3} as one masked product, then the running
-// product down to s0
+// product down to s0.  gamma_t (prefix products of alpha) and Gamma_{CK-1,t}
+// (the product of the alphas after t) come from DPP scans over each row of
+// 16 lanes, lane n holding alpha_n.
 template <int STR>
 __device__ inline void chunk16_gates(const float *alpha, const float (*kk)[STR],
                                      const float (*qk)[STR], float (*A)[STR], float (*Lq)[STR],
@@ -80,6 +90,17 @@ __device__ inline void chunk16_gates(const float *alpha, const float (*kk)[STR],
         l_row[e] = s <= t ? gts * qk[t][s] : 0.f;
         if (e > 0 && s <= t) gts *= alpha[s];  // Gamma_{t,s-1} = Gamma_{t,s} alpha_s
     }
+    const float x = alpha[lane & 15];
+    float pre = x, suf = x;
+    pre *= row_move_or_one<DPP_SHR + 1>(pre);
+    suf *= row_move_or_one<DPP_SHL + 1>(suf);
+    pre *= row_move_or_one<DPP_SHR + 2>(pre);
+    suf *= row_move_or_one<DPP_SHL + 2>(suf);
+    pre *= row_move_or_one<DPP_SHR + 4>(pre);
+    suf *= row_move_or_one<DPP_SHL + 4>(suf);
+    pre *= row_move_or_one<DPP_SHR + 8>(pre);
+    suf *= row_move_or_one<DPP_SHL + 8>(suf);
+    const float after = row_move_or_one<DPP_SHL + 1>(suf);  // product over r > t
     wave_sync();  // kk / qk are read before A / Lq may alias them
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -87,52 +108,68 @@ __device__ inline void chunk16_gates(const float *alpha, const float (*kk)[STR],
         Lq[t][s0 + e] = l_row[e];
     }
     if (lane < CK) {
-        float gm = 1.f, gc = 1.f;
-#pragma unroll
-        for (int r = 0; r < CK; ++r) {
-            gm *= r <= lane ? al[r] : 1.f;
-            gc *= r > lane ? al[r] : 1.f;
-        }
-        gam[lane] = gm;
-        gamC[lane] = gc;
+        gam[lane] = pre;
+        gamC[lane] = after;
     }
     wave_sync();
 }
 
-// UT transform: column s of Z = (I + diag(beta) A)^-1 by forward
-// substitution (one column per lane), T = Z diag(beta), stored transposed
+// UT transform in 8 x 8 blocks.  Z = (I + N)^-1 with N = diag(beta) A
+// strictly lower is [Z11 0; Z21 Z22] with Z11, Z22 the inverses of the
+// diagonal blocks and Z21 = -Z22 N21 Z11.  Lanes 0..15 substitute column
+// s = lane of its diagonal block (8 steps); then all 64 lanes form
+// Y = N21 Z11 and Z21 = -Z22 Y, one entry each.  Writes Zt[s][t] = Z[t][s]
+// (T = Z diag(beta) is left to the readers: T[t][s] = Z[t][s] beta_s).
 template <int STR>
-__device__ inline void chunk16_ut(const float (*A)[STR], const float *beta, float (*Tt)[STR],
+__device__ inline void chunk16_ut(const float (*A)[STR], const float *beta, float (*Zt)[STR],
                                   int lane) {
-    const int s = lane & 15;
-    float be[CK], z[CK];
+    {
+        const int s = lane & 15, rb = s & 8;  // column s, rows rb .. rb + 7 of its diagonal block
+        float z[8];
 #pragma unroll
-    for (int r = 0; r < CK; ++r) be[r] = beta[r];
+        for (int t = 0; t < 8; ++t) {
+            float sum = 0.f;
 #pragma unroll
-    for (int t = 0; t < CK; ++t) {
-        float sum = 0.f;
+            for (int u = 0; u < t; ++u) sum = fmaf(A[rb + t][rb + u], z[u], sum);
+            z[t] = (rb + t == s ? 1.f : 0.f) - beta[rb + t] * sum;
+        }
+        if (lane < CK) {
 #pragma unroll
-        for (int u = 0; u < t; ++u) sum = fmaf(A[t][u], z[u], sum);
-        z[t] = (t == s ? 1.f : 0.f) - be[t] * sum;
+            for (int t = 0; t < 8; ++t) Zt[s][rb + t] = z[t];
+        }
     }
-    if (lane < CK) {
+    wave_sync();
+    const int i = lane >> 3, j = lane & 7;
+    // Y[i][j] = beta_{8+i} sum_k A[8+i][k] Z[k][j], kept at Zt[8 + j][i] (the
+    // zero block of Z^T: rows s >= 8, columns t < 8)
+    float y = 0.f;
 #pragma unroll
-        for (int t = 0; t < CK; ++t) Tt[s][t] = z[t] * be[s];
-    }
+    for (int k = 0; k < 8; ++k) y = fmaf(A[8 + i][k], Zt[j][k], y);
+    Zt[8 + j][i] = beta[8 + i] * y;
+    wave_sync();
+    // Z21[i][j] = -sum_k Z[8+i][8+k] Y[k][j]; then the zero block is restored
+    float zz = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) zz = fmaf(Zt[8 + k][8 + i], Zt[8 + j][k], zz);
+    Zt[j][8 + i] = -zz;
+    wave_sync();  // every lane has read Y
+    Zt[8 + j][i] = 0.f;
     wave_sync();
 }
 
-// Lq T on float32 MFMA: step st takes column / row 4 st + g
+// Lq T on float32 MFMA from Zt = Z^T (T = Z diag(beta)): step st takes
+// column / row 4 st + g; the product's column n is scaled by beta_n
 template <int STR>
-__device__ inline void chunk16_lqt(const float (*Lq)[STR], const float (*Tt)[STR], float (*LqT)[STR],
-                                   int lane) {
+__device__ inline void chunk16_lqt(const float (*Lq)[STR], const float (*Zt)[STR], const float *beta,
+                                   float (*LqT)[STR], int lane) {
     const int g = lane >> 4, n = lane & 15;
     f32x4 D = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int st = 0; st < 4; ++st) D = mfma_f32_k4(Lq[n][4 * st + g], Tt[n][4 * st + g], D);
+    for (int st = 0; st < 4; ++st) D = mfma_f32_k4(Lq[n][4 * st + g], Zt[n][4 * st + g], D);
+    const float bn = beta[n];
     wave_sync();  // Lq is read before LqT may alias it
 #pragma unroll
-    for (int r = 0; r < 4; ++r) LqT[4 * g + r][n] = D[r];
+    for (int r = 0; r < 4; ++r) LqT[4 * g + r][n] = D[r] * bn;
     wave_sync();
 }
 

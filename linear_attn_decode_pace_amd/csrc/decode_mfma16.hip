@@ -37,7 +37,7 @@ struct alignas(16) Tile16Lds {
             // rows padded to CKS floats: a column's 16 entries in 16 banks
             float kkA[C16][CKS];   // k_t.k_s, then A (strictly lower Gamma * K K^T) in place
             float qkLq[C16][CKS];  // q_t.k_s, then Lq, then Lq T in place
-            float Tt[C16][CKS];    // Tt[s][t] = T[t][s]
+            float Zt[C16][CKS];    // Zt[s][t] = Z[t][s], T = Z diag(beta)
         } m;
         float o[C16][OROW16];      // outputs of two column blocks
     } u;
@@ -76,24 +76,25 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
         sring[c] = scl[16 * c + n];
     }
 
-    // ---- stage the chunk's tokens (48 rows) in LDS; padding tokens are zero ----
+    // ---- stage the chunk's tokens (48 rows) in LDS.  A padding token
+    //      (t >= n_tok, alpha = 1, beta = 0) repeats the last real token's
+    //      k, q, v: beta = 0 makes its row and column of T exactly zero, so
+    //      finite values there change no output or state entry ----
     {
         constexpr int CPR = DK / 8;                // 16-byte chunks per token row
-        constexpr int NL = 3 * C16 * CPR / 64;     // loads per lane (12 for d = 128)
+        constexpr int RPL = 64 / CPR;              // token rows per load
+        constexpr int NL = 3 * C16 / RPL;          // loads per lane (12 for d = 128)
+        constexpr int NT = C16 / RPL;              // distinct tokens of a lane (4 for d = 128)
         const uint16_t *srcs[3] = {a.k + tile_row * DK, a.q + tile_row * DK, a.v + tile_row * DK};
-        // load it reads token row (lane / CPR + (64 / CPR) it) & 15: the lane's
-        // own token plus a wave-uniform step (one per-lane 64-bit product)
-        const size_t lane_off = (size_t)(lane / CPR) * tok_elems + (lane % CPR) * 8;
+        // load it reads token row lane / CPR + RPL (it % NT) of source it / NT
+        size_t toff[NT];
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+            toff[i] = (size_t)min(lane / CPR + RPL * i, n_tok - 1) * tok_elems + (lane % CPR) * 8;
         u32x4 val[NL];
 #pragma unroll
-        for (int it = 0; it < NL; ++it) {
-            const int c = lane + 64 * it;
-            const int row = c / CPR;
-            const int t = row & 15, which = row >> 4;  // which is uniform per load
-            const size_t off = lane_off + (size_t)(((64 / CPR) * it) & 15) * tok_elems;
-            val[it] = u32x4{0u, 0u, 0u, 0u};
-            if (t < n_tok) val[it] = __builtin_nontemporal_load((const u32x4 *)(srcs[which] + off));
-        }
+        for (int it = 0; it < NL; ++it)
+            val[it] = __builtin_nontemporal_load((const u32x4 *)(srcs[it / NT] + toff[it % NT]));
         float ab = 0.f;
         if (lane < 32) {
             const int t = lane & 15;
@@ -148,8 +149,8 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
     // ---- the chunk's token-only matrices (chunk16.h) ----
     chunk16_gram<DK, LROW16>(L.kq, L.u.m.kkA, L.u.m.qkLq, lane);
     chunk16_gates(L.alpha, L.u.m.kkA, L.u.m.qkLq, L.u.m.kkA, L.u.m.qkLq, L.gam, L.gamC, lane);
-    chunk16_ut(L.u.m.kkA, L.beta, L.u.m.Tt, lane);
-    chunk16_lqt(L.u.m.qkLq, L.u.m.Tt, L.u.m.qkLq, lane);
+    chunk16_ut(L.u.m.kkA, L.beta, L.u.m.Zt, lane);
+    chunk16_lqt(L.u.m.qkLq, L.u.m.Zt, L.beta, L.u.m.qkLq, lane);
 
     // ---- chunk-mixing operands (float32 16x16x4 MFMA; step st takes token
     //      4 st + g from lane group g):
@@ -162,7 +163,7 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             const int s = 4 * st + g;
-            CW[st] = gct * L.u.m.Tt[s][n];
+            CW[st] = gct * (L.u.m.Zt[s][n] * L.beta[s]);  // Gamma_{C-1,n} T[n][s]
             CO[st] = L.u.m.qkLq[n][s];  // (Lq T)[n][s]
         }
     }
