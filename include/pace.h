@@ -122,9 +122,10 @@ extern "C" {
  * of up to period - 1 tokens (its k_t, v_t in in_dtype and alpha_t, beta_t in
  * float32) and a fill count; the token that completes a period applies the
  * buffer and itself to the decoded state and re-encodes it, every other token
- * is appended to the buffer.  This is the serving form of periodic rounding:
- * 'PACE: four-bit recurrent state by rounding less often', flowchart (new
- * tokens -> small buffer -> every k tokens a high-precision update -> encode).
+ * is appended to the buffer.  This is the serving form of periodic rounding
+ * ('PACE: four-bit recurrent state by rounding less often', flowchart 'Fewer
+ * roundings, less compounded error'): decoded tokens are held back and
+ * applied together once per period, followed by one encode.
  * Buffer bytes: B * H * (period - 1) * ((d_k + d_v) * elem + 8), plus
  * B * H * 4 for the fill counts (pace_stats.bytes_step_buffer).  Such a
  * handle rejects pace_decode_period. */

@@ -3,9 +3,9 @@
 Follows 'PACE: four-bit recurrent state by rounding less often': TL;DR point
 (1) (the state is left unquantized while a short run of tokens is applied and
 is rounded once when the run ends) and the flowchart 'Fewer roundings, less
-compounded error' (tokens wait in a buffer; each k tokens the state is updated
-in high precision, then encoded column by column at 4 bits, or 8 bits for the
-heads that keep their errors longest); also 'PACE: A New 4-Bit Recurrent State Quantization Method ...',
+compounded error' (decoded tokens are held back, then applied together once
+per period in high precision, after which each column is re-encoded at 4 bits,
+or 8 bits for the heads whose rounding errors last longest); also 'PACE: A New 4-Bit Recurrent State Quantization Method ...',
 section 'Periodic Rounding: Reducing Error Accumulation'.
 
 Readings where the pages are silent:
