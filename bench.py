@@ -45,6 +45,11 @@ KERNEL_SOURCES = ["linear_attn_decode_pace_amd/csrc/decode_mfma.hip",
                   "linear_attn_decode_pace_amd/csrc/mfma_common.h",
                   "linear_attn_decode_pace_amd/csrc/pace_mfma.h",
                   "linear_attn_decode_pace_amd/csrc/pace_layout.h"]
+PREFILL_SOURCES = ["linear_attn_decode_pace_amd/csrc/prefill_mfma.hip",
+                   "linear_attn_decode_pace_amd/csrc/pace_prefill.h",
+                   "linear_attn_decode_pace_amd/csrc/mfma_common.h",
+                   "linear_attn_decode_pace_amd/csrc/pace_mfma.h",
+                   "linear_attn_decode_pace_amd/csrc/pace_layout.h"]
 KERNEL_SOURCES_16 = ["linear_attn_decode_pace_amd/csrc/decode_mfma16.hip",
                      "linear_attn_decode_pace_amd/csrc/chunk16.h",
                      "linear_attn_decode_pace_amd/csrc/mfma_common.h",
@@ -104,9 +109,9 @@ def step_bytes_exact(w: inputs.Workload, head_bits, fill_before, closed) -> floa
     return float(total.item())
 
 
-def kernel_sha(period: int = 8) -> str:
+def kernel_sha(period: int = 8, prefill: bool = False) -> str:
     h = hashlib.sha256()
-    for p in (KERNEL_SOURCES_16 if period > 8 else KERNEL_SOURCES):
+    for p in (PREFILL_SOURCES if prefill else KERNEL_SOURCES_16 if period > 8 else KERNEL_SOURCES):
         fp = os.path.join(ROOT, p)
         if os.path.exists(fp):
             with open(fp, "rb") as f:
@@ -127,6 +132,8 @@ def generate(w, seed, jobs, workers):
 
 
 def traffic_from_profile(name: str, sha: str, n_launch_bytes: int):
+    """HBM bytes per launch from a committed counter profile, if it was taken
+    on these kernel sources (profiles/traffic_<name>.json)."""
     fp = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
     if not os.path.exists(fp):
         return None
@@ -347,8 +354,10 @@ def bench_prefill(args) -> int:
         st.prefill(big, out)
         ev[i][1].record()
     torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b) for a, b in ev) / K
+    per_launch = [a.elapsed_time(b) for a, b in ev]
+    ms = sum(per_launch) / K
     nbytes = prefill_bytes(w, T, head_bits)
+    sha = kernel_sha(prefill=True)
     achieved = nbytes / (ms * 1e-3) / 1e9
     res = {
         "metric": "prefill prompt tokens/s into the quantized state (seqs x prompt tokens)",
@@ -359,8 +368,11 @@ def bench_prefill(args) -> int:
                    "d_k": w.dk, "d_v": w.dv, "prompt_tokens": T, "distinct_prompt_tokens": D,
                    "heads_int8": int((head_bits == 8).sum()), "inputs": w.dtype},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
-                     "algorithmic_bytes_per_launch": nbytes, "launch_ms": ms},
+                     "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": traffic_from_profile(f"{w.name}_prefill", sha, nbytes),
+                     "algorithmic_bytes_per_launch": nbytes, "launch_ms": ms,
+                     "launch_ms_min": min(per_launch), "launch_ms_median": sorted(per_launch)[K // 2],
+                     "launch_ms_max": max(per_launch), "kernel_sha": sha},
         "cpu_baseline": None,
     }
     st.free()
