@@ -81,7 +81,7 @@ extern "C" {
 #define PACE_OK 0
 #define PACE_EINVAL (-1)       /* a bad argument: null pointer, size, enum, alignment */
 #define PACE_ENOMEM (-2)       /* device allocation failed */
-#define PACE_EUNSUPPORTED (-3) /* a shape or period this build has no kernel for */
+#define PACE_EUNSUPPORTED (-3) /* a shape or period the library has no kernel for */
 #define PACE_EDEVICE (-4)      /* a HIP error (no device, launch failure, earlier fault) */
 
 /* element types of q, k, v */

@@ -1,4 +1,4 @@
-"""Driver for GPU-vs-oracle decode runs, shared by the GPU tests."""
+"""Runner for GPU-vs-oracle decode cases, shared by the GPU tests."""
 from __future__ import annotations
 
 import sys
