@@ -81,6 +81,21 @@ def test_vanishing_decay(period, value):
              label=f"vanish-k{period}-{value:g}")
 
 
+def test_padded_periods_vanishing_int8():
+    # calls of 9, 11 and 15 tokens (the 16-token kernel pads them with 7, 5
+    # and 1 identity tokens that repeat the last real token's inputs), all
+    # heads at 8 bits, and the even sequences decaying by 1e-5 per token
+    # (the below-normal-decay branch)
+    w = inputs.ragged("pad-vanish8", 108, B=4, H=3, n_int8=3, period=16, steps=35)
+    run_case(w, 9, [(0, 9), (9, 20), (20, 35)], tok_hook=_vanishing_alpha(1e-5), label="pad-vanish8")
+
+
+def test_d64_padded_periods():
+    # d = 64 (two k-slices per column block) with 9-, 15- and 9-token calls
+    w = inputs.ragged("d64-pad", 109, B=3, H=4, dk=64, dv=64, n_int8=2, period=16, steps=33)
+    run_case(w, 10, [(0, 9), (9, 24), (24, 33)])
+
+
 @pytest.mark.parametrize("dv", [48, 80])
 def test_dv_differs_from_dk(dv):
     # d_v != d_k (the per-column kernels) with column blocks that do not fill
