@@ -37,24 +37,35 @@ from linear_attn_decode_pace_amd import inputs  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
 PROMPT_HEAD = 64
-# sources of the timed kernel (8-token chunks): a stored traffic figure counts
-# only while their hash matches
-# sources of the fused decode kernel a period runs on: 1..8 tokens per call,
-# or 9..16 (the 16-token chunk kernel)
+# sources (with every header they include) of each timed kernel: the fused
+# decode for 1..8 tokens per call, the 16-token chunk kernel for 9..16, the
+# prefill and the FP8-window step.  A stored traffic figure counts only while
+# the hash of its kernel's sources matches.
 KERNEL_SOURCES = ["linear_attn_decode_pace_amd/csrc/decode_mfma.hip",
                   "linear_attn_decode_pace_amd/csrc/mfma_common.h",
                   "linear_attn_decode_pace_amd/csrc/pace_mfma.h",
+                  "linear_attn_decode_pace_amd/csrc/pace_step.h",
                   "linear_attn_decode_pace_amd/csrc/pace_layout.h"]
 PREFILL_SOURCES = ["linear_attn_decode_pace_amd/csrc/prefill_mfma.hip",
                    "linear_attn_decode_pace_amd/csrc/pace_prefill.h",
                    "linear_attn_decode_pace_amd/csrc/mfma_common.h",
                    "linear_attn_decode_pace_amd/csrc/pace_mfma.h",
+                   "linear_attn_decode_pace_amd/csrc/pace_step.h",
                    "linear_attn_decode_pace_amd/csrc/pace_layout.h"]
 KERNEL_SOURCES_16 = ["linear_attn_decode_pace_amd/csrc/decode_mfma16.hip",
                      "linear_attn_decode_pace_amd/csrc/chunk16.h",
                      "linear_attn_decode_pace_amd/csrc/mfma_common.h",
                      "linear_attn_decode_pace_amd/csrc/pace_mfma.h",
+                     "linear_attn_decode_pace_amd/csrc/pace_step.h",
                      "linear_attn_decode_pace_amd/csrc/pace_layout.h"]
+# the FP8-window step kernel
+WINDOW_SOURCES = ["linear_attn_decode_pace_amd/csrc/window_mfma.hip",
+                  "linear_attn_decode_pace_amd/csrc/e4m3.h",
+                  "linear_attn_decode_pace_amd/csrc/pace_window.h",
+                  "linear_attn_decode_pace_amd/csrc/mfma_common.h",
+                  "linear_attn_decode_pace_amd/csrc/pace_mfma.h",
+                  "linear_attn_decode_pace_amd/csrc/pace_step.h",
+                  "linear_attn_decode_pace_amd/csrc/pace_layout.h"]
 
 
 def log(msg: str) -> None:
@@ -109,9 +120,11 @@ def step_bytes_exact(w: inputs.Workload, head_bits, fill_before, closed) -> floa
     return float(total.item())
 
 
-def kernel_sha(period: int = 8, prefill: bool = False) -> str:
+def kernel_sha(period: int = 8, prefill: bool = False, window: bool = False) -> str:
     h = hashlib.sha256()
-    for p in (PREFILL_SOURCES if prefill else KERNEL_SOURCES_16 if period > 8 else KERNEL_SOURCES):
+    srcs = (PREFILL_SOURCES if prefill else WINDOW_SOURCES if window
+            else KERNEL_SOURCES_16 if period > 8 else KERNEL_SOURCES)
+    for p in srcs:
         fp = os.path.join(ROOT, p)
         if os.path.exists(fp):
             with open(fp, "rb") as f:
@@ -537,7 +550,7 @@ def main() -> int:
     else:
         nbytes = algorithmic_bytes(w, C, head_bits)
     achieved = nbytes / (launch_ms * 1e-3) / 1e9
-    sha = kernel_sha(1 if step_mode else C)
+    sha = kernel_sha(1 if step_mode else C, window=window_mode)
     tokens_per_call = 1 if step_mode else C
     value = w.B * tokens_per_call * K / (total_ms * 1e-3)
     res = {
