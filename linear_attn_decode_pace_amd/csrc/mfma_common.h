@@ -176,21 +176,40 @@ struct Loader {
             }
         }
     }
-    // KAPPA * code of (row tile rt, row r in the lane's group) as float: 4-bit
-    // codes are moved to the high nibble of their byte (a signed byte worth
-    // 16 c), so one sign-extending byte conversion reads each of them
-    static constexpr float KAPPA = BITS == 4 ? 16.f : 1.f;
+    // KAPPA * code of (row tile rt, row r in the lane's group) as float.  A
+    // 4-bit code is read by v_cvt_off_f32_i4, which takes bits 3:0 of its
+    // source (here one byte, or the byte's high half moved down) as a signed
+    // 4-bit integer c and returns c / 16: one instruction per code, with the
+    // factor KAPPA = 1/16 folded exactly into the scale units.  8-bit codes
+    // are one sign-extending byte conversion each.
+    static constexpr float KAPPA = BITS == 4 ? 1.f / 16.f : 1.f;
+    template <int B>
+    __device__ static inline float nibble_f32(uint32_t x) {
+        float r;
+        if constexpr (B == 0)
+            asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(x));
+        else if constexpr (B == 1)
+            asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(x));
+        else if constexpr (B == 2)
+            asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(x));
+        else
+            asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(x));
+        return r;
+    }
     __device__ inline void codes_f32(f32x4 *acc) const {
         if constexpr (BITS == 4) {
 #pragma unroll
             for (int ks = 0; ks < ND; ++ks) {
-                const uint32_t lo = (d[ks] << 4) & 0xf0f0f0f0u;  // row tile 2 ks
-                const uint32_t hi = d[ks] & 0xf0f0f0f0u;         // row tile 2 ks + 1
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    acc[2 * ks][r] = (float)(int)__builtin_amdgcn_sbfe(lo, 8 * r, 8);
-                    acc[2 * ks + 1][r] = (float)(int)__builtin_amdgcn_sbfe(hi, 8 * r, 8);
-                }
+                const uint32_t lo = d[ks];       // row tile 2 ks: low nibbles
+                const uint32_t hi = d[ks] >> 4;  // row tile 2 ks + 1: high nibbles
+                acc[2 * ks][0] = nibble_f32<0>(lo);
+                acc[2 * ks][1] = nibble_f32<1>(lo);
+                acc[2 * ks][2] = nibble_f32<2>(lo);
+                acc[2 * ks][3] = nibble_f32<3>(lo);
+                acc[2 * ks + 1][0] = nibble_f32<0>(hi);
+                acc[2 * ks + 1][1] = nibble_f32<1>(hi);
+                acc[2 * ks + 1][2] = nibble_f32<2>(hi);
+                acc[2 * ks + 1][3] = nibble_f32<3>(hi);
             }
         } else {
 #pragma unroll
