@@ -14,7 +14,11 @@
 // from each lane; the chunk-mixing chain then returns W and O rows 4 g + r,
 // i.e. tokens 4 g + r, which are the reduction indices this lane feeds to the
 // K^T W update (16x16x16 bf16 MFMA, W in two bf16 parts, hi + mid): no
-// cross-lane exchange is needed at C = 16.
+// cross-lane exchange is needed at C = 16.  W (the update's right factor)
+// comes from float32 16x16x4 steps; O, which only leaves as an output, from
+// three bf16 16x16x16 products over two parts of each factor (hi.hi + hi.mid
+// + mid.hi: relative error near 2^-16 per product, against 1e-4 for the
+// outputs), 48 instead of 128 matrix-core cycles per column block.
 #include "chunk16.h"
 
 namespace pace {
@@ -152,8 +156,9 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
     chunk16_ut(L.u.m.kkA, L.beta, L.u.m.Zt, lane);
     chunk16_lqt(L.u.m.qkLq, L.u.m.Zt, L.beta, L.u.m.qkLq, lane);
 
-    // ---- chunk-mixing operands (float32 16x16x4 MFMA; step st takes token
-    //      4 st + g from lane group g):
+    // ---- chunk-mixing operands (step st takes token 4 st + g from lane
+    //      group g; 16x16x4 float32 MFMA for W, the same four k-slots of a
+    //      16x16x16 bf16 MFMA for O):
     //      W chain, row m = token m: A = Gamma_{C-1,m} T[m][4 st + k]
     //      O chain, row m = token m: A = (Lq T)[m][4 st + k] on X; Y is added
     //      in place, its rows already in output order ----
@@ -174,6 +179,15 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
         gam_o[r] = L.gam[4 * g + r];
     }
     const float gamC = L.gam[C16 - 1];
+    // the O coefficients in two bf16 parts (hi + mid), k-slot 4 g + st
+    s16x4 COH, COM;
+    {
+        const uint32_t h01 = pk_bf16(CO[0], CO[1]), h23 = pk_bf16(CO[2], CO[3]);
+        const uint32_t m01 = pk_bf16(CO[0] - lo_f32(h01), CO[1] - hi_f32(h01));
+        const uint32_t m23 = pk_bf16(CO[2] - lo_f32(h23), CO[3] - hi_f32(h23));
+        COH = __builtin_bit_cast(s16x4, u32x2{h01, h23});
+        COM = __builtin_bit_cast(s16x4, u32x2{m01, m23});
+    }
 
     // K^T as the update's A operand: row i = 16 rt + n, k index 4 g + e is token 4 g + e
     s16x4 AU[NRT];
@@ -234,9 +248,16 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
         }
         f32x4 W = {0.f, 0.f, 0.f, 0.f}, O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            W = mfma_f32_k4(CW[st], X[st] * inv_sig, W);
-            O = mfma_f32_k4(CO[st], X[st], O);
+        for (int st = 0; st < 4; ++st) W = mfma_f32_k4(CW[st], X[st] * inv_sig, W);
+        {
+            const uint32_t xh01 = pk_bf16(X[0], X[1]), xh23 = pk_bf16(X[2], X[3]);
+            const uint32_t xm01 = pk_bf16(X[0] - lo_f32(xh01), X[1] - hi_f32(xh01));
+            const uint32_t xm23 = pk_bf16(X[2] - lo_f32(xh23), X[3] - hi_f32(xh23));
+            const s16x4 XH = __builtin_bit_cast(s16x4, u32x2{xh01, xh23});
+            const s16x4 XM = __builtin_bit_cast(s16x4, u32x2{xm01, xm23});
+            O = mfma_bf16_k16(COH, XH, O);
+            O = mfma_bf16_k16(COH, XM, O);
+            O = mfma_bf16_k16(COM, XH, O);
         }
         // + Y = diag(gamma) Q M0, tokens 4 g + r
 #pragma unroll
