@@ -214,3 +214,62 @@ def test_error_statistics_off_and_zero_init():
     assert s["err_tracked"] == 1 and len(s["err_sq"]) == W.H
     assert not any(s["err_sq"]) and not any(s["ref_sq"])
     z.free()
+
+
+@pytest.mark.parametrize("period,dk", [(8, 128), (16, 128), (8, 64), (16, 64)])
+def test_every_code_value_decodes(period, dk):
+    # A raw image whose code bytes are random (nibbles -7..7, bytes -127..127:
+    # every code a stored state can hold, each column full of +-qmax, which an
+    # encode only writes at its absmax entry).  The per-column reader and the
+    # fused decode kernels must agree on every value: read_codes against the
+    # bytes (as multisets, independent of the pool layout), then one period
+    # against the oracle started from the codes read.
+    import torch
+    from linear_attn_decode_pace_amd import pace, runtime
+    w = inputs.ragged(f"code-range-k{period}-d{dk}", 210, B=3, H=4, dk=dk, dv=dk, n_int8=2,
+                      period=period, steps=period)
+    say(f"[case] every code value: period {period}, d {dk}")
+    st, bits = _state(w, 4)
+    raw = st.read_raw()
+    st.free()
+    n4 = int((bits == 4).sum()) * w.B * dk * dk // 2
+    n8 = int((bits == 8).sum()) * w.B * dk * dk
+    rng = np.random.default_rng(11 + period + dk)
+    b4 = rng.integers(0, 256, n4, dtype=np.uint8)
+    b4 = np.where((b4 & 0x0F) == 0x08, b4 & 0xF0, b4)       # no nibble -8
+    b4 = np.where((b4 & 0xF0) == 0x80, b4 & 0x0F, b4)
+    b8 = rng.integers(0, 256, n8, dtype=np.uint8)
+    b8 = np.where(b8 == 0x80, 0, b8).astype(np.uint8)         # no byte -128
+    img = raw.clone()
+    img[:n4 + n8] = torch.as_tensor(np.concatenate([b4, b8]), device=img.device)
+    st = runtime.State(w, bits, pace.PACE_INIT_RAW, img)
+    c, s = st.read_codes()
+    n = w.B * w.H
+    codes = c.reshape(n, dk, dk).cpu().numpy().astype(np.int64)
+    scales = s.reshape(n, dk).cpu().numpy()
+    bits_t = np.tile(bits, w.B).astype(np.int64)
+
+    def signed4(x):
+        x = x.astype(np.int64)
+        return np.where(x >= 8, x - 16, x)
+    want4 = np.bincount(np.concatenate([signed4(b4 & 0x0F), signed4(b4 >> 4)]) + 8, minlength=16)
+    want8 = np.bincount(b8.view(np.int8).astype(np.int64) + 128, minlength=256)
+    got4 = np.bincount(codes[bits_t == 4].ravel() + 8, minlength=16)
+    got8 = np.bincount(codes[bits_t == 8].ravel() + 128, minlength=256)
+    assert np.array_equal(got4, want4) and np.array_equal(got8, want8)
+    assert got4[1] > 0 and got4[15] > 0 and got8[1] > 0 and got8[255] > 0  # -7, 7, -127, 127 present
+
+    tok = inputs.decode_period(w, 4, 0)
+    out = runtime.out_buffer(w, tok.T)
+    st.decode(runtime.DeviceTokens(tok), out)
+    o = out.reshape(tok.T, n, dk).cpu().numpy()
+    nc, ns = st.read_codes()
+    nc = nc.reshape(n, dk, dk).cpu().numpy()
+    ns = ns.reshape(n, dk).cpu().numpy()
+    q, k, v, a, b = tok_tiles(tok, np.arange(n), w.H)
+    O, c2, s2, Mpre = opace.period(codes, scales, bits_t, q, k, v, a, b)
+    m = parity.check_outputs(o, O, f"code range k={period} d={dk}")
+    rep = parity.check_encoded(nc, ns, c2, s2, Mpre, f"code range k={period} d={dk}")
+    say(f"[case] every code value: output rel err {m:.2e}, scale rel err {rep.max_scale:.2e}, "
+        f"flips {rep.flips}/{rep.entries}")
+    st.free()
