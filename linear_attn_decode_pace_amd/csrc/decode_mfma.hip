@@ -21,8 +21,10 @@
 //     because codes (|c| <= 127) and bf16 inputs are exact in bf16 and their
 //     products exact in float32;
 //   * the 8 x 8 chunk matrices applied to X and Y = diag(gamma) Q M0 give W
-//     (the update's right factor) and O: float32 MFMA (16x16x4), whose
-//     operand layout matches what each lane already holds;
+//     (the update's right factor) and O: float32 MFMA (16x16x4) on X, whose
+//     operand layout matches what each lane already holds, and Y (which
+//     enters only O, with coefficient 1) added by one bf16 MFMA over two
+//     parts of Y;
 //   * K^T W (d x 8 x 16 per column block): bf16 MFMA with W in two bf16
 //     parts (hi + mid: 16 significant bits, relative error below 2^-17)
 //     stacked along the reduction dimension, one 16-deep product per row
@@ -305,8 +307,8 @@ __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int
     }
     tile_sync<WPT>();
 
-    // ---- A operand of the chunk mixing (float32 16x16x4 MFMA, 4 steps over
-    //      [X tokens 0-3, X 4-7, Y 0-3, Y 4-7]):
+    // ---- A operand of the chunk mixing (4 steps over [X tokens 0-3, X 4-7,
+    //      Y 0-3, Y 4-7]; float32 16x16x4 MFMA for the X steps):
     //      rows 0..7  -> W_t = Gamma_{C-1,t} (T X)_t          (A = Gamma_C T, 0)
     //      rows 8..15 -> O_t = (Lq T X)_t + Y_t               (A = Lq T, I) ----
     float CA[4];
@@ -331,6 +333,12 @@ __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int
         CA[2] = (is_o && t == g) ? 1.f : 0.f;
         CA[3] = (is_o && t == 4 + g) ? 1.f : 0.f;
     }
+    // Y enters only the O rows, with coefficient 1: one bf16 16x16x16 product
+    // adds it, Y in two parts (k-slots 4 g + [Y0 hi, Y1 hi, Y0 mid, Y1 mid]),
+    // in place of the two float32 Y steps (16 instead of 64 matrix-core
+    // cycles).  W's rows get exact zeros from it; O gets Y to 2^-17.
+    const uint32_t ay = pk_bf16(CA[2], CA[3]);
+    const s16x4 AY = __builtin_bit_cast(s16x4, u32x2{ay, ay});
     const float gam_g = L.gam[g], gam_4g = L.gam[4 + g], gamC = L.gam[CH - 1];
     TRACE(4, CA[0]); TRACE(5, CA[1]); TRACE(6, CA[2]); TRACE(7, CA[3]);
     TRACE(10, gam_g); TRACE(11, gam_4g); TRACE(12, gamC);
@@ -409,11 +417,12 @@ __device__ void process_tile(const MfmaArgs &a, TileLds &L, WaveOut &WO_lds, int
         const float inv_sig = __builtin_amdgcn_rcpf(sig);
 
         // one chain: lanes g < 2 get W (tokens 4 g + r), lanes g >= 2 get O
+        const uint32_t yh = pk_bf16(Y0, Y1);
+        const uint32_t ym = pk_bf16(Y0 - lo_f32(yh), Y1 - hi_f32(yh));
         f32x4 WO = {0.f, 0.f, 0.f, 0.f};
         WO = mfma_f32_k4(CA[0], X0, WO);
         WO = mfma_f32_k4(CA[1], X1, WO);
-        WO = mfma_f32_k4(CA[2], Y0, WO);
-        WO = mfma_f32_k4(CA[3], Y1, WO);
+        WO = mfma_bf16_k16(AY, __builtin_bit_cast(s16x4, u32x2{yh, ym}), WO);
         f32x4 W;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
