@@ -13,9 +13,8 @@
 // which is exactly the reduction index the float32 16x16x4 MFMA steps take
 // from each lane; the chunk-mixing chain then returns W and O rows 4 g + r,
 // i.e. tokens 4 g + r, which are the reduction indices this lane feeds to the
-// K^T W update (one 16x16x32 bf16 MFMA per row tile: W's hi and mid parts in
-// the upper and lower four k-slots of each lane group, the key operand
-// repeated): no cross-lane exchange is needed at C = 16.  W (the update's right factor)
+// K^T W update (16x16x16 bf16 MFMA, W in two bf16 parts, hi + mid): no
+// cross-lane exchange is needed at C = 16.  W (the update's right factor)
 // comes from float32 16x16x4 steps; O, which only leaves as an output, from
 // three bf16 16x16x16 products over two parts of each factor (hi.hi + hi.mid
 // + mid.hi: relative error near 2^-16 per product, against 1e-4 for the
@@ -283,14 +282,12 @@ __device__ void process_tile16(const MfmaArgs &a, Tile16Lds &L, int b, int h, in
         const float r0 = W[0] - lo_f32(hi01), r1 = W[1] - hi_f32(hi01);
         const float r2 = W[2] - lo_f32(hi23), r3 = W[3] - hi_f32(hi23);
         const uint32_t md01 = pk_bf16(r0, r1), md23 = pk_bf16(r2, r3);
-        // one 32-deep product per row tile: k-slots 8 g .. 8 g + 3 pair the keys
-        // of tokens 4 g + e with W's hi part, 8 g + 4 .. 8 g + 7 the same keys
-        // with its mid part (a 16x16x32 product costs what a 16x16x16 one does)
-        const bf16x8 BHM = __builtin_bit_cast(bf16x8, u32x4{hi01, hi23, md01, md23});
+        const s16x4 BH = __builtin_bit_cast(s16x4, u32x2{hi01, hi23});
+        const s16x4 BM = __builtin_bit_cast(s16x4, u32x2{md01, md23});
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
-            const u32x2 a = __builtin_bit_cast(u32x2, AU[rt]);
-            acc[rt] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, u32x4{a[0], a[1], a[0], a[1]}), BHM, acc[rt]);
+            acc[rt] = mfma_bf16_k16(AU[rt], BH, acc[rt]);
+            acc[rt] = mfma_bf16_k16(AU[rt], BM, acc[rt]);
         }
 
         // ---- re-encode the column ----
